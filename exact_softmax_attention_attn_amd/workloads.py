@@ -1,0 +1,119 @@
+"""Seeded synthetic inputs for the attention backward, shared by tests and bench.
+
+This module holds shapes, seeds and value recipes only: none of the attention
+arithmetic lives here, so the oracle and the HIP path can both draw from it
+without sharing any of the method.
+
+The five workloads stand in for the pages' own workloads (no dataset or
+trained weights exist for them):
+
+* ``c1_tiny``  -- the toy of ddx issue #217's repro script: 3 sequences, 2
+  heads, 8 positions, 4 channels per head, scale 1/2, and Q/K/V filled with
+  sin(flat_index * 0.37 + phase) for phases 0, 1, 2 over the row-major
+  (sequence, position, head, channel) flattening.  dO ~ N(0, 1) from the seed.
+* ``c2_nanogpt_cpu`` -- the GPT demo size of issue #217: batch 12, 4 heads,
+  64 positions, 128 channels (head dim 32), scale 1/sqrt(32).
+* ``c3_single_seq`` -- PR #162's timing workload: one sequence of 256 tokens
+  with 64 features, one head, scale 1/8.
+* ``c4_batched`` -- 1,024 tokens as in issue #243 item 1, batch 4 x 16 heads,
+  head dim 64, bf16 in / fp32 accumulate, scale 1/8 (1/sqrt(d); unstated).
+* ``c5_long`` -- 16,384 tokens as in issue #243 item 2, 16 heads, head dim 128,
+  bf16 in / fp32 accumulate, scale 1/sqrt(128).
+
+Random draws use numpy's PCG64 ``default_rng(seed)`` in fp64, in the order
+Q, K, V, dO, each of shape [B, N, H, d]; Q/K/V are multiplied by ``qkv_std``.
+bf16 workloads are rounded fp64 -> fp32 -> bf16, each step round-to-nearest-
+even, and returned as fp32 arrays that hold bf16 values exactly.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+__all__ = ["Workload", "WORKLOADS", "get", "make_inputs", "make_random", "bf16_round"]
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    scale: float
+    dtype: str            # "f32" or "bf16": the device input/output type
+    qkv_std: float = 1.0
+    qkv: str = "normal"   # "normal" or "sin" (the issue #217 toy recipe)
+    causal: bool = True
+    description: str = ""
+
+    @property
+    def shape(self):
+        return (self.B, self.N, self.H, self.d)
+
+
+WORKLOADS = (
+    Workload("c1_tiny", 3, 2, 8, 4, 0.5, "f32", qkv="sin",
+             description="toy of issue #217: 3 seq x 2 heads x 8 pos x d 4, scale 1/2, sin inputs"),
+    Workload("c2_nanogpt_cpu", 12, 4, 64, 32, 1.0 / math.sqrt(32), "f32",
+             description="nanoGPT CPU size: batch 12, 4 heads, 64 pos, d 32"),
+    Workload("c3_single_seq", 1, 1, 256, 64, 1.0 / 8.0, "f32",
+             description="one sequence, 256 tokens x 64 features"),
+    Workload("c4_batched", 4, 16, 1024, 64, 1.0 / 8.0, "bf16", qkv_std=0.5,
+             description="batch 4 x 16 heads x 1024 tokens x d 64, bf16"),
+    Workload("c5_long", 1, 16, 16384, 128, 1.0 / math.sqrt(128), "bf16", qkv_std=0.5,
+             description="1 x 16 heads x 16384 tokens x d 128, bf16"),
+)
+
+
+def get(name: str) -> Workload:
+    for w in WORKLOADS:
+        if w.name == name:
+            return w
+    raise KeyError(name)
+
+
+def bf16_round(x) -> np.ndarray:
+    """Round to bf16 (via fp32), nearest-even at each step; returns fp32 values."""
+    f = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    u = f.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32).reshape(f.shape)
+
+
+def _cast(x: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "f32":
+        return np.asarray(x, dtype=np.float32)
+    if dtype == "bf16":
+        return bf16_round(x)
+    raise ValueError(dtype)
+
+
+def _sin_fill(shape, phase: float) -> np.ndarray:
+    n = int(np.prod(shape))
+    return np.sin(np.arange(n) * 0.37 + phase).reshape(shape)
+
+
+def make_inputs(w: Workload, seed: int = 0) -> dict:
+    """Q, K, V, dO for a workload as fp32 arrays [B, N, H, d] (bf16-exact for bf16)."""
+    rng = np.random.default_rng(seed)
+    shape = w.shape
+    if w.qkv == "sin":
+        q, k, v = (_sin_fill(shape, ph) for ph in (0.0, 1.0, 2.0))
+    else:
+        q = rng.standard_normal(shape) * w.qkv_std
+        k = rng.standard_normal(shape) * w.qkv_std
+        v = rng.standard_normal(shape) * w.qkv_std
+    do = rng.standard_normal(shape)
+    return {"q": _cast(q, w.dtype), "k": _cast(k, w.dtype), "v": _cast(v, w.dtype),
+            "do": _cast(do, w.dtype)}
+
+
+def make_random(B: int, H: int, N: int, d: int, dtype: str, seed: int = 0,
+                qkv_std: float = 1.0) -> dict:
+    """Normal inputs of any shape (edge cases: ragged N, small d, N = 1, ...)."""
+    w = Workload("random", B, H, N, d, 1.0 / math.sqrt(d), dtype, qkv_std=qkv_std)
+    return make_inputs(w, seed)

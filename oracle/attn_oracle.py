@@ -1,0 +1,312 @@
+"""Exact softmax attention, forward and backward, as a plain fp64 CPU oracle.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module: only the test suite, the smoke check and the benchmark's
+CPU-baseline leg use it.  It shares no code with the HIP library and imports
+nothing from it.
+
+What it computes, and where that is defined
+-------------------------------------------
+Sources are the pages' titles and sections:
+
+* ddx issue #217, "Backward of batched attention builds a contraction over
+  every pair of sequences and heads", repro script: the SQL loss (CTEs
+  ``scores``, ``weights``, ``norm``, ``heads``) and the JAX loss beside it.
+  Scores are the per-head dot product of a query row with a key row times a
+  scale (1/2 there); a key position is kept when it is not after the query
+  position (diagonal kept); the weights are exp(score minus the row max); the
+  row normaliser z is their sum; the head output is the weighted sum of value
+  rows divided by z.  Tensors are indexed (sequence, position, head, channel)
+  in row-major order.
+* ddx issue #243, "Attention's gradient: a softmax shift's backward computed
+  twice, and recomputing scores instead of saving them", item 1: the gradient
+  through the row max cancels because the shift cancels in w/z; item 2: the
+  backward needs the scores, dP = dO V^T, and the softmax-weighted sums of dP,
+  and one saved number per row, m + log z, is enough to rebuild the scores.
+* ddx PR #162, "perf(ddx-ad): transpose causal attention's contractions
+  without their joins", section "What changed": transpose p = w/z per score,
+  then p @ v (the plan jax.grad uses).
+
+Everything here is the textbook definition materialised at N x N per
+(batch, head), in float64, so a reader can check each line against the
+formulas: no tiling, no online softmax, no fusion.  The only grouping is in
+``attn_bwd_sampled``, which evaluates whole rows (or whole columns) of the same
+definition for a few chosen indices; rows are independent, so batching them
+changes no value.
+
+Pins (tests/test_oracle_pins.py): pair counts against the counts the pages
+print, central finite differences, the shift-cancellation identity, sum rules,
+metamorphic shifts, closed forms for Q = 0 and N = 1, scipy's logsumexp and
+torch's CPU fp64 scaled_dot_product_attention with autograd.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "causal_keep",
+    "scores",
+    "masked_scores",
+    "softmax_rows",
+    "softmax_backward",
+    "grad_q_k",
+    "head_forward",
+    "head_backward",
+    "attn_fwd",
+    "attn_bwd",
+    "attn_bwd_sampled",
+    "literal_backward_head",
+    "loss_value",
+    "pair_count",
+    "bwd_flops",
+]
+
+
+# --------------------------------------------------------------------------
+# Forward steps (issue #217 repro: CTEs scores -> weights -> norm -> heads)
+# --------------------------------------------------------------------------
+
+def causal_keep(n_q: int, n_k: int) -> np.ndarray:
+    """Boolean keep-mask: key position j is kept for query position i iff j <= i.
+
+    Issue #217 repro: the score join keeps q.pos >= k.pos; the JAX loss uses a
+    lower-triangular mask.  The diagonal is kept, so every row keeps >= 1 key.
+    """
+    i = np.arange(n_q)[:, None]
+    j = np.arange(n_k)[None, :]
+    return j <= i
+
+
+def scores(q: np.ndarray, k: np.ndarray, scale: float) -> np.ndarray:
+    """S[i, j] = scale * sum_c q[i, c] k[j, c]  (issue #217 repro, CTE ``scores``)."""
+    return scale * (q @ k.T)
+
+
+def masked_scores(q: np.ndarray, k: np.ndarray, scale: float, causal: bool) -> np.ndarray:
+    """Scores with masked-out pairs set to -inf (absent rows in the SQL spelling)."""
+    s = scores(q, k, scale)
+    if causal:
+        s = np.where(causal_keep(s.shape[0], s.shape[1]), s, -np.inf)
+    return s
+
+
+def softmax_rows(s: np.ndarray):
+    """Row max m, shifted weights w = exp(s - m), normaliser z = sum_j w.
+
+    Issue #217 repro, CTEs ``weights`` (exp of the score minus the row MAX
+    window) and ``norm`` (SUM of the weights per row).  -inf scores give w = 0.
+    """
+    m = s.max(axis=1)
+    w = np.exp(s - m[:, None])
+    z = w.sum(axis=1)
+    return m, w, z
+
+
+def head_forward(q, k, v, scale: float, causal: bool):
+    """One (batch, head): O = (w / z) V and the saved row scalar L = m + log z.
+
+    O follows the CTE ``heads`` of the issue #217 repro; L is the one number per
+    row that issue #243 (item 2) names as enough to rebuild the scores.
+    Returns O [N, d], L [N], P [N, N].
+    """
+    s = masked_scores(q, k, scale, causal)
+    m, w, z = softmax_rows(s)
+    p = w / z[:, None]
+    o = p @ v
+    lse = m + np.log(z)
+    return o, lse, p
+
+
+# --------------------------------------------------------------------------
+# Backward steps (PR #162 "What changed": transpose p = w/z, then p @ v)
+# --------------------------------------------------------------------------
+
+def softmax_backward(p: np.ndarray, dp: np.ndarray):
+    """dS = P o (dP - D) with D_i = sum_j P_ij dP_ij.
+
+    The cotangent of the softmax input.  There is no term for the row-max
+    shift: issue #243 (item 1) notes that its gradient cancels in w/z.
+    D is formed from P and dP here (the definition); that it equals
+    rowsum(dO o O) is checked by the pins, not assumed.
+    """
+    d = (p * dp).sum(axis=1)
+    ds = p * (dp - d[:, None])
+    return ds, d
+
+
+def grad_q_k(ds: np.ndarray, q: np.ndarray, k: np.ndarray, scale: float):
+    """dQ = scale * dS K and dK = scale * dS^T Q (S = scale * Q K^T)."""
+    dq = scale * (ds @ k)
+    dk = scale * (ds.T @ q)
+    return dq, dk
+
+
+def head_backward(q, k, v, do, scale: float, causal: bool):
+    """Exact gradient of sum(dO o O) for one (batch, head), every table materialised.
+
+    Returns dQ, dK, dV [N, d], D [N], dS row sums [N], P [N, N].
+    """
+    _, _, p = head_forward(q, k, v, scale, causal)
+    dv = p.T @ do                      # p @ v transposed against the output cotangent
+    dp = do @ v.T                      # dP = dO V^T (issue #243, item 2)
+    ds, d = softmax_backward(p, dp)
+    dq, dk = grad_q_k(ds, q, k, scale)
+    return dq, dk, dv, d, ds.sum(axis=1), p
+
+
+def literal_backward_head(q, k, v, do, scale: float, causal: bool):
+    """The same gradient spelled step by step as the SQL plan names its tables.
+
+    Issue #217 repro output lists the backward steps in the order
+    cotangent_2 (dO) -> contraction_0 (g = dO V^T) -> cotangent_1 (z-bar) ->
+    cotangent_0 (s-bar) -> grad_0_q.  Here, with w = exp(s - m):
+      g_ij    = dO_i . v_j
+      zbar_i  = -sum_j w_ij g_ij / z_i^2
+      wbar_ij = g_ij / z_i + zbar_i
+      sbar_ij = w_ij wbar_ij            (direct path into the scores)
+      mbar_i  = -sum_j sbar_ij          (path through the row max)
+    Issue #243 (item 1) says mbar cancels; the pins check |mbar| ~ 0 and that
+    sbar equals softmax_backward's dS.  Returns sbar [N, N] and mbar [N].
+    """
+    s = masked_scores(q, k, scale, causal)
+    m, w, z = softmax_rows(s)
+    g = do @ v.T
+    zbar = -(w * g).sum(axis=1) / z ** 2
+    wbar = g / z[:, None] + zbar[:, None]
+    sbar = w * wbar
+    mbar = -sbar.sum(axis=1)
+    return sbar, mbar
+
+
+# --------------------------------------------------------------------------
+# Batched entry points, tensors laid out [B, N, H, d] (sequence, pos, head, c)
+# --------------------------------------------------------------------------
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+def attn_fwd(Q, K, V, scale: float, causal: bool = True):
+    """O [B, N, H, d] and L [B, H, N] (natural log) for every (batch, head)."""
+    Q, K, V = _f64(Q), _f64(K), _f64(V)
+    B, N, H, _ = Q.shape
+    O = np.empty_like(V)
+    L = np.empty((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            o, lse, _ = head_forward(Q[b, :, h], K[b, :, h], V[b, :, h], scale, causal)
+            O[b, :, h] = o
+            L[b, h] = lse
+    return O, L
+
+
+def attn_bwd(Q, K, V, dO, scale: float, causal: bool = True):
+    """dQ, dK, dV [B, N, H, d] plus diagnostics D and dS row sums [B, H, N]."""
+    Q, K, V, dO = _f64(Q), _f64(K), _f64(V), _f64(dO)
+    B, N, H, _ = Q.shape
+    dQ = np.empty_like(Q)
+    dK = np.empty_like(K)
+    dV = np.empty_like(V)
+    D = np.empty((B, H, N))
+    ds_rows = np.empty((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            dq, dk, dv, d, dsr, _ = head_backward(
+                Q[b, :, h], K[b, :, h], V[b, :, h], dO[b, :, h], scale, causal)
+            dQ[b, :, h], dK[b, :, h], dV[b, :, h] = dq, dk, dv
+            D[b, h], ds_rows[b, h] = d, dsr
+    return {"dQ": dQ, "dK": dK, "dV": dV, "D": D, "dS_rowsum": ds_rows}
+
+
+def attn_bwd_sampled(Q, K, V, dO, scale: float, causal: bool, b: int, h: int,
+                     rows, cols, row_block: int = 512):
+    """Selected outputs of one (b, h) without any N x N array.
+
+    dQ and O are returned for the query rows ``rows``; dK and dV for the key
+    rows ``cols``.  Each is the definition of ``head_backward`` evaluated for
+    that row or column alone:
+      * query row i needs score row i, its softmax, dP row i and D_i;
+      * key row j needs column j of P and dS, hence L_i and D_i for every
+        query row i; those come from full score rows evaluated ``row_block``
+        rows at a time (rows are independent, so the grouping changes nothing).
+    """
+    q = _f64(Q[b, :, h]); k = _f64(K[b, :, h]); v = _f64(V[b, :, h]); do = _f64(dO[b, :, h])
+    n = q.shape[0]
+    rows = np.asarray(rows, dtype=np.int64)
+    cols = np.asarray(cols, dtype=np.int64)
+
+    def row_stats(r0, r1):
+        s = scale * (q[r0:r1] @ k.T)
+        if causal:
+            s = np.where(np.arange(n)[None, :] <= np.arange(r0, r1)[:, None], s, -np.inf)
+        m = s.max(axis=1)
+        w = np.exp(s - m[:, None])
+        z = w.sum(axis=1)
+        p = w / z[:, None]
+        dp = do[r0:r1] @ v.T
+        d = (p * dp).sum(axis=1)
+        return m + np.log(z), d, p, dp
+
+    # per-row scalars L and D for all rows
+    L = np.empty(n)
+    D = np.empty(n)
+    for r0 in range(0, n, row_block):
+        r1 = min(n, r0 + row_block)
+        L[r0:r1], D[r0:r1], _, _ = row_stats(r0, r1)
+
+    out = {"rows": rows, "cols": cols, "L": L, "D": D}
+    dq = np.empty((rows.size, q.shape[1]))
+    o = np.empty((rows.size, v.shape[1]))
+    for t, i in enumerate(rows):
+        _, _, p, dp = row_stats(int(i), int(i) + 1)
+        ds = p * (dp - D[i])
+        dq[t] = scale * (ds @ k)[0]
+        o[t] = (p @ v)[0]
+    out["dQ"] = dq
+    out["O"] = o
+
+    dk = np.empty((cols.size, k.shape[1]))
+    dv = np.empty((cols.size, v.shape[1]))
+    for t, j in enumerate(cols):
+        s_col = scale * (q @ k[j])                       # S[:, j]
+        p_col = np.exp(s_col - L)                        # P[:, j] = exp(S - L)
+        if causal:
+            p_col = np.where(np.arange(n) >= j, p_col, 0.0)
+        dp_col = do @ v[j]                               # dP[:, j]
+        ds_col = p_col * (dp_col - D)
+        dv[t] = p_col @ do
+        dk[t] = scale * (ds_col @ q)
+    out["dK"] = dk
+    out["dV"] = dv
+    return out
+
+
+# --------------------------------------------------------------------------
+# Scalars used by pins and by the FLOP accounting
+# --------------------------------------------------------------------------
+
+def loss_value(Q, K, V, dO, scale: float, causal: bool = True) -> float:
+    """l = sum(dO o O): the scalar whose gradient attn_bwd returns."""
+    O, _ = attn_fwd(Q, K, V, scale, causal)
+    return float((_f64(dO) * O).sum())
+
+
+def pair_count(B: int, H: int, N: int, causal: bool = True) -> int:
+    """Number of kept (i, j) pairs: B*H*N(N+1)/2 causal (diagonal kept), else B*H*N^2.
+
+    Counted from the mask itself, so a wrong mask shows up against the row
+    counts the pages print for the score tables.
+    """
+    if N == 0:
+        return 0
+    keep = causal_keep(N, N) if causal else np.ones((N, N), dtype=bool)
+    return int(B * H * int(keep.sum()))
+
+
+def bwd_flops(B: int, H: int, N: int, d: int, causal: bool = True) -> int:
+    """Metric FLOPs of the backward: five contractions x 2d FLOP x kept pairs.
+
+    The five are S = QK^T, dP = dO V^T, dV = P^T dO, dQ = dS K, dK = dS^T Q.
+    """
+    return 10 * d * pair_count(B, H, N, causal)
