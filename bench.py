@@ -1,0 +1,195 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact causal attention backward (attn_bwd) on one MI355X.
+
+One step = one attn_bwd over the whole workload: the preprocess (D), the
+dK/dV kernel and the dQ kernel, launched through the C ABI stage entry
+points on torch's current stream.  Inputs, O and L (from attn_fwd_lse) are
+resident in HBM before the timed region starts.
+
+Prints one JSON line.  `value` is attn_bwd TFLOP/s with FLOPs counted as
+10 * d * (kept pairs), kept pairs = B*H*N(N+1)/2 causal.  `roofline` covers
+the dominant kernel (dK/dV): its algorithmic FLOPs (8 * d * pairs: S, dP,
+dV, dK) over its mean duration from HIP events recorded around it on the
+launch stream, against the bf16 dense MFMA peak.  `cpu_baseline` times the
+fp64 oracle on one (batch, head) of the same workload on the host cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "causal attention bwd TFLOP/s and % of bf16 MFMA peak at N=16K, d=128"
+PEAK = {"bf16": 2516.6, "f32": 157.3}          # dense MFMA TFLOP/s, MI355X spec
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dkdv_c5_long_traffic.json")
+KERNEL_SOURCES = ("exact_softmax_attention_attn_amd/csrc/attn_bwd.hip",
+                  "exact_softmax_attention_attn_amd/csrc/common.h")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def pairs(B, H, N, causal=True):
+    return B * H * (N * (N + 1) // 2 if causal else N * N)
+
+
+def traffic_record():
+    """HBM bytes per dK/dV launch from committed rocprofv3 counters, if still valid."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, x):
+    """The oracle as it stands, on one (batch, head) of the workload."""
+    import numpy as np
+    from oracle import attn_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()
+                       if p.get("user_api") == "blas"] or [os.cpu_count()])
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        threads = os.cpu_count()
+    q, k, v, do = (x[n][:1, :, :1].astype(np.float64) for n in ("q", "k", "v", "do"))
+    t0 = time.perf_counter()
+    orc.attn_bwd(q, k, v, do, w.scale, w.causal)
+    dt = time.perf_counter() - t0
+    flops = 10 * w.d * pairs(1, 1, w.N, w.causal)
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"one (batch, head) of {w.name} (N={w.N}, d={w.d}, causal), fp64 numpy, "
+                      f"{dt:.1f} s; scaled by its own FLOP count"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c5_long")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run one plain copy of this many MiB (counter calibration runs)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(every (batch, head) is independent, see the sharding note in the design doc)",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from exact_softmax_attention_attn_amd import binding, workloads
+
+    binding.load()
+    w = workloads.get(args.workload)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] {w.name}: inputs", file=sys.stderr, flush=True)
+    x = workloads.make_inputs(w, seed=0)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    q, k, v, do = (torch.from_numpy(x[n]).to(dev).to(tdt) for n in ("q", "k", "v", "do"))
+    o, lse = binding.attn_fwd_lse(q, k, v, causal=w.causal, scale=w.scale)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    ws = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        binding.attn_bwd_preprocess(o, do, ws)
+        if ev is not None:
+            ev[1].record()
+        binding.attn_bwd_dkdv(q, k, v, do, lse, ws, dk, dv, causal=w.causal, scale=w.scale)
+        if ev is not None:
+            ev[2].record()
+        binding.attn_bwd_dq(q, k, v, do, lse, ws, dq, causal=w.causal, scale=w.scale)
+        if ev is not None:
+            ev[3].record()
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    pre = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    dkdv = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    dqk = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    ms = wall / args.steps * 1e3
+    P = pairs(w.B, w.H, w.N, w.causal)
+    flops = 10 * w.d * P
+    value = flops / (ms * 1e-3) / 1e12
+    dkdv_flops = 8 * w.d * P
+    achieved = dkdv_flops / (dkdv * 1e-3) / 1e12
+    peak = PEAK[w.dtype]
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+
+    esz = 2 if w.dtype == "bf16" else 4
+    alg_bytes = 8 * w.B * w.N * w.H * w.d * esz + 4 * w.B * w.H * w.N
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "causal": w.causal, "scale": w.scale, "layout": "[B,N,H,d]",
+                   "parallelism": "single GPU"},
+        "pct_of_peak": round(100 * value / peak, 2),
+        "stages_ms": {"preprocess": round(pre, 4), "dkdv": round(dkdv, 4), "dq": round(dqk, 4)},
+        "hbm_gbs_algorithmic": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
+        "roofline": {"kernel": "bwd_dkdv_kernel", "bound": "mfma", "achieved": round(achieved, 3),
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": traffic_record()},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle, one head)", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(w, x)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

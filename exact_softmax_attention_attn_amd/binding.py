@@ -1,0 +1,186 @@
+"""ctypes binding of libattn.so: argument marshalling only.
+
+Every function here has the name of the C entry point it calls (declared in
+``include/attn.h``) and takes torch tensors laid out [B, N, H, d] (float32 or
+bfloat16) plus L / workspace [B, H, N] float32, all on one HIP device.  The
+work is enqueued on ``torch.cuda.current_stream()``.  There is no fallback:
+if the library is missing or a call fails, an exception is raised.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch  # imported before the library so that one HIP runtime is mapped
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libattn.so")
+
+ATTN_F32, ATTN_BF16 = 0, 1
+ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+
+_SIGNATURES = {
+    "attn_fwd_lse": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "attn_bwd_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
+    "attn_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "attn_bwd_preprocess": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P]),
+    "attn_bwd_dkdv": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "attn_bwd_dq": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "attn_status_string": (ctypes.c_char_p, [_I]),
+    "attn_last_error": (ctypes.c_char_p, []),
+}
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        lib = load()
+        msg = lib.attn_status_string(status).decode()
+        if status == ATTN_ERR_HIP:
+            msg += ": " + lib.attn_last_error().decode()
+        super().__init__(f"{where}: {msg} (status {status})")
+        self.status = status
+
+
+def load(path: str = LIB_PATH):
+    """Load libattn.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
+            "or `python exact_softmax_attention_attn_amd/build_lib.py`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _ptr(t: torch.Tensor):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check_bnhd(*ts: torch.Tensor):
+    ref = ts[0]
+    if ref.dim() != 4:
+        raise ValueError("expected [B, N, H, d] tensors")
+    for t in ts:
+        if t.shape != ref.shape or t.dtype != ref.dtype or t.device != ref.device:
+            raise ValueError("Q, K, V, O, dO and outputs must share shape, dtype and device")
+        if not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("tensors must be contiguous HIP device tensors")
+
+
+def _check_rows(t: torch.Tensor, B: int, H: int, N: int, device):
+    if t.dtype != torch.float32 or tuple(t.shape) != (B, H, N) or not t.is_contiguous() \
+            or t.device != device:
+        raise ValueError(f"expected a contiguous float32 [B, H, N] = {(B, H, N)} tensor on {device}")
+
+
+def _call(name: str, *args):
+    st = getattr(load(), name)(*args)
+    if st != ATTN_OK:
+        raise AttnError(st, name)
+
+
+def default_scale(d: int) -> float:
+    return 1.0 / math.sqrt(d)
+
+
+def attn_bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
+    return int(load().attn_bwd_workspace_bytes(B, H, N, d))
+
+
+def attn_fwd_lse(q, k, v, causal: bool = True, scale: float | None = None, o=None, lse=None):
+    """O [B, N, H, d] and L [B, H, N] float32 (natural log of the row normaliser)."""
+    _check_bnhd(q, k, v)
+    B, N, H, d = q.shape
+    scale = default_scale(d) if scale is None else float(scale)
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_bnhd(q, o)
+    _check_rows(lse, B, H, N, q.device)
+    with torch.cuda.device(q.device):
+        _call("attn_fwd_lse", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
+              int(bool(causal)), scale, _dtype_code(q), _stream(q.device))
+    return o, lse
+
+
+def attn_bwd(q, k, v, o, do, lse, causal: bool = True, scale: float | None = None,
+             dq=None, dk=None, dv=None, workspace=None):
+    """dQ, dK, dV [B, N, H, d]; workspace (float32 [B, H, N]) ends up holding D."""
+    _check_bnhd(q, k, v, o, do)
+    B, N, H, d = q.shape
+    _check_rows(lse, B, H, N, q.device)
+    scale = default_scale(d) if scale is None else float(scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    _check_bnhd(q, dq, dk, dv)
+    workspace = torch.empty((B, H, N), dtype=torch.float32, device=q.device) \
+        if workspace is None else workspace
+    _check_rows(workspace, B, H, N, q.device)
+    with torch.cuda.device(q.device):
+        _call("attn_bwd", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
+              _ptr(dk), _ptr(dv), _ptr(workspace), B, H, N, d, int(bool(causal)), scale,
+              _dtype_code(q), _stream(q.device))
+    return dq, dk, dv
+
+
+def attn_bwd_preprocess(o, do, workspace):
+    _check_bnhd(o, do)
+    B, N, H, d = o.shape
+    _check_rows(workspace, B, H, N, o.device)
+    with torch.cuda.device(o.device):
+        _call("attn_bwd_preprocess", _ptr(o), _ptr(do), _ptr(workspace), B, H, N, d,
+              _dtype_code(o), _stream(o.device))
+    return workspace
+
+
+def attn_bwd_dkdv(q, k, v, do, lse, workspace, dk, dv, causal: bool = True,
+                  scale: float | None = None):
+    _check_bnhd(q, k, v, do, dk, dv)
+    B, N, H, d = q.shape
+    _check_rows(lse, B, H, N, q.device)
+    _check_rows(workspace, B, H, N, q.device)
+    scale = default_scale(d) if scale is None else float(scale)
+    with torch.cuda.device(q.device):
+        _call("attn_bwd_dkdv", _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(workspace),
+              _ptr(dk), _ptr(dv), B, H, N, d, int(bool(causal)), scale, _dtype_code(q),
+              _stream(q.device))
+    return dk, dv
+
+
+def attn_bwd_dq(q, k, v, do, lse, workspace, dq, causal: bool = True, scale: float | None = None):
+    _check_bnhd(q, k, v, do, dq)
+    B, N, H, d = q.shape
+    _check_rows(lse, B, H, N, q.device)
+    _check_rows(workspace, B, H, N, q.device)
+    scale = default_scale(d) if scale is None else float(scale)
+    with torch.cuda.device(q.device):
+        _call("attn_bwd_dq", _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(workspace),
+              _ptr(dq), B, H, N, d, int(bool(causal)), scale, _dtype_code(q), _stream(q.device))
+    return dq

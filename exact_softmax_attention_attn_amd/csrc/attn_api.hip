@@ -1,0 +1,164 @@
+// C-ABI layer of libattn.so: argument validation (no HIP call until every
+// check passes), dispatch to the kernel launchers, status reporting.
+#include <initializer_list>
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "attn.h"
+#include "launch.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+void set_hip_error(hipError_t e) {
+  const char* s = hipGetErrorString(e);
+  strncpy(g_last_error, s ? s : "unknown HIP error", sizeof(g_last_error) - 1);
+  g_last_error[sizeof(g_last_error) - 1] = '\0';
+}
+
+int finish(hipError_t e) {
+  if (e != hipSuccess) {
+    set_hip_error(e);
+    return ATTN_ERR_HIP;
+  }
+  return ATTN_OK;
+}
+
+// Sizes: each >= 1; grid limits (B, H <= 65535; B*H*N < 2^31); byte counts fit.
+int check_sizes(int B, int H, int N, int d) {
+  if (B < 1 || H < 1 || N < 1 || d < 1) return ATTN_ERR_INVALID;
+  if (B > 65535 || H > 65535) return ATTN_ERR_UNSUPPORTED;
+  const int64_t rows = (int64_t)B * H * N;
+  if (rows >= ((int64_t)1 << 31)) return ATTN_ERR_UNSUPPORTED;
+  if (rows * d >= ((int64_t)1 << 40)) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+int check_dtype_dim(int d, int dtype) {
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (d > 128) return ATTN_ERR_UNSUPPORTED;
+  if (dtype == ATTN_F32 && d % 4 != 0) return ATTN_ERR_UNSUPPORTED;
+  if (dtype == ATTN_BF16 && d % 8 != 0) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+int check_scale_causal(float scale, int causal) {
+  if (!(scale > 0.f) || !isfinite(scale)) return ATTN_ERR_INVALID;
+  if (causal != 0 && causal != 1) return ATTN_ERR_INVALID;
+  return ATTN_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_ptrs(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (p == nullptr || !aligned16(p)) return ATTN_ERR_INVALID;
+  return ATTN_OK;
+}
+
+#define ATTN_TRY(expr)           \
+  do {                           \
+    const int st_ = (expr);      \
+    if (st_ != ATTN_OK) return st_; \
+  } while (0)
+
+attn::BwdArgs make_bwd(const void* Q, const void* K, const void* V, const void* dO,
+                       const float* L, const void* ws, void* dQ, void* dK, void* dV, int B,
+                       int H, int N, int d, int causal, float scale, int dtype) {
+  attn::BwdArgs a;
+  a.Q = Q; a.K = K; a.V = V; a.dO = dO; a.L = L;
+  a.Dws = static_cast<const float*>(ws);
+  a.dQ = dQ; a.dK = dK; a.dV = dV;
+  a.B = B; a.H = H; a.N = N; a.d = d;
+  a.causal = causal; a.scale = scale; a.dtype = dtype;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd_lse(const void* Q, const void* K, const void* V, void* O, float* L, int B, int H,
+                 int N, int d, int causal, float scale, int dtype, void* stream) {
+  ATTN_TRY(check_ptrs({Q, K, V, O, L}));
+  ATTN_TRY(check_sizes(B, H, N, d));
+  ATTN_TRY(check_scale_causal(scale, causal));
+  ATTN_TRY(check_dtype_dim(d, dtype));
+  attn::FwdArgs a;
+  a.Q = Q; a.K = K; a.V = V; a.O = O; a.L = L;
+  a.B = B; a.H = H; a.N = N; a.d = d;
+  a.causal = causal; a.scale = scale; a.dtype = dtype;
+  return finish(attn::launch_fwd_lse(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t attn_bwd_workspace_bytes(int B, int H, int N, int d) {
+  if (check_sizes(B, H, N, d) != ATTN_OK) return 0;
+  return (size_t)B * (size_t)H * (size_t)N * sizeof(float);
+}
+
+int attn_bwd_preprocess(const void* O, const void* dO, void* workspace, int B, int H, int N,
+                        int d, int dtype, void* stream) {
+  ATTN_TRY(check_ptrs({O, dO, workspace}));
+  ATTN_TRY(check_sizes(B, H, N, d));
+  ATTN_TRY(check_dtype_dim(d, dtype));
+  return finish(attn::launch_bwd_preprocess(O, dO, static_cast<float*>(workspace), B, H, N, d,
+                                            dtype, static_cast<hipStream_t>(stream)));
+}
+
+int attn_bwd_dkdv(const void* Q, const void* K, const void* V, const void* dO, const float* L,
+                  const void* workspace, void* dK, void* dV, int B, int H, int N, int d,
+                  int causal, float scale, int dtype, void* stream) {
+  ATTN_TRY(check_ptrs({Q, K, V, dO, L, workspace, dK, dV}));
+  ATTN_TRY(check_sizes(B, H, N, d));
+  ATTN_TRY(check_scale_causal(scale, causal));
+  ATTN_TRY(check_dtype_dim(d, dtype));
+  const attn::BwdArgs a =
+      make_bwd(Q, K, V, dO, L, workspace, nullptr, dK, dV, B, H, N, d, causal, scale, dtype);
+  return finish(attn::launch_bwd_dkdv(a, static_cast<hipStream_t>(stream)));
+}
+
+int attn_bwd_dq(const void* Q, const void* K, const void* V, const void* dO, const float* L,
+                const void* workspace, void* dQ, int B, int H, int N, int d, int causal,
+                float scale, int dtype, void* stream) {
+  ATTN_TRY(check_ptrs({Q, K, V, dO, L, workspace, dQ}));
+  ATTN_TRY(check_sizes(B, H, N, d));
+  ATTN_TRY(check_scale_causal(scale, causal));
+  ATTN_TRY(check_dtype_dim(d, dtype));
+  const attn::BwdArgs a =
+      make_bwd(Q, K, V, dO, L, workspace, dQ, nullptr, nullptr, B, H, N, d, causal, scale, dtype);
+  return finish(attn::launch_bwd_dq(a, static_cast<hipStream_t>(stream)));
+}
+
+int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+             const float* L, void* dQ, void* dK, void* dV, void* workspace, int B, int H, int N,
+             int d, int causal, float scale, int dtype, void* stream) {
+  ATTN_TRY(check_ptrs({Q, K, V, O, dO, L, dQ, dK, dV, workspace}));
+  ATTN_TRY(check_sizes(B, H, N, d));
+  ATTN_TRY(check_scale_causal(scale, causal));
+  ATTN_TRY(check_dtype_dim(d, dtype));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = attn::launch_bwd_preprocess(O, dO, static_cast<float*>(workspace), B, H, N, d,
+                                             dtype, s);
+  if (e != hipSuccess) return finish(e);
+  const attn::BwdArgs a =
+      make_bwd(Q, K, V, dO, L, workspace, dQ, dK, dV, B, H, N, d, causal, scale, dtype);
+  e = attn::launch_bwd_dkdv(a, s);
+  if (e != hipSuccess) return finish(e);
+  return finish(attn::launch_bwd_dq(a, s));
+}
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_INVALID: return "invalid argument";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported size, head dim or dtype";
+    case ATTN_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+const char* attn_last_error(void) { return g_last_error; }
+
+}  // extern "C"

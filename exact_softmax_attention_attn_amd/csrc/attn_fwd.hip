@@ -1,0 +1,143 @@
+// Forward kernel that also writes the saved row scalar L = m + log z.
+//
+// O follows the attention loss of ddx issue #217 ("Backward of batched
+// attention builds a contraction over every pair of sequences and heads",
+// repro script, CTEs scores / weights / norm / heads); L is the one number
+// per row that ddx issue #243 (item 2) says the backward needs to rebuild the
+// scores.  The row max and sum are kept online across key blocks.
+#include "common.h"
+#include "launch.h"
+
+namespace attn {
+
+// Workgroup = 4 waves = one block of 128 query rows of one (b, h).  Wave w
+// owns query rows qw + [0, 32); its Q rows sit in registers as the B operand
+// of S^T = K Q^T, so each lane owns one query row (column of S^T) and the row
+// max / row sum reduce over the lane's 16 registers plus its partner lane in
+// the other half-wave.  Key blocks of 64 rows are staged in LDS: K
+// row-major, V in the layout the contraction over keys reads.
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void fwd_lse_kernel(const T* __restrict__ Q,
+                                                         const T* __restrict__ K,
+                                                         const T* __restrict__ V,
+                                                         T* __restrict__ O, float* __restrict__ L,
+                                                         int H, int N, int d, float scale_log2) {
+  using M = Mma<T>;
+  using frag = typename M::frag;
+  constexpr int BQ = 128, BKV = 64, KS = D / M::K, MT = D / 32, RS = 32 / M::K;
+  using KTile = Tile<T, BKV, D, false>;
+  using VTile = Tile<T, BKV, D, sizeof(T) == 2>;
+
+  __shared__ __align__(16) unsigned char smem[KTile::BYTES + VTile::BYTES];
+  T* sbase = reinterpret_cast<T*>(smem);
+  const KTile ks_{sbase, nullptr};
+  const VTile vs_{sbase + KTile::RM_ELEMS, sbase + KTile::RM_ELEMS + VTile::RM_ELEMS};
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int nqb = gridDim.x;
+  const int ib = CAUSAL ? (nqb - 1 - (int)blockIdx.x) : (int)blockIdx.x;  // longest first
+  const int head = blockIdx.y, b = blockIdx.z;
+  const long rs = (long)H * d;
+  const long base = ((long)b * N * H + head) * d;
+
+  const int qb = ib * BQ;
+  const int qw = qb + wave * 32;
+  const int q = qw + l32;
+  frag qf[KS];
+  load_row_frags<T, D>(qf, Q + base, rs, q, N, d, h);
+
+  f32x16 acc[MT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) acc[i] = zero16();
+  float m = -1e30f;   // running max of the scaled scores, log2 units
+  float l = 0.f;      // running sum of exp2(score - m)
+
+  const int kv_end = CAUSAL ? min(N, qb + BQ) : N;
+  const int nkt = (kv_end + BKV - 1) / BKV;
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int k0 = kt * BKV;
+    __syncthreads();
+    ks_.template stage<256>(K + base, rs, k0, N, d, tid);
+    vs_.template stage<256>(V + base, rs, k0, N, d, tid);
+    __syncthreads();
+#pragma unroll
+    for (int st = 0; st < BKV / 32; ++st) {
+      const int ka = k0 + st * 32;
+      if (CAUSAL && ka > qw + 31) continue;
+      f32x16 s = zero16();
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) s = M::mma(ks_.along_cols(st * 32 + l32, kk, h), qf[kk], s);
+      // register r = key row ka + acc_row(r, h), column = query row q
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kv = ka + acc_row(r, h);
+        float x = s[r] * scale_log2;
+        if ((CAUSAL && kv > q) || kv >= N) x = -__builtin_inff();
+        s[r] = x;
+        mx = fmaxf(mx, x);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m, mx);
+      const float alpha = fast_exp2(m - m_new);
+      float sum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(s[r] - m_new);
+        s[r] = p;
+        sum += p;
+      }
+      sum += __shfl_xor(sum, 32);
+      l = l * alpha + sum;
+      m = m_new;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;
+#pragma unroll
+      for (int ss = 0; ss < RS; ++ss) {
+        const frag bp = M::pack(s, ss);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          acc[mt] = M::mma(vs_.along_rows(mt * 32 + l32, st * 32, ss, h), bp, acc[mt]);
+      }
+    }
+  }
+  const float inv = 1.f / l;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+    store_acc_transposed<T>(acc[mt], O + base, rs, qw, mt * 32, N, d, inv, lane);
+  if (h == 0 && q < N) L[((long)b * H + head) * N + q] = (m + log2f(l)) * 0.69314718055994531f;
+}
+
+template <typename T, int D, bool C>
+static hipError_t fwd_go(const FwdArgs& a, hipStream_t stream) {
+  dim3 grid((a.N + 127) / 128, a.H, a.B);
+  hipLaunchKernelGGL((fwd_lse_kernel<T, D, C>), grid, dim3(256), 0, stream,
+                     static_cast<const T*>(a.Q), static_cast<const T*>(a.K),
+                     static_cast<const T*>(a.V), static_cast<T*>(a.O), a.L, a.H, a.N, a.d,
+                     a.scale * kLog2e);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_lse(const FwdArgs& a, hipStream_t stream) {
+  const int bucket = head_dim_bucket(a.d);
+  if (a.dtype == 1) {
+    if (a.causal) {
+      if (bucket == 32) return fwd_go<bf16, 32, true>(a, stream);
+      if (bucket == 64) return fwd_go<bf16, 64, true>(a, stream);
+      return fwd_go<bf16, 128, true>(a, stream);
+    }
+    if (bucket == 32) return fwd_go<bf16, 32, false>(a, stream);
+    if (bucket == 64) return fwd_go<bf16, 64, false>(a, stream);
+    return fwd_go<bf16, 128, false>(a, stream);
+  }
+  if (a.causal) {
+    if (bucket == 32) return fwd_go<float, 32, true>(a, stream);
+    if (bucket == 64) return fwd_go<float, 64, true>(a, stream);
+    return fwd_go<float, 128, true>(a, stream);
+  }
+  if (bucket == 32) return fwd_go<float, 32, false>(a, stream);
+  if (bucket == 64) return fwd_go<float, 64, false>(a, stream);
+  return fwd_go<float, 128, false>(a, stream);
+}
+
+}  // namespace attn

@@ -1,0 +1,46 @@
+// Internal interface between the C-ABI layer and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace attn {
+
+struct BwdArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const void* dO;
+  const float* L;
+  const float* Dws;
+  void* dQ;
+  void* dK;
+  void* dV;
+  int B, H, N, d;
+  int causal;
+  float scale;
+  int dtype;  // 0 = f32, 1 = bf16
+};
+
+struct FwdArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  void* O;
+  float* L;
+  int B, H, N, d;
+  int causal;
+  float scale;
+  int dtype;
+};
+
+// Head dims are served by kernels compiled for 32, 64 or 128 columns; a
+// smaller d runs in the next bucket with the extra columns read as zero.
+inline int head_dim_bucket(int d) { return d <= 32 ? 32 : (d <= 64 ? 64 : 128); }
+
+hipError_t launch_bwd_preprocess(const void* O, const void* dO, float* Dws, int B, int H, int N,
+                                 int d, int dtype, hipStream_t stream);
+hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_fwd_lse(const FwdArgs& a, hipStream_t stream);
+
+}  // namespace attn

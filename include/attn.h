@@ -1,0 +1,142 @@
+/*
+ * attn.h -- C ABI of libattn.so: exact softmax attention forward (with the
+ * saved row scalar) and its exact backward by score recomputation, for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * What is computed.  For each batch b and head h, with q_i, k_j, v_j the rows
+ * of Q, K, V at (b, ., h, .):
+ *
+ *   S_ij = scale * q_i . k_j          kept for j <= i when causal (diagonal
+ *                                     kept), every j otherwise
+ *   P_ij = exp(S_ij - L_i),  L_i = m_i + log z_i,  m_i = max_j S_ij,
+ *          z_i = sum_j exp(S_ij - m_i)
+ *   O_i  = sum_j P_ij v_j
+ *
+ * This is the attention loss of ddx issue #217 ("Backward of batched
+ * attention builds a contraction over every pair of sequences and heads",
+ * repro script: CTEs scores, weights, norm, heads), with L the one saved
+ * number per row of ddx issue #243, item 2 ("Attention's gradient: a softmax
+ * shift's backward computed twice, and recomputing scores instead of saving
+ * them").  The backward returns the gradient of sum(dO o O):
+ *
+ *   dV = P^T dO,  dP = dO V^T,  D_i = sum_c dO_ic O_ic,
+ *   dS = P o (dP - D),  dQ = scale dS K,  dK = scale dS^T Q
+ *
+ * with no term for the row-max shift (issue #243, item 1: it cancels), and
+ * with S and P rebuilt tile by tile from Q, K and L (issue #243, item 2), so
+ * no N x N array is ever stored in device memory.
+ *
+ * Conventions shared by every entry point.
+ *  - Layout.  Q, K, V, O, dO, dQ, dK, dV are dense, row-major [B, N, H, d]
+ *    (sequence, position, head, channel), the index order of issue #217's
+ *    tables.  L and the workspace are dense [B, H, N] float32.
+ *  - dtype.  ATTN_F32: all [B, N, H, d] tensors are float32, arithmetic is
+ *    float32.  ATTN_BF16: they are bfloat16; products run on bf16 matrix
+ *    cores with float32 accumulation; P and dS are rounded to bf16 (nearest
+ *    even) before they enter a product; outputs are rounded to bf16.
+ *  - Pointers are device pointers (or host-coherent pointers the GPU can
+ *    read), aligned to 16 bytes.  The caller owns every buffer; the library
+ *    allocates nothing, frees nothing and keeps no pointer after returning.
+ *  - Outputs must not alias inputs or each other; they are overwritten.
+ *  - stream is a hipStream_t (NULL = the null stream).  Calls only enqueue
+ *    work and return; results are visible after the stream is synchronised.
+ *    There is no global mutable state, so calls are thread-safe.
+ *  - Errors.  The return value is an attn_status_t.  On ATTN_ERR_INVALID or
+ *    ATTN_ERR_UNSUPPORTED nothing was enqueued, no HIP call was made, and the
+ *    outputs are untouched.  ATTN_ERR_HIP means a launch failed; the text of
+ *    the HIP error is returned by attn_last_error() on the calling thread.
+ *    Non-finite inputs are not checked; they propagate.
+ *  - Limits.  B, H, N, d >= 1; d <= 128; d % 4 == 0 (f32) or d % 8 == 0
+ *    (bf16); B*N*H*d and B*H*N must fit in int32 (ATTN_ERR_UNSUPPORTED
+ *    otherwise); scale finite and > 0.  causal is 1 (keep j <= i) or 0 (keep
+ *    every pair).
+ */
+#ifndef ATTN_H_
+#define ATTN_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype_t;
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID = 1,      /* null pointer, size < 1, bad scale or flag */
+  ATTN_ERR_UNSUPPORTED = 2,  /* d or dtype outside what the kernels take  */
+  ATTN_ERR_HIP = 3           /* a HIP launch failed                       */
+} attn_status_t;
+
+/*
+ * Forward pass that also saves the row scalar.
+ *   in : Q, K, V  [B, N, H, d] (dtype)
+ *   out: O        [B, N, H, d] (dtype)   O_i = sum_j P_ij v_j
+ *        L        [B, H, N]    float32   L_i = m_i + log z_i (natural log)
+ * Issue #217 repro (CTEs scores .. heads) for O; issue #243 item 2 for L.
+ */
+int attn_fwd_lse(const void* Q, const void* K, const void* V, void* O, float* L,
+                 int B, int H, int N, int d, int causal, float scale, int dtype,
+                 void* stream);
+
+/* Bytes of device workspace attn_bwd needs: B*H*N*sizeof(float) (holds D).
+ * Returns 0 when a size is < 1 or the product overflows. */
+size_t attn_bwd_workspace_bytes(int B, int H, int N, int d);
+
+/*
+ * Backward pass by score recomputation: the three stages below, in order, on
+ * one stream.
+ *   in : Q, K, V, O, dO [B, N, H, d] (dtype); L [B, H, N] float32 as written
+ *        by attn_fwd_lse (or any L_i = log sum_j exp(S_ij) of the same kept set)
+ *   out: dQ, dK, dV     [B, N, H, d] (dtype)
+ *   workspace: >= attn_bwd_workspace_bytes(B, H, N, d) bytes of device memory;
+ *        on return (after the stream completes) it holds D [B, H, N] float32.
+ * PR #162 ("perf(ddx-ad): transpose causal attention's contractions without
+ * their joins", section "What changed") names the plan: transpose p = w/z per
+ * score, then p @ v.
+ */
+int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+             const float* L, void* dQ, void* dK, void* dV, void* workspace,
+             int B, int H, int N, int d, int causal, float scale, int dtype, void* stream);
+
+/*
+ * Stage 1 of attn_bwd: D_i = sum_c dO_ic O_ic in float32 (the softmax-weighted
+ * sum of dP, issue #243 item 2), written to workspace as [B, H, N].
+ */
+int attn_bwd_preprocess(const void* O, const void* dO, void* workspace,
+                        int B, int H, int N, int d, int dtype, void* stream);
+
+/*
+ * Stage 2 of attn_bwd: dK and dV.  One workgroup owns a block of key rows,
+ * keeps K, V and the dK, dV accumulators on chip, and walks the query blocks
+ * that can see them (from the diagonal down when causal), rebuilding S, P,
+ * dP and dS per tile.  Reads D from workspace (stage 1 must have run).
+ */
+int attn_bwd_dkdv(const void* Q, const void* K, const void* V, const void* dO,
+                  const float* L, const void* workspace, void* dK, void* dV,
+                  int B, int H, int N, int d, int causal, float scale, int dtype,
+                  void* stream);
+
+/*
+ * Stage 3 of attn_bwd: dQ.  One workgroup owns a block of query rows and walks
+ * the key blocks it can see, rebuilding S, P, dP and dS and accumulating
+ * dS K on chip.  No atomics: every dQ element is written once by one thread,
+ * so results are bitwise repeatable.  Reads D from workspace.
+ */
+int attn_bwd_dq(const void* Q, const void* K, const void* V, const void* dO,
+                const float* L, const void* workspace, void* dQ,
+                int B, int H, int N, int d, int causal, float scale, int dtype,
+                void* stream);
+
+/* Static text for a status code ("ok", "invalid argument", ...). */
+const char* attn_status_string(int status);
+
+/* Text of the last ATTN_ERR_HIP on the calling thread ("" if none). */
+const char* attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H_ */

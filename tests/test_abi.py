@@ -1,0 +1,136 @@
+"""The C ABI without a GPU: symbols, argument validation, one HIP runtime.
+
+Every call made here fails validation by construction (null pointers, bad
+sizes, bad dtype), so nothing is ever launched; the library promises to make
+no HIP call before validation passes.
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from exact_softmax_attention_attn_amd import binding, build_lib
+    if not os.path.exists(binding.LIB_PATH):
+        build_lib.build()
+    return binding.load()
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(attn_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert _declared() == sorted([
+        "attn_bwd", "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_preprocess",
+        "attn_bwd_workspace_bytes", "attn_fwd_lse", "attn_last_error", "attn_status_string"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    from exact_softmax_attention_attn_amd import binding
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH],
+                         stdout=subprocess.PIPE, text=True, check=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    for name in _declared():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_library_never_allocates_device_memory(lib):
+    # the caller owns every buffer: no allocation or free entry point is imported
+    from exact_softmax_attention_attn_amd import binding
+    out = subprocess.run(["nm", "-D", "--undefined-only", binding.LIB_PATH],
+                         stdout=subprocess.PIPE, text=True, check=True).stdout
+    imported = [line.split()[-1] for line in out.splitlines() if line.strip()]
+    bad = [s for s in imported if re.match(r"hip(Ext)?(Malloc|Free|MallocAsync|FreeAsync|HostMalloc)", s)]
+    assert bad == []
+
+
+def test_status_strings(lib):
+    assert lib.attn_status_string(0) == b"ok"
+    assert lib.attn_status_string(1) == b"invalid argument"
+    assert lib.attn_status_string(2).startswith(b"unsupported")
+    assert lib.attn_status_string(3).startswith(b"HIP")
+    assert lib.attn_status_string(99) == b"unknown status"
+    assert lib.attn_last_error() == b""
+
+
+def test_workspace_bytes(lib):
+    assert lib.attn_bwd_workspace_bytes(1, 16, 16384, 128) == 16 * 16384 * 4
+    assert lib.attn_bwd_workspace_bytes(3, 2, 8, 4) == 48 * 4
+    assert lib.attn_bwd_workspace_bytes(0, 2, 8, 4) == 0
+    assert lib.attn_bwd_workspace_bytes(1, 1, -5, 4) == 0
+
+
+FAKE = ctypes.c_void_p(0x10000)      # never dereferenced: every call below fails validation
+NUL = ctypes.c_void_p(0)
+MIS = ctypes.c_void_p(0x10008)       # not 16-byte aligned
+
+
+def _fwd(lib, ptrs, B=1, H=1, N=8, d=8, causal=1, scale=0.5, dtype=0):
+    return lib.attn_fwd_lse(*ptrs, B, H, N, d, causal, scale, dtype, NUL)
+
+
+def _bwd(lib, ptrs, B=1, H=1, N=8, d=8, causal=1, scale=0.5, dtype=0):
+    return lib.attn_bwd(*ptrs, B, H, N, d, causal, scale, dtype, NUL)
+
+
+def test_validation_rejects_bad_arguments_without_launching(lib):
+    f5 = [FAKE] * 5
+    b10 = [FAKE] * 10
+    # null or misaligned pointers
+    for i in range(5):
+        p = list(f5); p[i] = NUL
+        assert _fwd(lib, p, d=132) == 1           # pointer checked before d
+        p[i] = MIS
+        assert _fwd(lib, p, d=132) == 1
+    for i in range(10):
+        p = list(b10); p[i] = NUL
+        assert _bwd(lib, p, d=132) == 1
+    # sizes < 1
+    for kw in ({"B": 0}, {"H": 0}, {"N": 0}, {"d": 0}, {"N": -3}):
+        assert _fwd(lib, f5, **kw) == 1
+        assert _bwd(lib, b10, **kw) == 1
+    # scale and causal flag
+    for kw in ({"scale": 0.0}, {"scale": -1.0}, {"scale": float("inf")}, {"scale": float("nan")},
+               {"causal": 2}, {"causal": -1}):
+        assert _fwd(lib, f5, **kw) == 1
+        assert _bwd(lib, b10, **kw) == 1
+    # unsupported head dims and dtypes
+    for kw in ({"d": 136}, {"d": 6}, {"d": 4, "dtype": 1}, {"d": 12, "dtype": 1}, {"dtype": 2},
+               {"dtype": -1}, {"B": 70000}, {"H": 70000}, {"B": 65535, "H": 65535, "N": 1024}):
+        assert _fwd(lib, f5, **kw) == 2, kw
+        assert _bwd(lib, b10, **kw) == 2, kw
+    # the stage entry points validate the same way
+    assert lib.attn_bwd_preprocess(FAKE, NUL, FAKE, 1, 1, 8, 8, 0, NUL) == 1
+    assert lib.attn_bwd_preprocess(FAKE, FAKE, FAKE, 1, 1, 8, 6, 0, NUL) == 2
+    assert lib.attn_bwd_dkdv(*([FAKE] * 7), NUL, 1, 1, 8, 8, 1, 0.5, 0, NUL) == 1
+    assert lib.attn_bwd_dkdv(*([FAKE] * 8), 1, 1, 8, 8, 1, 0.0, 0, NUL) == 1
+    assert lib.attn_bwd_dq(*([FAKE] * 6), NUL, 1, 1, 8, 8, 1, 0.5, 0, NUL) == 1
+    assert lib.attn_bwd_dq(*([FAKE] * 7), 1, 1, 8, 256, 1, 0.5, 1, NUL) == 2
+    assert lib.attn_last_error() == b""
+
+
+def test_binding_marshals_and_checks_before_calling():
+    torch = pytest.importorskip("torch")
+    from exact_softmax_attention_attn_amd import binding
+    q = torch.zeros(1, 8, 1, 8)
+    with pytest.raises(ValueError):
+        binding.attn_fwd_lse(q, q, q)          # CPU tensors are refused before any call
+    with pytest.raises(TypeError):
+        binding._dtype_code(torch.zeros(1, dtype=torch.float16))
+
+
+def test_one_hip_runtime_is_mapped(lib):
+    maps = open("/proc/self/maps").read()
+    hip = set(l.split()[-1] for l in maps.splitlines() if "libamdhip64" in l)
+    assert len(hip) == 1, hip

@@ -1,0 +1,54 @@
+"""Seeded generators: determinism, recipes, bf16 rounding."""
+
+import math
+
+import numpy as np
+
+from exact_softmax_attention_attn_amd import workloads
+
+
+def test_five_workloads_with_their_shapes():
+    names = [w.name for w in workloads.WORKLOADS]
+    assert names == ["c1_tiny", "c2_nanogpt_cpu", "c3_single_seq", "c4_batched", "c5_long"]
+    assert workloads.get("c1_tiny").shape == (3, 8, 2, 4)
+    assert workloads.get("c2_nanogpt_cpu").shape == (12, 64, 4, 32)
+    assert workloads.get("c3_single_seq").shape == (1, 256, 1, 64)
+    assert workloads.get("c4_batched").shape == (4, 1024, 16, 64)
+    assert workloads.get("c5_long").shape == (1, 16384, 16, 128)
+    for w in workloads.WORKLOADS:
+        assert math.isclose(w.scale, 1 / math.sqrt(w.d)) or w.name == "c1_tiny"
+    assert workloads.get("c1_tiny").scale == 0.5
+
+
+def test_generators_are_deterministic_and_seed_dependent():
+    w = workloads.get("c2_nanogpt_cpu")
+    a = workloads.make_inputs(w, 0)
+    b = workloads.make_inputs(w, 0)
+    c = workloads.make_inputs(w, 1)
+    for k in "q", "k", "v", "do":
+        np.testing.assert_array_equal(a[k], b[k])
+        assert not np.array_equal(a[k], c[k])
+        assert a[k].dtype == np.float32 and a[k].shape == w.shape
+    assert abs(a["q"].std() - 1.0) < 0.02
+
+
+def test_bf16_workloads_hold_bf16_values():
+    w = workloads.get("c4_batched")
+    x = workloads.make_inputs(w, 0)
+    for k in "q", "k", "v", "do":
+        bits = x[k].view(np.uint32)
+        assert np.all(bits & 0xFFFF == 0)
+    assert abs(x["q"].std() - 0.5) < 0.01 and abs(x["do"].std() - 1.0) < 0.01
+
+
+def test_bf16_round_is_nearest_even():
+    # 1 + 2^-8 is halfway between bf16 neighbours 1 and 1 + 2^-7: ties go to even (1)
+    vals = np.array([1.0, 1 + 2 ** -8, 1 + 3 * 2 ** -8, 1 + 2 ** -8 + 2 ** -20, -2.5, 3.0e38],
+                    dtype=np.float64)
+    got = workloads.bf16_round(vals)
+    assert got[0] == 1.0
+    assert got[1] == 1.0
+    assert got[2] == 1 + 2 ** -6          # halfway, rounds to the even mantissa
+    assert got[3] == 1 + 2 ** -7
+    assert got[4] == -2.5
+    assert np.all(got.view(np.uint32) & 0xFFFF == 0)
