@@ -111,19 +111,19 @@ def main(argv=None):
     q, k, v, do = (torch.from_numpy(x[n]).to(dev).to(tdt) for n in ("q", "k", "v", "do"))
     o, lse = binding.attn_fwd_lse(q, k, v, causal=w.causal, scale=w.scale)
     dq, dk, dv = (torch.empty_like(q) for _ in range(3))
-    ws = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    ws = binding.new_workspace(w.B, w.H, w.N, dev)
     torch.cuda.synchronize()
 
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        binding.attn_bwd_preprocess(o, do, ws)
+        binding.attn_bwd_preprocess(o, do, lse, ws)
         if ev is not None:
             ev[1].record()
-        binding.attn_bwd_dkdv(q, k, v, do, lse, ws, dk, dv, causal=w.causal, scale=w.scale)
+        binding.attn_bwd_dkdv(q, k, v, do, ws, dk, dv, causal=w.causal, scale=w.scale)
         if ev is not None:
             ev[2].record()
-        binding.attn_bwd_dq(q, k, v, do, lse, ws, dq, causal=w.causal, scale=w.scale)
+        binding.attn_bwd_dq(q, k, v, do, ws, dq, causal=w.causal, scale=w.scale)
         if ev is not None:
             ev[3].record()
 

@@ -29,9 +29,9 @@ _SIGNATURES = {
     "attn_fwd_lse": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
     "attn_bwd_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "attn_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
-    "attn_bwd_preprocess": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P]),
-    "attn_bwd_dkdv": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
-    "attn_bwd_dq": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "attn_bwd_preprocess": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
+    "attn_bwd_dkdv": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "attn_bwd_dq": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
     "attn_status_string": (ctypes.c_char_p, [_I]),
     "attn_last_error": (ctypes.c_char_p, []),
 }
@@ -94,10 +94,16 @@ def _check_bnhd(*ts: torch.Tensor):
             raise ValueError("tensors must be contiguous HIP device tensors")
 
 
-def _check_rows(t: torch.Tensor, B: int, H: int, N: int, device):
-    if t.dtype != torch.float32 or tuple(t.shape) != (B, H, N) or not t.is_contiguous() \
+def _check_rows(t: torch.Tensor, B: int, H: int, N: int, device, lead=()):
+    shape = tuple(lead) + (B, H, N)
+    if t.dtype != torch.float32 or tuple(t.shape) != shape or not t.is_contiguous() \
             or t.device != device:
-        raise ValueError(f"expected a contiguous float32 [B, H, N] = {(B, H, N)} tensor on {device}")
+        raise ValueError(f"expected a contiguous float32 {shape} tensor on {device}")
+
+
+def new_workspace(B: int, H: int, N: int, device) -> torch.Tensor:
+    """Workspace for attn_bwd: [2, B, H, N] float32 (D, then L * log2(e))."""
+    return torch.empty((2, B, H, N), dtype=torch.float32, device=device)
 
 
 def _call(name: str, *args):
@@ -131,7 +137,7 @@ def attn_fwd_lse(q, k, v, causal: bool = True, scale: float | None = None, o=Non
 
 def attn_bwd(q, k, v, o, do, lse, causal: bool = True, scale: float | None = None,
              dq=None, dk=None, dv=None, workspace=None):
-    """dQ, dK, dV [B, N, H, d]; workspace (float32 [B, H, N]) ends up holding D."""
+    """dQ, dK, dV [B, N, H, d]; workspace ([2, B, H, N] float32) ends up holding D, L*log2(e)."""
     _check_bnhd(q, k, v, o, do)
     B, N, H, d = q.shape
     _check_rows(lse, B, H, N, q.device)
@@ -140,9 +146,8 @@ def attn_bwd(q, k, v, o, do, lse, causal: bool = True, scale: float | None = Non
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
     _check_bnhd(q, dq, dk, dv)
-    workspace = torch.empty((B, H, N), dtype=torch.float32, device=q.device) \
-        if workspace is None else workspace
-    _check_rows(workspace, B, H, N, q.device)
+    workspace = new_workspace(B, H, N, q.device) if workspace is None else workspace
+    _check_rows(workspace, B, H, N, q.device, lead=(2,))
     with torch.cuda.device(q.device):
         _call("attn_bwd", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
               _ptr(dk), _ptr(dv), _ptr(workspace), B, H, N, d, int(bool(causal)), scale,
@@ -150,37 +155,36 @@ def attn_bwd(q, k, v, o, do, lse, causal: bool = True, scale: float | None = Non
     return dq, dk, dv
 
 
-def attn_bwd_preprocess(o, do, workspace):
+def attn_bwd_preprocess(o, do, lse, workspace):
     _check_bnhd(o, do)
     B, N, H, d = o.shape
-    _check_rows(workspace, B, H, N, o.device)
+    _check_rows(lse, B, H, N, o.device)
+    _check_rows(workspace, B, H, N, o.device, lead=(2,))
     with torch.cuda.device(o.device):
-        _call("attn_bwd_preprocess", _ptr(o), _ptr(do), _ptr(workspace), B, H, N, d,
+        _call("attn_bwd_preprocess", _ptr(o), _ptr(do), _ptr(lse), _ptr(workspace), B, H, N, d,
               _dtype_code(o), _stream(o.device))
     return workspace
 
 
-def attn_bwd_dkdv(q, k, v, do, lse, workspace, dk, dv, causal: bool = True,
+def attn_bwd_dkdv(q, k, v, do, workspace, dk, dv, causal: bool = True,
                   scale: float | None = None):
     _check_bnhd(q, k, v, do, dk, dv)
     B, N, H, d = q.shape
-    _check_rows(lse, B, H, N, q.device)
-    _check_rows(workspace, B, H, N, q.device)
+    _check_rows(workspace, B, H, N, q.device, lead=(2,))
     scale = default_scale(d) if scale is None else float(scale)
     with torch.cuda.device(q.device):
-        _call("attn_bwd_dkdv", _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(workspace),
+        _call("attn_bwd_dkdv", _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(workspace),
               _ptr(dk), _ptr(dv), B, H, N, d, int(bool(causal)), scale, _dtype_code(q),
               _stream(q.device))
     return dk, dv
 
 
-def attn_bwd_dq(q, k, v, do, lse, workspace, dq, causal: bool = True, scale: float | None = None):
+def attn_bwd_dq(q, k, v, do, workspace, dq, causal: bool = True, scale: float | None = None):
     _check_bnhd(q, k, v, do, dq)
     B, N, H, d = q.shape
-    _check_rows(lse, B, H, N, q.device)
-    _check_rows(workspace, B, H, N, q.device)
+    _check_rows(workspace, B, H, N, q.device, lead=(2,))
     scale = default_scale(d) if scale is None else float(scale)
     with torch.cuda.device(q.device):
-        _call("attn_bwd_dq", _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(workspace),
+        _call("attn_bwd_dq", _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(workspace),
               _ptr(dq), B, H, N, d, int(bool(causal)), scale, _dtype_code(q), _stream(q.device))
     return dq

@@ -65,10 +65,10 @@ int check_ptrs(std::initializer_list<const void*> ps) {
   } while (0)
 
 attn::BwdArgs make_bwd(const void* Q, const void* K, const void* V, const void* dO,
-                       const float* L, const void* ws, void* dQ, void* dK, void* dV, int B,
-                       int H, int N, int d, int causal, float scale, int dtype) {
+                       const void* ws, void* dQ, void* dK, void* dV, int B, int H, int N, int d,
+                       int causal, float scale, int dtype) {
   attn::BwdArgs a;
-  a.Q = Q; a.K = K; a.V = V; a.dO = dO; a.L = L;
+  a.Q = Q; a.K = K; a.V = V; a.dO = dO;
   a.Dws = static_cast<const float*>(ws);
   a.dQ = dQ; a.dK = dK; a.dV = dV;
   a.B = B; a.H = H; a.N = N; a.d = d;
@@ -95,39 +95,39 @@ int attn_fwd_lse(const void* Q, const void* K, const void* V, void* O, float* L,
 
 size_t attn_bwd_workspace_bytes(int B, int H, int N, int d) {
   if (check_sizes(B, H, N, d) != ATTN_OK) return 0;
-  return (size_t)B * (size_t)H * (size_t)N * sizeof(float);
+  return 2 * (size_t)B * (size_t)H * (size_t)N * sizeof(float);
 }
 
-int attn_bwd_preprocess(const void* O, const void* dO, void* workspace, int B, int H, int N,
-                        int d, int dtype, void* stream) {
-  ATTN_TRY(check_ptrs({O, dO, workspace}));
+int attn_bwd_preprocess(const void* O, const void* dO, const float* L, void* workspace, int B,
+                        int H, int N, int d, int dtype, void* stream) {
+  ATTN_TRY(check_ptrs({O, dO, L, workspace}));
   ATTN_TRY(check_sizes(B, H, N, d));
   ATTN_TRY(check_dtype_dim(d, dtype));
-  return finish(attn::launch_bwd_preprocess(O, dO, static_cast<float*>(workspace), B, H, N, d,
+  return finish(attn::launch_bwd_preprocess(O, dO, L, static_cast<float*>(workspace), B, H, N, d,
                                             dtype, static_cast<hipStream_t>(stream)));
 }
 
-int attn_bwd_dkdv(const void* Q, const void* K, const void* V, const void* dO, const float* L,
+int attn_bwd_dkdv(const void* Q, const void* K, const void* V, const void* dO,
                   const void* workspace, void* dK, void* dV, int B, int H, int N, int d,
                   int causal, float scale, int dtype, void* stream) {
-  ATTN_TRY(check_ptrs({Q, K, V, dO, L, workspace, dK, dV}));
+  ATTN_TRY(check_ptrs({Q, K, V, dO, workspace, dK, dV}));
   ATTN_TRY(check_sizes(B, H, N, d));
   ATTN_TRY(check_scale_causal(scale, causal));
   ATTN_TRY(check_dtype_dim(d, dtype));
   const attn::BwdArgs a =
-      make_bwd(Q, K, V, dO, L, workspace, nullptr, dK, dV, B, H, N, d, causal, scale, dtype);
+      make_bwd(Q, K, V, dO, workspace, nullptr, dK, dV, B, H, N, d, causal, scale, dtype);
   return finish(attn::launch_bwd_dkdv(a, static_cast<hipStream_t>(stream)));
 }
 
-int attn_bwd_dq(const void* Q, const void* K, const void* V, const void* dO, const float* L,
+int attn_bwd_dq(const void* Q, const void* K, const void* V, const void* dO,
                 const void* workspace, void* dQ, int B, int H, int N, int d, int causal,
                 float scale, int dtype, void* stream) {
-  ATTN_TRY(check_ptrs({Q, K, V, dO, L, workspace, dQ}));
+  ATTN_TRY(check_ptrs({Q, K, V, dO, workspace, dQ}));
   ATTN_TRY(check_sizes(B, H, N, d));
   ATTN_TRY(check_scale_causal(scale, causal));
   ATTN_TRY(check_dtype_dim(d, dtype));
   const attn::BwdArgs a =
-      make_bwd(Q, K, V, dO, L, workspace, dQ, nullptr, nullptr, B, H, N, d, causal, scale, dtype);
+      make_bwd(Q, K, V, dO, workspace, dQ, nullptr, nullptr, B, H, N, d, causal, scale, dtype);
   return finish(attn::launch_bwd_dq(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -139,11 +139,11 @@ int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const v
   ATTN_TRY(check_scale_causal(scale, causal));
   ATTN_TRY(check_dtype_dim(d, dtype));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = attn::launch_bwd_preprocess(O, dO, static_cast<float*>(workspace), B, H, N, d,
-                                             dtype, s);
+  hipError_t e = attn::launch_bwd_preprocess(O, dO, L, static_cast<float*>(workspace), B, H, N,
+                                             d, dtype, s);
   if (e != hipSuccess) return finish(e);
   const attn::BwdArgs a =
-      make_bwd(Q, K, V, dO, L, workspace, dQ, dK, dV, B, H, N, d, causal, scale, dtype);
+      make_bwd(Q, K, V, dO, workspace, dQ, dK, dV, B, H, N, d, causal, scale, dtype);
   e = attn::launch_bwd_dkdv(a, s);
   if (e != hipSuccess) return finish(e);
   return finish(attn::launch_bwd_dq(a, s));

@@ -7,21 +7,29 @@
 // transpose causal attention's contractions without their joins", section
 // "What changed": transpose p = w/z per score, then p @ v).  The row-max
 // shift contributes nothing (issue #243, item 1), so dS = P o (dP - D).
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
 namespace attn {
 
+template <bool B> using bool_c = std::integral_constant<bool, B>;
+
 // ---------------------------------------------------------------------------
-// D[b, h, n] = sum_c dO[b, n, h, c] * O[b, n, h, c], float32.
-// 16 lanes per row, 16 rows per 256-thread block; 16-lane shuffle reduction.
+// Preprocess.  D[b, h, n] = sum_c dO[b, n, h, c] * O[b, n, h, c] in float32
+// (the softmax-weighted sum of dP, since sum_j P_ij dP_ij = dO_i . O_i), and
+// L2[b, h, n] = L[b, h, n] * log2(e), the row scalar in the base-2 units the
+// kernels exponentiate in.  16 lanes per row, 16 rows per 256-thread block.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_preprocess_kernel(const T* __restrict__ O,
                                                              const T* __restrict__ dO,
-                                                             float* __restrict__ Dout, int B, int H,
-                                                             int N, int d) {
-  constexpr int VEC = Mma<T>::VEC;
+                                                             const float* __restrict__ L,
+                                                             float* __restrict__ Dout,
+                                                             float* __restrict__ L2out, int B,
+                                                             int H, int N, int d) {
+  constexpr int VEC = Mma<T>::CHUNK;
   const int sub = threadIdx.x & 15;
   const long row = (long)blockIdx.x * 16 + (threadIdx.x >> 4);  // row = (b * N + n) * H + h
   const long rows = (long)B * N * H;
@@ -50,49 +58,53 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(const T* __restrict
     const long bn = row / H;
     const int n = (int)(bn % N);
     const int b = (int)(bn / N);
-    Dout[((long)b * H + h) * N + n] = acc;
+    const long i = ((long)b * H + h) * N + n;
+    Dout[i] = acc;
+    L2out[i] = L[i] * kLog2e;
   }
 }
 
 // ---------------------------------------------------------------------------
 // dK, dV.  Workgroup = 4 waves = one block of 128 key rows of one (b, h);
-// wave w owns key rows kv0 + [0, 32).  K and V of those rows live in
-// registers as B operands of S = Q K^T and dP = dO V^T (column n = key row).
-// The accumulators hold dV^T and dK^T (rows = head dim, columns = key rows).
-// Query blocks of 64 rows are staged in LDS (row-major for the contractions
-// over the head dim, transposed for the contractions over positions).
+// wave w owns key rows kv0 + [0, 32).  K and V of those rows sit in
+// registers as B operands of S = Q K^T and dP = dO V^T (column n = key row),
+// so P and dS come out with the query rows along the registers and feed
+// dV^T += dO^T P and dK^T += Q^T dS directly.  The accumulators hold dV^T
+// and dK^T (rows = head dim, columns = key rows).  Query blocks of 64 rows
+// (Q, dO and their L2, D) are double-buffered in LDS: the next block is
+// copied in while the current one is consumed.  Causal: the walk starts at
+// the diagonal; only the two diagonal blocks carry the element mask.
 // ---------------------------------------------------------------------------
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
-    const T* __restrict__ dO, const float* __restrict__ L, const float* __restrict__ Dws,
+    const T* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dws,
     T* __restrict__ dK, T* __restrict__ dV, int H, int N, int d, float scale_log2, float scale) {
   using M = Mma<T>;
   using frag = typename M::frag;
   constexpr int BKV = 128, BQ = 64, KS = D / M::K, MT = D / 32, RS = 32 / M::K;
-  using QTile = Tile<T, BQ, D, sizeof(T) == 2>;
-
-  __shared__ __align__(16) unsigned char smem[2 * QTile::BYTES + 2 * BQ * sizeof(float)];
-  T* sbase = reinterpret_cast<T*>(smem);
-  const QTile qs{sbase, sbase + QTile::RM_ELEMS};
-  const QTile dos{sbase + QTile::RM_ELEMS + QTile::TR_ELEMS,
-                  sbase + 2 * QTile::RM_ELEMS + QTile::TR_ELEMS};
-  float* sL = reinterpret_cast<float*>(smem + 2 * QTile::BYTES);
-  float* sD = sL + BQ;
+  using QT = Tile<T, BQ, D>;
+  struct __align__(16) Buf {
+    T q[QT::ELEMS];
+    T o[QT::ELEMS];
+    float l[BQ];
+    float dd[BQ];
+  };
+  __shared__ Buf bufA, bufB;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
   const int jb = blockIdx.x, head = blockIdx.y, b = blockIdx.z;
-  const int H_ = H;
-  const long rs = (long)H_ * d;                       // elements between positions
-  const long base = ((long)b * N * H_ + head) * d;    // (b, 0, head, 0)
-  const float* Lh = L + ((long)b * H_ + head) * N;
-  const float* Dh = Dws + ((long)b * H_ + head) * N;
+  const long rs = (long)H * d;                       // elements between positions
+  const long base = ((long)b * N * H + head) * d;    // (b, 0, head, 0)
+  const float* Lh = L2 + ((long)b * H + head) * N;
+  const float* Dh = Dws + ((long)b * H + head) * N;
 
   const int kvb = jb * BKV;
   const int kv0 = kvb + wave * 32;
+  const int kv = kv0 + l32;                          // this lane's key row
   frag kf[KS], vf[KS];
-  load_row_frags<T, D>(kf, K + base, rs, kv0 + l32, N, d, h);
-  load_row_frags<T, D>(vf, V + base, rs, kv0 + l32, N, d, h);
+  load_row_frags<T, D>(kf, K + base, rs, kv, N, d, h);
+  load_row_frags<T, D>(vf, V + base, rs, kv, N, d, h);
 
   f32x16 dv_acc[MT], dk_acc[MT];
 #pragma unroll
@@ -100,50 +112,104 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 
   const int nqt = (N + BQ - 1) / BQ;
   const int qt0 = CAUSAL ? kvb / BQ : 0;
-  for (int qt = qt0; qt < nqt; ++qt) {
+
+  auto fill = [&](Buf& B, int qt) {
     const int q0 = qt * BQ;
-    __syncthreads();
-    qs.template stage<256>(Q + base, rs, q0, N, d, tid);
-    dos.template stage<256>(dO + base, rs, q0, N, d, tid);
+    if constexpr (sizeof(T) == 2) {
+      if (q0 + BQ <= N && d == D) {
+        fill_async(QT{B.q}, Q + base, rs, q0, wave, lane);
+        fill_async(QT{B.o}, dO + base, rs, q0, wave, lane);
+        if (wave == 0) fill_async_row64(B.l, Lh + q0);
+        if (wave == 1) fill_async_row64(B.dd, Dh + q0);
+        return;
+      }
+    }
+    fill_sync(QT{B.q}, Q + base, rs, q0, N, d, tid);
+    fill_sync(QT{B.o}, dO + base, rs, q0, N, d, tid);
     if (tid < BQ) {
       const int q = q0 + tid;
-      sL[tid] = q < N ? Lh[q] * kLog2e : __builtin_inff();
-      sD[tid] = q < N ? Dh[q] : 0.f;
+      B.l[tid] = q < N ? Lh[q] : __builtin_inff();   // padded rows: P = 0
+      B.dd[tid] = q < N ? Dh[q] : 0.f;
     }
-    __syncthreads();
+  };
+
+  auto body = [&](const Buf& B, int q0, auto masked_c) {
+    constexpr bool MASKED = decltype(masked_c)::value;
+    const QT qt_{const_cast<T*>(B.q)}, ot_{const_cast<T*>(B.o)};
 #pragma unroll
     for (int st = 0; st < BQ / 32; ++st) {
-      const int qa = q0 + st * 32;                       // first query row of the sub-tile
-      if (CAUSAL && qa + 31 < kv0) continue;             // every pair above the diagonal
+      const int qa = q0 + st * 32;                 // first query row of the sub-tile
+      if (MASKED && qa + 31 < kv0) continue;       // every pair above the diagonal
+      // S and dP: register r = query row qa + acc_row(r, h), column = key row kv
+      frag aq[KS], ao[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) aq[ks] = qt_.along_cols(st * 32 + l32, ks, h);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) ao[ks] = ot_.along_cols(st * 32 + l32, ks, h);
       f32x16 s = zero16(), dp = zero16();
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        s = M::mma(qs.along_cols(st * 32 + l32, ks, h), kf[ks], s);
-        dp = M::mma(dos.along_cols(st * 32 + l32, ks, h), vf[ks], dp);
-      }
-      // s, dp: register r = query row qa + acc_row(r, h), column = key row kv0 + l32
-      const bool diag = CAUSAL && (qa < kv0 + 32);
-      const int kv = kv0 + l32;
+      for (int ks = 0; ks < KS; ++ks) s = M::mma(aq[ks], kf[ks], s);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qi = st * 32 + acc_row(r, h);
-        float p = fast_exp2(s[r] * scale_log2 - sL[qi]);
-        if (diag && kv > q0 + qi) p = 0.f;
-        s[r] = p;
-        dp[r] = p * (dp[r] - sD[qi]);
-      }
+      for (int ks = 0; ks < KS; ++ks) dp = M::mma(ao[ks], vf[ks], dp);
+      // P = exp2(S * scale * log2 e - L2), masked above the diagonal
 #pragma unroll
-      for (int ss = 0; ss < RS; ++ss) {
-        const frag bp = M::pack(s, ss);
-        const frag bds = M::pack(dp, ss);
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 lg = *reinterpret_cast<const f32x4*>(&B.l[st * 32 + 8 * g + 4 * h]);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          dv_acc[mt] = M::mma(dos.along_rows(mt * 32 + l32, st * 32, ss, h), bp, dv_acc[mt]);
-          dk_acc[mt] = M::mma(qs.along_rows(mt * 32 + l32, st * 32, ss, h), bds, dk_acc[mt]);
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * g + i;
+          float p = fast_exp2(__builtin_fmaf(s[r], scale_log2, -lg[i]));
+          if (MASKED && kv > qa + acc_row(r, h)) p = 0.f;
+          s[r] = p;
         }
       }
+      frag bp[RS];
+#pragma unroll
+      for (int ss = 0; ss < RS; ++ss) bp[ss] = M::pack(s, ss);
+      // dV^T += dO^T P
+#pragma unroll
+      for (int ss = 0; ss < RS; ++ss)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          dv_acc[mt] = M::mma(ot_.along_rows(mt * 32 + l32, st * 32, ss, h), bp[ss], dv_acc[mt]);
+      // dS = P o (dP - D)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 dg = *reinterpret_cast<const f32x4*>(&B.dd[st * 32 + 8 * g + 4 * h]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dp[4 * g + i] = s[4 * g + i] * (dp[4 * g + i] - dg[i]);
+      }
+      frag bds[RS];
+#pragma unroll
+      for (int ss = 0; ss < RS; ++ss) bds[ss] = M::pack(dp, ss);
+      // dK^T += Q^T dS
+#pragma unroll
+      for (int ss = 0; ss < RS; ++ss)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          dk_acc[mt] = M::mma(qt_.along_rows(mt * 32 + l32, st * 32, ss, h), bds[ss], dk_acc[mt]);
     }
+  };
+
+  auto step = [&](const Buf& cur, Buf& nxt, int qt) {
+    if (qt + 1 < nqt) fill(nxt, qt + 1);
+    const int q0 = qt * BQ;
+    if (CAUSAL && q0 < kvb + BKV)
+      body(cur, q0, bool_c<true>{});
+    else
+      body(cur, q0, bool_c<false>{});
+    wait_async_fills();
+    __syncthreads();
+  };
+
+  fill(bufA, qt0);
+  wait_async_fills();
+  __syncthreads();
+  for (int qt = qt0; qt < nqt; qt += 2) {
+    step(bufA, bufB, qt);
+    if (qt + 1 < nqt) step(bufB, bufA, qt + 1);
   }
+
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     store_acc_transposed<T>(dv_acc[mt], dV + base, rs, kv0, mt * 32, N, d, 1.f, lane);
@@ -153,26 +219,26 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 
 // ---------------------------------------------------------------------------
 // dQ.  Workgroup = 4 waves = one block of 128 query rows of one (b, h); wave
-// w owns query rows q0 + [0, 32), whose Q and dO sit in registers as B
-// operands of S^T = K Q^T and dP^T = V dO^T (column n = query row), so L and
-// D are one scalar per lane.  Key blocks of 64 rows are staged in LDS.  The
-// accumulator holds dQ^T; every dQ element is written once, no atomics.
+// w owns query rows qw + [0, 32), whose Q and dO sit in registers as B
+// operands of S^T = K Q^T and dP^T = V dO^T (column n = query row), so L2 and
+// D are one scalar per lane and dS^T comes out with the key rows along the
+// registers, ready for dQ^T += K^T dS^T.  Key blocks of 64 rows (K, V) are
+// double-buffered in LDS.  Every dQ element is written once: no atomics.
 // ---------------------------------------------------------------------------
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
-    const T* __restrict__ dO, const float* __restrict__ L, const float* __restrict__ Dws,
+    const T* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dws,
     T* __restrict__ dQ, int H, int N, int d, float scale_log2, float scale) {
   using M = Mma<T>;
   using frag = typename M::frag;
   constexpr int BQ = 128, BKV = 64, KS = D / M::K, MT = D / 32, RS = 32 / M::K;
-  using KTile = Tile<T, BKV, D, sizeof(T) == 2>;
-  using VTile = Tile<T, BKV, D, false>;
-
-  __shared__ __align__(16) unsigned char smem[KTile::BYTES + VTile::BYTES];
-  T* sbase = reinterpret_cast<T*>(smem);
-  const KTile ks_{sbase, sbase + KTile::RM_ELEMS};
-  const VTile vs_{sbase + KTile::RM_ELEMS + KTile::TR_ELEMS, nullptr};
+  using KT = Tile<T, BKV, D>;
+  struct __align__(16) Buf {
+    T k[KT::ELEMS];
+    T v[KT::ELEMS];
+  };
+  __shared__ Buf bufA, bufB;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
   const int nqb = gridDim.x;
@@ -180,7 +246,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
   const int head = blockIdx.y, b = blockIdx.z;
   const long rs = (long)H * d;
   const long base = ((long)b * N * H + head) * d;
-  const float* Lh = L + ((long)b * H + head) * N;
+  const float* Lh = L2 + ((long)b * H + head) * N;
   const float* Dh = Dws + ((long)b * H + head) * N;
 
   const int qb = ib * BQ;
@@ -189,7 +255,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
   frag qf[KS], of[KS];
   load_row_frags<T, D>(qf, Q + base, rs, q, N, d, h);
   load_row_frags<T, D>(of, dO + base, rs, q, N, d, h);
-  const float Lq = q < N ? Lh[q] * kLog2e : __builtin_inff();
+  const float Lq = q < N ? Lh[q] : __builtin_inff();
   const float Dq = q < N ? Dh[q] : 0.f;
 
   f32x16 acc[MT];
@@ -198,38 +264,72 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
 
   const int kv_end = CAUSAL ? min(N, qb + BQ) : N;
   const int nkt = (kv_end + BKV - 1) / BKV;
-  for (int kt = 0; kt < nkt; ++kt) {
+
+  auto fill = [&](Buf& B, int kt) {
     const int k0 = kt * BKV;
-    __syncthreads();
-    ks_.template stage<256>(K + base, rs, k0, N, d, tid);
-    vs_.template stage<256>(V + base, rs, k0, N, d, tid);
-    __syncthreads();
+    if constexpr (sizeof(T) == 2) {
+      if (k0 + BKV <= N && d == D) {
+        fill_async(KT{B.k}, K + base, rs, k0, wave, lane);
+        fill_async(KT{B.v}, V + base, rs, k0, wave, lane);
+        return;
+      }
+    }
+    fill_sync(KT{B.k}, K + base, rs, k0, N, d, tid);
+    fill_sync(KT{B.v}, V + base, rs, k0, N, d, tid);
+  };
+
+  auto body = [&](const Buf& B, int k0, auto masked_c) {
+    constexpr bool MASKED = decltype(masked_c)::value;
+    const KT kt_{const_cast<T*>(B.k)}, vt_{const_cast<T*>(B.v)};
 #pragma unroll
     for (int st = 0; st < BKV / 32; ++st) {
       const int ka = k0 + st * 32;
-      if (CAUSAL && ka > qw + 31) continue;
+      if (MASKED && ka > qw + 31) continue;        // every pair above the diagonal
+      frag ak[KS], av[KS];
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) ak[kk] = kt_.along_cols(st * 32 + l32, kk, h);
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) av[kk] = vt_.along_cols(st * 32 + l32, kk, h);
       f32x16 s = zero16(), dp = zero16();
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
-        s = M::mma(ks_.along_cols(st * 32 + l32, kk, h), qf[kk], s);
-        dp = M::mma(vs_.along_cols(st * 32 + l32, kk, h), of[kk], dp);
-      }
+      for (int kk = 0; kk < KS; ++kk) s = M::mma(ak[kk], qf[kk], s);
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) dp = M::mma(av[kk], of[kk], dp);
       // register r = key row ka + acc_row(r, h), column = query row q
-      const bool diag = CAUSAL && (ka + 31 > qw);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float p = fast_exp2(s[r] * scale_log2 - Lq);
-        if (diag && ka + acc_row(r, h) > q) p = 0.f;
+        float p = fast_exp2(__builtin_fmaf(s[r], scale_log2, -Lq));
+        if (MASKED && ka + acc_row(r, h) > q) p = 0.f;
         dp[r] = p * (dp[r] - Dq);
       }
+      frag bds[RS];
 #pragma unroll
-      for (int ss = 0; ss < RS; ++ss) {
-        const frag bds = M::pack(dp, ss);
+      for (int ss = 0; ss < RS; ++ss) bds[ss] = M::pack(dp, ss);
+#pragma unroll
+      for (int ss = 0; ss < RS; ++ss)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
-          acc[mt] = M::mma(ks_.along_rows(mt * 32 + l32, st * 32, ss, h), bds, acc[mt]);
-      }
+          acc[mt] = M::mma(kt_.along_rows(mt * 32 + l32, st * 32, ss, h), bds[ss], acc[mt]);
     }
+  };
+
+  auto step = [&](const Buf& cur, Buf& nxt, int kt) {
+    if (kt + 1 < nkt) fill(nxt, kt + 1);
+    const int k0 = kt * BKV;
+    if (CAUSAL && k0 + BKV - 1 > qb)
+      body(cur, k0, bool_c<true>{});
+    else
+      body(cur, k0, bool_c<false>{});
+    wait_async_fills();
+    __syncthreads();
+  };
+
+  fill(bufA, 0);
+  wait_async_fills();
+  __syncthreads();
+  for (int kt = 0; kt < nkt; kt += 2) {
+    step(bufA, bufB, kt);
+    if (kt + 1 < nkt) step(bufB, bufA, kt + 1);
   }
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
@@ -240,27 +340,30 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
 // Launchers
 // ---------------------------------------------------------------------------
 template <typename T>
-hipError_t launch_bwd_preprocess_t(const void* O, const void* dO, float* Dws, int B, int H, int N,
-                                   int d, hipStream_t stream) {
+hipError_t launch_bwd_preprocess_t(const void* O, const void* dO, const float* L, float* ws, int B,
+                                   int H, int N, int d, hipStream_t stream) {
   const long rows = (long)B * N * H;
   const unsigned grid = (unsigned)((rows + 15) / 16);
   hipLaunchKernelGGL(bwd_preprocess_kernel<T>, dim3(grid), dim3(256), 0, stream,
-                     static_cast<const T*>(O), static_cast<const T*>(dO), Dws, B, H, N, d);
+                     static_cast<const T*>(O), static_cast<const T*>(dO), L, ws, ws + rows, B, H,
+                     N, d);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_preprocess(const void* O, const void* dO, float* Dws, int B, int H, int N,
-                                 int d, int dtype, hipStream_t stream) {
-  if (dtype == 1) return launch_bwd_preprocess_t<bf16>(O, dO, Dws, B, H, N, d, stream);
-  return launch_bwd_preprocess_t<float>(O, dO, Dws, B, H, N, d, stream);
+hipError_t launch_bwd_preprocess(const void* O, const void* dO, const float* L, float* ws, int B,
+                                 int H, int N, int d, int dtype, hipStream_t stream) {
+  if (dtype == 1) return launch_bwd_preprocess_t<bf16>(O, dO, L, ws, B, H, N, d, stream);
+  return launch_bwd_preprocess_t<float>(O, dO, L, ws, B, H, N, d, stream);
 }
+
+static inline long rows_of(const BwdArgs& a) { return (long)a.B * a.H * a.N; }
 
 template <typename T, int D, bool C>
 static hipError_t dkdv_go(const BwdArgs& a, hipStream_t stream) {
   dim3 grid((a.N + 127) / 128, a.H, a.B);
   hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, C>), grid, dim3(256), 0, stream,
                      static_cast<const T*>(a.Q), static_cast<const T*>(a.K),
-                     static_cast<const T*>(a.V), static_cast<const T*>(a.dO), a.L, a.Dws,
+                     static_cast<const T*>(a.V), static_cast<const T*>(a.dO), a.Dws + rows_of(a), a.Dws,
                      static_cast<T*>(a.dK), static_cast<T*>(a.dV), a.H, a.N, a.d,
                      a.scale * kLog2e, a.scale);
   return hipGetLastError();
@@ -271,7 +374,7 @@ static hipError_t dq_go(const BwdArgs& a, hipStream_t stream) {
   dim3 grid((a.N + 127) / 128, a.H, a.B);
   hipLaunchKernelGGL((bwd_dq_kernel<T, D, C>), grid, dim3(256), 0, stream,
                      static_cast<const T*>(a.Q), static_cast<const T*>(a.K),
-                     static_cast<const T*>(a.V), static_cast<const T*>(a.dO), a.L, a.Dws,
+                     static_cast<const T*>(a.V), static_cast<const T*>(a.dO), a.Dws + rows_of(a), a.Dws,
                      static_cast<T*>(a.dQ), a.H, a.N, a.d, a.scale * kLog2e, a.scale);
   return hipGetLastError();
 }

@@ -5,6 +5,8 @@
 // repro script, CTEs scores / weights / norm / heads); L is the one number
 // per row that ddx issue #243 (item 2) says the backward needs to rebuild the
 // scores.  The row max and sum are kept online across key blocks.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -14,8 +16,8 @@ namespace attn {
 // owns query rows qw + [0, 32); its Q rows sit in registers as the B operand
 // of S^T = K Q^T, so each lane owns one query row (column of S^T) and the row
 // max / row sum reduce over the lane's 16 registers plus its partner lane in
-// the other half-wave.  Key blocks of 64 rows are staged in LDS: K
-// row-major, V in the layout the contraction over keys reads.
+// the other half-wave.  P^T then feeds O^T += V^T P^T straight from the
+// registers.  Key blocks of 64 rows (K, V) are double-buffered in LDS.
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void fwd_lse_kernel(const T* __restrict__ Q,
                                                          const T* __restrict__ K,
@@ -25,13 +27,12 @@ __global__ __launch_bounds__(256, 1) void fwd_lse_kernel(const T* __restrict__ Q
   using M = Mma<T>;
   using frag = typename M::frag;
   constexpr int BQ = 128, BKV = 64, KS = D / M::K, MT = D / 32, RS = 32 / M::K;
-  using KTile = Tile<T, BKV, D, false>;
-  using VTile = Tile<T, BKV, D, sizeof(T) == 2>;
-
-  __shared__ __align__(16) unsigned char smem[KTile::BYTES + VTile::BYTES];
-  T* sbase = reinterpret_cast<T*>(smem);
-  const KTile ks_{sbase, nullptr};
-  const VTile vs_{sbase + KTile::RM_ELEMS, sbase + KTile::RM_ELEMS + VTile::RM_ELEMS};
+  using KT = Tile<T, BKV, D>;
+  struct __align__(16) Buf {
+    T k[KT::ELEMS];
+    T v[KT::ELEMS];
+  };
+  __shared__ Buf bufA, bufB;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
   const int nqb = gridDim.x;
@@ -54,26 +55,39 @@ __global__ __launch_bounds__(256, 1) void fwd_lse_kernel(const T* __restrict__ Q
 
   const int kv_end = CAUSAL ? min(N, qb + BQ) : N;
   const int nkt = (kv_end + BKV - 1) / BKV;
-  for (int kt = 0; kt < nkt; ++kt) {
+
+  auto fill = [&](Buf& B, int kt) {
     const int k0 = kt * BKV;
-    __syncthreads();
-    ks_.template stage<256>(K + base, rs, k0, N, d, tid);
-    vs_.template stage<256>(V + base, rs, k0, N, d, tid);
-    __syncthreads();
+    if constexpr (sizeof(T) == 2) {
+      if (k0 + BKV <= N && d == D) {
+        fill_async(KT{B.k}, K + base, rs, k0, wave, lane);
+        fill_async(KT{B.v}, V + base, rs, k0, wave, lane);
+        return;
+      }
+    }
+    fill_sync(KT{B.k}, K + base, rs, k0, N, d, tid);
+    fill_sync(KT{B.v}, V + base, rs, k0, N, d, tid);
+  };
+
+  auto body = [&](const Buf& B, int k0, auto masked_c) {
+    constexpr bool MASKED = decltype(masked_c)::value;
+    const KT kt_{const_cast<T*>(B.k)}, vt_{const_cast<T*>(B.v)};
 #pragma unroll
     for (int st = 0; st < BKV / 32; ++st) {
       const int ka = k0 + st * 32;
-      if (CAUSAL && ka > qw + 31) continue;
+      if (MASKED && CAUSAL && ka > qw + 31) continue;
       f32x16 s = zero16();
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk) s = M::mma(ks_.along_cols(st * 32 + l32, kk, h), qf[kk], s);
+      for (int kk = 0; kk < KS; ++kk) s = M::mma(kt_.along_cols(st * 32 + l32, kk, h), qf[kk], s);
       // register r = key row ka + acc_row(r, h), column = query row q
       float mx = -__builtin_inff();
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int kv = ka + acc_row(r, h);
         float x = s[r] * scale_log2;
-        if ((CAUSAL && kv > q) || kv >= N) x = -__builtin_inff();
+        if (MASKED) {
+          const int kv = ka + acc_row(r, h);
+          if ((CAUSAL && kv > q) || kv >= N) x = -__builtin_inff();
+        }
         s[r] = x;
         mx = fmaxf(mx, x);
       }
@@ -97,9 +111,28 @@ __global__ __launch_bounds__(256, 1) void fwd_lse_kernel(const T* __restrict__ Q
         const frag bp = M::pack(s, ss);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
-          acc[mt] = M::mma(vs_.along_rows(mt * 32 + l32, st * 32, ss, h), bp, acc[mt]);
+          acc[mt] = M::mma(vt_.along_rows(mt * 32 + l32, st * 32, ss, h), bp, acc[mt]);
       }
     }
+  };
+
+  auto step = [&](const Buf& cur, Buf& nxt, int kt) {
+    if (kt + 1 < nkt) fill(nxt, kt + 1);
+    const int k0 = kt * BKV;
+    if ((CAUSAL && k0 + BKV - 1 > qb) || k0 + BKV > N)
+      body(cur, k0, std::integral_constant<bool, true>{});
+    else
+      body(cur, k0, std::integral_constant<bool, false>{});
+    wait_async_fills();
+    __syncthreads();
+  };
+
+  fill(bufA, 0);
+  wait_async_fills();
+  __syncthreads();
+  for (int kt = 0; kt < nkt; kt += 2) {
+    step(bufA, bufB, kt);
+    if (kt + 1 < nkt) step(bufB, bufA, kt + 1);
   }
   const float inv = 1.f / l;
 #pragma unroll

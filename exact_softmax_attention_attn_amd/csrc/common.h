@@ -1,14 +1,14 @@
 // Device-side building blocks shared by the attention kernels (gfx950 only).
 //
-// Matrix-core conventions used throughout (CDNA3/CDNA4 32x32 MFMA, wave64):
+// Matrix-core conventions used throughout (32x32 MFMA, wave64):
 //   lane l, half h = l / 32, l32 = l % 32
-//   A operand (32 x K): lane holds row m = l32, K-slots of half h
-//   B operand (K x 32): lane holds column n = l32, K-slots of half h
+//   A operand (32 x K): lane holds row m = l32, the K slots of half h
+//   B operand (K x 32): lane holds column n = l32, the K slots of half h
 //   C/D (32 x 32), 16 floats per lane: register r holds
 //        row m = 8 * (r / 4) + 4 * h + (r % 4), column n = l32
-// A and B only need to agree on which logical K index sits in each
-// (half, slot); the hardware then sums over all of them.  That freedom lets a
-// C accumulator feed the B operand of the next product directly: its rows
+// A and B only have to agree on which logical K index sits in each
+// (half, slot); the hardware sums over all of them.  That freedom lets an
+// accumulator feed the B operand of the next product directly: its rows
 // become the K dimension, in the order the registers hold them.
 #pragma once
 
@@ -20,182 +20,209 @@ namespace attn {
 typedef __bf16 bf16;
 typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kThreads = 256;   // every attention kernel runs 4 waves per workgroup
 
-__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+// Row (within a 32-row accumulator block) held by accumulator register r in half h.
+__device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---------------------------------------------------------------------------
 // Element type traits: which 32x32 MFMA, how deep one instruction contracts,
-// how fragments are packed.
+// how accumulator registers become a B operand.
 // ---------------------------------------------------------------------------
 template <typename T> struct Mma;
 
 template <> struct Mma<bf16> {
   using frag = bf16x8;
+  using chunk = bf16x8;                  // 16 bytes of a row
   static constexpr int K = 16;           // v_mfma_f32_32x32x16_bf16
-  static constexpr int VEC = 8;          // elements per 16-byte global access
+  static constexpr int CHUNK = 8;        // elements per 16-byte chunk
   static __device__ __forceinline__ f32x16 mma(frag a, frag b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
-  // B fragment for K step s taken from accumulator registers 8s .. 8s+7
+  // B fragment for K step s from accumulator registers 8s .. 8s+7 (rounded to
+  // nearest even), i.e. rows 16 s + 8 (t / 4) + 4 h + (t % 4) of the block.
   static __device__ __forceinline__ frag pack(const f32x16& c, int s) {
     frag f;
 #pragma unroll
     for (int t = 0; t < 8; ++t) f[t] = (bf16)c[8 * s + t];
     return f;
   }
-  static __device__ __forceinline__ frag zero() { return frag{}; }
 };
 
 template <> struct Mma<float> {
   using frag = float;
+  using chunk = f32x4;
   static constexpr int K = 2;            // v_mfma_f32_32x32x2_f32
-  static constexpr int VEC = 4;
+  static constexpr int CHUNK = 4;
   static __device__ __forceinline__ f32x16 mma(frag a, frag b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
   }
+  // step s uses accumulator register s: row acc_row(s, h) of the block
   static __device__ __forceinline__ frag pack(const f32x16& c, int s) { return c[s]; }
-  static __device__ __forceinline__ frag zero() { return 0.f; }
 };
 
-// Row index (within a 32-row accumulator block) of K slot t, step s, half h,
-// when accumulator registers are used as a B operand.  bf16: slots 0..7 of
-// step s are registers 8s+t; f32: the single slot of step s is register s.
-__device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
-
 // ---------------------------------------------------------------------------
-// A ROWS x D tile staged in LDS.
-//   rm: row-major, row stride LDR (padding keeps 32 lanes reading 32
-//       different rows on distinct banks).
-//   tr: (bf16 only) the transpose, D rows of ROWS entries, stride LDT, with
-//       the row index XOR-swizzled by 4 * ((c >> 5) & 3) so that the staging
-//       writes of 16 neighbouring column groups land on distinct banks.
-// along_cols(): operand whose K slots run along a row (contraction over the
-//               tile's columns, e.g. over the head dim).
-// along_rows(): operand whose K slots run down a column, in the order the
-//               accumulator registers of a 32-row block hold their rows
-//               (contraction over the tile's rows, e.g. over positions).
+// A ROWS x D tile of a [pos, row_stride] global matrix staged in LDS.
+//
+// bf16: row-major, 16-byte chunks permuted within each row: logical chunk c
+// of row r sits at chunk c ^ swz(r).
+//   - along_cols (ds_read_b128, 32 lanes on 32 rows, one chunk): any 16
+//     consecutive rows hit 16 distinct chunk slots, i.e. all 64 banks once.
+//   - along_rows (ds_read_b64_tr_b16): a 16-lane group reads 4 consecutive
+//     rows x 2 neighbouring chunks; the 8 slots are distinct.
+// f32: row-major with 4 floats of padding per row (a 1-float fragment reads
+//   any layout in one access).
+//
+// along_cols(r, ks, h): operand with K slots along row r (contraction over
+//   the tile's columns, e.g. the head dim), K step ks.
+// along_rows(c, r0, s, h): operand with K slots down column c, rows in the
+//   order the accumulator registers of the 32-row block at r0 hold them (see
+//   Mma::pack), K step s (contraction over the tile's rows, e.g. positions).
 // ---------------------------------------------------------------------------
-template <typename T, int ROWS, int D, bool TRANS> struct Tile;
+template <typename T, int ROWS, int D> struct Tile;
 
-template <int ROWS, int D, bool TRANS> struct Tile<bf16, ROWS, D, TRANS> {
-  static constexpr int LDR = D + 8;
-  static constexpr int LDT = ROWS + 4;
-  static constexpr int RM_ELEMS = ROWS * LDR;
-  static constexpr int TR_ELEMS = TRANS ? D * LDT : 0;
-  static constexpr int BYTES = (RM_ELEMS + TR_ELEMS) * 2;
-  bf16* rm;
-  bf16* tr;
+template <int ROWS, int D> struct Tile<bf16, ROWS, D> {
+  static constexpr int ELEMS = ROWS * D;
+  static constexpr int BYTES = ELEMS * 2;
+  static constexpr int CPR = D / 8;                       // chunks per row
+  static_assert(CPR >= 4 && (CPR & (CPR - 1)) == 0, "head-dim bucket must be 32, 64 or 128");
+  bf16* p;
 
-  __device__ __forceinline__ static int swz(int c) { return ((c >> 5) & 3) << 2; }
-
+  // Bank slot of (row, physical chunk) = (row % (16 / CPR)) * CPR + chunk; the
+  // permutation keeps 16 consecutive rows on 16 distinct slots for one logical
+  // chunk, and 4 consecutive rows x 2 neighbouring chunks on 8 distinct slots.
+  __device__ __forceinline__ static int swz(int r) {
+    if constexpr (CPR == 16) return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8);
+    else if constexpr (CPR == 8) return (r & 2) | ((r >> 2) & 1) | ((r >> 1) & 4);
+    else return (r >> 2) & 3;
+  }
+  __device__ __forceinline__ int off(int r, int chunk) const {
+    return r * D + ((chunk ^ swz(r)) << 3);
+  }
   __device__ __forceinline__ bf16x8 along_cols(int r, int ks, int h) const {
-    return *reinterpret_cast<const bf16x8*>(rm + r * LDR + ks * 16 + h * 8);
+    return *reinterpret_cast<const bf16x8*>(p + off(r, 2 * ks + h));
   }
-  // rows r0 + 16 s + 8 (t / 4) + 4 h + (t % 4), column c
   __device__ __forceinline__ bf16x8 along_rows(int c, int r0, int s, int h) const {
-    const int x = swz(c);
-    const bf16* base = tr + c * LDT;
-    const int ra = (r0 + 16 * s + 4 * h) ^ x;
-    const int rb = (r0 + 16 * s + 8 + 4 * h) ^ x;
-    bf16x4 lo = *reinterpret_cast<const bf16x4*>(base + ra);
-    bf16x4 hi = *reinterpret_cast<const bf16x4*>(base + rb);
-    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    // 16-lane group g = lane / 16 reads rows ra + j / 4 (j = lane % 16), columns
+    // cb + 4 (j % 4); the transposing read hands lane j column cb + j, 4 rows.
+    const int lane = threadIdx.x & 63;
+    const int j = lane & 15;
+    const int cb = (c & ~31) + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+    const int ra = r0 + 16 * s + 4 * h + (j >> 2);
+    const int e0 = off(ra, cb >> 3) + (cb & 7);
+    const int e1 = off(ra + 8, cb >> 3) + (cb & 7);
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + e0));
+    i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + e1));
+    bf16x4 fa = __builtin_bit_cast(bf16x4, a);
+    bf16x4 fb = __builtin_bit_cast(bf16x4, b);
+    return bf16x8{fa[0], fa[1], fa[2], fa[3], fb[0], fb[1], fb[2], fb[3]};
   }
-
-  // Cooperative copy of rows [row0, row0 + ROWS) x columns [0, D) of a global
-  // [.., row_stride] matrix; rows >= nrows and columns >= ncols read as 0.
-  template <int NT>
-  __device__ __forceinline__ void stage(const bf16* g, long row_stride, int row0, int nrows,
-                                       int ncols, int tid) const {
-    if constexpr (TRANS) {
-      // unit = 4 rows x 8 columns: four 16-byte reads, four 16-byte row-major
-      // writes, eight 8-byte transposed writes
-      constexpr int CG = D / 8;
-      constexpr int UNITS = (ROWS / 4) * CG;
-#pragma unroll
-      for (int u0 = 0; u0 < UNITS; u0 += NT) {
-        const int u = u0 + tid;
-        if (UNITS % NT == 0 || u < UNITS) {
-          const int cg = u % CG, rg = u / CG;
-          const int c = cg * 8;
-          bf16x8 x[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = row0 + rg * 4 + i;
-            if (r < nrows && c < ncols)
-              x[i] = *reinterpret_cast<const bf16x8*>(g + (long)r * row_stride + c);
-            else
-              x[i] = bf16x8{};
-            *reinterpret_cast<bf16x8*>(rm + (rg * 4 + i) * LDR + c) = x[i];
-          }
-#pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            const int cc = c + t;
-            bf16x4 y{x[0][t], x[1][t], x[2][t], x[3][t]};
-            *reinterpret_cast<bf16x4*>(tr + cc * LDT + ((rg * 4) ^ swz(cc))) = y;
-          }
-        }
-      }
-    } else {
-      constexpr int CG = D / 8;
-      constexpr int UNITS = ROWS * CG;
-#pragma unroll
-      for (int u0 = 0; u0 < UNITS; u0 += NT) {
-        const int u = u0 + tid;
-        if (UNITS % NT == 0 || u < UNITS) {
-          const int cg = u % CG, r = u / CG;
-          const int c = cg * 8;
-          bf16x8 x = bf16x8{};
-          if (row0 + r < nrows && c < ncols)
-            x = *reinterpret_cast<const bf16x8*>(g + (long)(row0 + r) * row_stride + c);
-          *reinterpret_cast<bf16x8*>(rm + r * LDR + c) = x;
-        }
-      }
-    }
+  __device__ __forceinline__ void put(int r, int chunk, const bf16x8& v) const {
+    *reinterpret_cast<bf16x8*>(p + off(r, chunk)) = v;
   }
 };
 
-template <int ROWS, int D, bool TRANS> struct Tile<float, ROWS, D, TRANS> {
+template <int ROWS, int D> struct Tile<float, ROWS, D> {
   static constexpr int LDR = D + 4;
-  static constexpr int RM_ELEMS = ROWS * LDR;
-  static constexpr int TR_ELEMS = 0;
-  static constexpr int BYTES = RM_ELEMS * 4;
-  float* rm;
-  float* tr;  // unused: a one-element fragment reads any layout in one access
+  static constexpr int ELEMS = ROWS * LDR;
+  static constexpr int BYTES = ELEMS * 4;
+  static constexpr int CPR = D / 4;
+  float* p;
 
   __device__ __forceinline__ float along_cols(int r, int ks, int h) const {
-    return rm[r * LDR + ks * 2 + h];
+    return p[r * LDR + ks * 2 + h];
   }
   __device__ __forceinline__ float along_rows(int c, int r0, int s, int h) const {
-    return rm[(r0 + acc_row(s, h)) * LDR + c];
+    return p[(r0 + acc_row(s, h)) * LDR + c];
   }
-
-  template <int NT>
-  __device__ __forceinline__ void stage(const float* g, long row_stride, int row0, int nrows,
-                                       int ncols, int tid) const {
-    constexpr int CG = D / 4;
-    constexpr int UNITS = ROWS * CG;
-#pragma unroll
-    for (int u0 = 0; u0 < UNITS; u0 += NT) {
-      const int u = u0 + tid;
-      if (UNITS % NT == 0 || u < UNITS) {
-        const int cg = u % CG, r = u / CG;
-        const int c = cg * 4;
-        f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (row0 + r < nrows && c < ncols)
-          x = *reinterpret_cast<const f32x4*>(g + (long)(row0 + r) * row_stride + c);
-        *reinterpret_cast<f32x4*>(rm + r * LDR + c) = x;
-      }
-    }
+  __device__ __forceinline__ void put(int r, int chunk, const f32x4& v) const {
+    *reinterpret_cast<f32x4*>(p + r * LDR + chunk * 4) = v;
   }
 };
 
+// ---------------------------------------------------------------------------
+// Filling a Tile with rows [row0, row0 + ROWS) x columns [0, D) of a global
+// [pos, row_stride] matrix, by all 256 threads.
+//
+// fill_async (bf16, whole tiles only): global_load_lds_dwordx4 copies 16
+// bytes per lane straight into LDS without passing through registers; one
+// wave instruction fills 1 KB of LDS, lane l landing at byte 16 l.  Each lane
+// therefore fetches the logical chunk that the swizzle stores at its LDS
+// slot.  Completion: s_waitcnt vmcnt(0) before the barrier that publishes it.
+// fill_sync: 16-byte loads into registers, then LDS stores; rows >= nrows and
+// columns >= ncols read as 0 (ragged tiles and the f32 layout).
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int ROWS, int D>
+__device__ __forceinline__ void fill_async(const Tile<bf16, ROWS, D>& t, const bf16* g, long rs,
+                                           int row0, int wave, int lane) {
+  constexpr int CPR = D / 8;              // chunks per row
+  constexpr int RPI = 64 / CPR;           // rows per wave instruction
+  constexpr int NI = ROWS / RPI;          // wave instructions per tile
+  static_assert(NI % 4 == 0, "tile must split evenly over 4 waves");
+#pragma unroll
+  for (int i = 0; i < NI / 4; ++i) {
+    const int inst = wave * (NI / 4) + i;
+    const int r = inst * RPI + lane / CPR;
+    const int chunk = (lane % CPR) ^ Tile<bf16, ROWS, D>::swz(r);
+    const bf16* src = g + (long)(row0 + r) * rs + chunk * 8;
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)(t.p + inst * 512), 16, 0, 0);
+  }
+}
+
+// 64 consecutive floats (one wave instruction, 4 bytes per lane) into LDS.
+__device__ __forceinline__ void fill_async_row64(float* lds, const float* g) {
+  __builtin_amdgcn_global_load_lds(g + (threadIdx.x & 63), (lds_void*)lds, 4, 0, 0);
+}
+
+// Wait until every global->LDS copy issued by this wave has landed.
+__device__ __forceinline__ void wait_async_fills() {
+  // vmcnt = 0; expcnt and lgkmcnt left at their maxima (no wait)
+  __builtin_amdgcn_s_waitcnt(0x3F70);
+}
+
+template <typename T, int ROWS, int D>
+__device__ __forceinline__ void fill_sync(const Tile<T, ROWS, D>& t, const T* g, long rs, int row0,
+                                          int nrows, int ncols, int tid) {
+  using chunk = typename Mma<T>::chunk;
+  constexpr int CH = Mma<T>::CHUNK;
+  constexpr int CPR = D / CH;
+  constexpr int NCH = ROWS * CPR / kThreads;
+  static_assert(ROWS * CPR % kThreads == 0, "tile must split evenly over 256 threads");
+  chunk v[NCH];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int u = tid + kThreads * i;
+    const int r = u / CPR, c = (u % CPR) * CH;
+    v[i] = chunk{};
+    if (row0 + r < nrows && c < ncols)
+      v[i] = *reinterpret_cast<const chunk*>(g + (long)(row0 + r) * rs + c);
+  }
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int u = tid + kThreads * i;
+    t.put(u / CPR, u % CPR, v[i]);
+  }
+}
+
 // A register-resident operand for a contraction over the head dim: the
-// lane's row `row` of a global [.., row_stride] matrix, K slots along the
+// lane's row `row` of a global [pos, row_stride] matrix, K slots along the
 // columns.  Out-of-range rows or columns read as 0.
 template <typename T, int D>
 __device__ __forceinline__ void load_row_frags(typename Mma<T>::frag (&f)[D / Mma<T>::K],
@@ -242,14 +269,5 @@ __device__ __forceinline__ void store_acc_transposed(const f32x16& acc, T* g, lo
     }
   }
 }
-
-__device__ __forceinline__ f32x16 zero16() {
-  f32x16 z;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) z[i] = 0.f;
-  return z;
-}
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 }  // namespace attn

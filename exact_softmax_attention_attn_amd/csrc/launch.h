@@ -10,8 +10,7 @@ struct BwdArgs {
   const void* K;
   const void* V;
   const void* dO;
-  const float* L;
-  const float* Dws;
+  const float* Dws;   // workspace: D [B, H, N] then L * log2(e) [B, H, N]
   void* dQ;
   void* dK;
   void* dV;
@@ -37,8 +36,8 @@ struct FwdArgs {
 // smaller d runs in the next bucket with the extra columns read as zero.
 inline int head_dim_bucket(int d) { return d <= 32 ? 32 : (d <= 64 ? 64 : 128); }
 
-hipError_t launch_bwd_preprocess(const void* O, const void* dO, float* Dws, int B, int H, int N,
-                                 int d, int dtype, hipStream_t stream);
+hipError_t launch_bwd_preprocess(const void* O, const void* dO, const float* L, float* ws, int B,
+                                 int H, int N, int d, int dtype, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_lse(const FwdArgs& a, hipStream_t stream);

@@ -65,8 +65,8 @@ def test_status_strings(lib):
 
 
 def test_workspace_bytes(lib):
-    assert lib.attn_bwd_workspace_bytes(1, 16, 16384, 128) == 16 * 16384 * 4
-    assert lib.attn_bwd_workspace_bytes(3, 2, 8, 4) == 48 * 4
+    assert lib.attn_bwd_workspace_bytes(1, 16, 16384, 128) == 2 * 16 * 16384 * 4
+    assert lib.attn_bwd_workspace_bytes(3, 2, 8, 4) == 2 * 48 * 4
     assert lib.attn_bwd_workspace_bytes(0, 2, 8, 4) == 0
     assert lib.attn_bwd_workspace_bytes(1, 1, -5, 4) == 0
 
@@ -111,12 +111,13 @@ def test_validation_rejects_bad_arguments_without_launching(lib):
         assert _fwd(lib, f5, **kw) == 2, kw
         assert _bwd(lib, b10, **kw) == 2, kw
     # the stage entry points validate the same way
-    assert lib.attn_bwd_preprocess(FAKE, NUL, FAKE, 1, 1, 8, 8, 0, NUL) == 1
-    assert lib.attn_bwd_preprocess(FAKE, FAKE, FAKE, 1, 1, 8, 6, 0, NUL) == 2
-    assert lib.attn_bwd_dkdv(*([FAKE] * 7), NUL, 1, 1, 8, 8, 1, 0.5, 0, NUL) == 1
-    assert lib.attn_bwd_dkdv(*([FAKE] * 8), 1, 1, 8, 8, 1, 0.0, 0, NUL) == 1
-    assert lib.attn_bwd_dq(*([FAKE] * 6), NUL, 1, 1, 8, 8, 1, 0.5, 0, NUL) == 1
-    assert lib.attn_bwd_dq(*([FAKE] * 7), 1, 1, 8, 256, 1, 0.5, 1, NUL) == 2
+    assert lib.attn_bwd_preprocess(FAKE, NUL, FAKE, FAKE, 1, 1, 8, 8, 0, NUL) == 1
+    assert lib.attn_bwd_preprocess(FAKE, FAKE, NUL, FAKE, 1, 1, 8, 8, 0, NUL) == 1
+    assert lib.attn_bwd_preprocess(FAKE, FAKE, FAKE, FAKE, 1, 1, 8, 6, 0, NUL) == 2
+    assert lib.attn_bwd_dkdv(*([FAKE] * 6), NUL, 1, 1, 8, 8, 1, 0.5, 0, NUL) == 1
+    assert lib.attn_bwd_dkdv(*([FAKE] * 7), 1, 1, 8, 8, 1, 0.0, 0, NUL) == 1
+    assert lib.attn_bwd_dq(*([FAKE] * 5), NUL, 1, 1, 8, 8, 1, 0.5, 0, NUL) == 1
+    assert lib.attn_bwd_dq(*([FAKE] * 6), 1, 1, 8, 256, 1, 0.5, 1, NUL) == 2
     assert lib.attn_last_error() == b""
 
 

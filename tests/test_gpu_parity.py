@@ -148,7 +148,7 @@ def test_no_device_allocation_during_backward(B):
     q, k, v, do = (_dev(x[n], w.dtype) for n in ("q", "k", "v", "do"))
     o, lse = B.attn_fwd_lse(q, k, v, causal=True, scale=w.scale)
     dq, dk, dv = (torch.empty_like(q) for _ in range(3))
-    ws = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+    ws = B.new_workspace(w.B, w.H, w.N, "cuda")
     B.attn_bwd(q, k, v, o, do, lse, scale=w.scale, dq=dq, dk=dk, dv=dv, workspace=ws)
     torch.cuda.synchronize()
     free0, _ = torch.cuda.mem_get_info()
