@@ -17,7 +17,11 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libattn.so")
-SOURCES = ("attn_api.hip", "attn_fwd.hip", "attn_bwd.hip")
+SOURCES = ("attn_api.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_bwd_pipe.hip")
+# The pipelined kernels keep long-lived operands in AGPRs (pinned in the
+# source) and want every MFMA result and accumulator in VGPRs, where the VALU
+# can read them without copies.
+PER_SOURCE_FLAGS = {"attn_bwd_pipe.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 COMMON_FLAGS = [
@@ -44,7 +48,8 @@ def build(verbose: bool = False, extra_flags=()) -> str:
     jobs = []
     for src in SOURCES:
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-        cmd = [HIPCC, *COMMON_FLAGS, *extra_flags, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC, *COMMON_FLAGS, *PER_SOURCE_FLAGS.get(src, []), *extra_flags, "-c",
+               os.path.join(CSRC, src), "-o", obj]
         jobs.append((src, obj, cmd))
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
         results = list(ex.map(lambda j: (j, _run(j[2])), jobs))

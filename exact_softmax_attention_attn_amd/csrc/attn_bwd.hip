@@ -113,7 +113,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   const int nqt = (N + BQ - 1) / BQ;
   const int qt0 = CAUSAL ? kvb / BQ : 0;
 
-  auto fill = [&](Buf& B, int qt) {
+  auto fill = [&](Buf& B, int qt) ATTN_INLINE {
     const int q0 = qt * BQ;
     if constexpr (sizeof(T) == 2) {
       if (q0 + BQ <= N && d == D) {
@@ -133,7 +133,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     }
   };
 
-  auto body = [&](const Buf& B, int q0, auto masked_c) {
+  auto body = [&](const Buf& B, int q0, auto masked_c) ATTN_INLINE {
     constexpr bool MASKED = decltype(masked_c)::value;
     const QT qt_{const_cast<T*>(B.q)}, ot_{const_cast<T*>(B.o)};
 #pragma unroll
@@ -191,7 +191,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     }
   };
 
-  auto step = [&](const Buf& cur, Buf& nxt, int qt) {
+  auto step = [&](const Buf& cur, Buf& nxt, int qt) ATTN_INLINE {
     if (qt + 1 < nqt) fill(nxt, qt + 1);
     const int q0 = qt * BQ;
     if (CAUSAL && q0 < kvb + BKV)
@@ -265,7 +265,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
   const int kv_end = CAUSAL ? min(N, qb + BQ) : N;
   const int nkt = (kv_end + BKV - 1) / BKV;
 
-  auto fill = [&](Buf& B, int kt) {
+  auto fill = [&](Buf& B, int kt) ATTN_INLINE {
     const int k0 = kt * BKV;
     if constexpr (sizeof(T) == 2) {
       if (k0 + BKV <= N && d == D) {
@@ -278,7 +278,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
     fill_sync(KT{B.v}, V + base, rs, k0, N, d, tid);
   };
 
-  auto body = [&](const Buf& B, int k0, auto masked_c) {
+  auto body = [&](const Buf& B, int k0, auto masked_c) ATTN_INLINE {
     constexpr bool MASKED = decltype(masked_c)::value;
     const KT kt_{const_cast<T*>(B.k)}, vt_{const_cast<T*>(B.v)};
 #pragma unroll
@@ -313,7 +313,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
     }
   };
 
-  auto step = [&](const Buf& cur, Buf& nxt, int kt) {
+  auto step = [&](const Buf& cur, Buf& nxt, int kt) ATTN_INLINE {
     if (kt + 1 < nkt) fill(nxt, kt + 1);
     const int k0 = kt * BKV;
     if (CAUSAL && k0 + BKV - 1 > qb)
@@ -402,7 +402,17 @@ static hipError_t dq_go(const BwdArgs& a, hipStream_t stream) {
     return FN<float, 128, false>(a, stream);                                          \
   } while (0)
 
-hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) { ATTN_DISPATCH(dkdv_go, a, stream); }
-hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream) { ATTN_DISPATCH(dq_go, a, stream); }
+// bf16 with a 64- or 128-column head-dim bucket runs the software-pipelined
+// kernels; everything else the generic ones.
+static bool use_pipe(const BwdArgs& a) { return a.dtype == 1 && head_dim_bucket(a.d) >= 64; }
+
+hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
+  if (use_pipe(a)) return launch_bwd_dkdv_bf16_pipe(a, stream);
+  ATTN_DISPATCH(dkdv_go, a, stream);
+}
+hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {
+  if (use_pipe(a)) return launch_bwd_dq_bf16_pipe(a, stream);
+  ATTN_DISPATCH(dq_go, a, stream);
+}
 
 }  // namespace attn

@@ -56,7 +56,7 @@ __global__ __launch_bounds__(256, 1) void fwd_lse_kernel(const T* __restrict__ Q
   const int kv_end = CAUSAL ? min(N, qb + BQ) : N;
   const int nkt = (kv_end + BKV - 1) / BKV;
 
-  auto fill = [&](Buf& B, int kt) {
+  auto fill = [&](Buf& B, int kt) ATTN_INLINE {
     const int k0 = kt * BKV;
     if constexpr (sizeof(T) == 2) {
       if (k0 + BKV <= N && d == D) {
@@ -69,7 +69,7 @@ __global__ __launch_bounds__(256, 1) void fwd_lse_kernel(const T* __restrict__ Q
     fill_sync(KT{B.v}, V + base, rs, k0, N, d, tid);
   };
 
-  auto body = [&](const Buf& B, int k0, auto masked_c) {
+  auto body = [&](const Buf& B, int k0, auto masked_c) ATTN_INLINE {
     constexpr bool MASKED = decltype(masked_c)::value;
     const KT kt_{const_cast<T*>(B.k)}, vt_{const_cast<T*>(B.v)};
 #pragma unroll
@@ -116,7 +116,7 @@ __global__ __launch_bounds__(256, 1) void fwd_lse_kernel(const T* __restrict__ Q
     }
   };
 
-  auto step = [&](const Buf& cur, Buf& nxt, int kt) {
+  auto step = [&](const Buf& cur, Buf& nxt, int kt) ATTN_INLINE {
     if (kt + 1 < nkt) fill(nxt, kt + 1);
     const int k0 = kt * BKV;
     if ((CAUSAL && k0 + BKV - 1 > qb) || k0 + BKV > N)

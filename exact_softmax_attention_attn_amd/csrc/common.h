@@ -24,6 +24,10 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// Lambdas in kernels must inline: a call would pass the accumulators through
+// memory-like calling conventions and wreck register allocation.
+#define ATTN_INLINE __attribute__((always_inline))
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kThreads = 256;   // every attention kernel runs 4 waves per workgroup
 
@@ -38,6 +42,30 @@ __device__ __forceinline__ f32x16 zero16() {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Keep a matrix-core operand that lives for the whole kernel in the
+// accumulation register file: the MFMA reads A/B operands from AGPRs directly,
+// and the architectural VGPRs stay free for the per-tile working set.
+template <typename V>
+__device__ __forceinline__ void pin_agpr(V& x) { asm volatile("" : "+a"(x)); }
+
+// Accumulate into an AGPR-resident 32x32 tile: acc += A B with
+// v_mfma_f32_32x32x16_bf16 in its AGPR form.  Kernels compiled with every
+// builtin MFMA in VGPR form (their results feed the VALU) use this for the
+// accumulators that only ever meet the matrix core.  The compiler cannot see
+// into the asm, so it is made hazard-safe by itself: the leading s_nop covers
+// the wait states a matrix instruction needs after a VALU write of its A/B
+// operands; back-to-back accumulation into the same registers needs none.
+__device__ __forceinline__ void mma_acc_agpr(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+// Before the VALU reads AGPR accumulators written by mma_acc_agpr: the last
+// 32x32 matrix instruction must have written its results back (it takes 8
+// passes of 4 cycles plus write-back latency).
+__device__ __forceinline__ void mma_acc_drain() {
+  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
+}
 
 // ---------------------------------------------------------------------------
 // Element type traits: which 32x32 MFMA, how deep one instruction contracts,
@@ -134,6 +162,49 @@ template <int ROWS, int D> struct Tile<bf16, ROWS, D> {
   }
   __device__ __forceinline__ void put(int r, int chunk, const bf16x8& v) const {
     *reinterpret_cast<bf16x8*>(p + off(r, chunk)) = v;
+  }
+};
+
+// Per-lane LDS offsets for the swizzled bf16 tiles, computed once per kernel.
+// The swizzle depends only on a row's position inside its 16-row group, so
+// the offset of any operand read is  plan entry + (16-row-aligned row) * D:
+// a register plus an instruction immediate.
+//   col[n]    : along_cols, rows r0 + l32, K step n (logical chunk 2n + h)
+//   tr[mt][e] : along_rows, columns mt*32 + (the lane's column), first (e=0)
+//               or second (e=1) group of 4 rows of K step s
+template <int D> struct LanePlan {
+  static constexpr int CPR = D / 8;
+  int col[D / 16];
+  int tr[D / 32][2];
+  __device__ __forceinline__ explicit LanePlan(int lane) {
+    using TT = Tile<bf16, 32, D>;
+    const int h = lane >> 5, l32 = lane & 31, j = lane & 15;
+#pragma unroll
+    for (int n = 0; n < D / 16; ++n) col[n] = l32 * D + (((2 * n + h) ^ TT::swz(l32)) << 3);
+#pragma unroll
+    for (int mt = 0; mt < D / 32; ++mt) {
+      const int cb = mt * 32 + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int rr = 4 * h + (j >> 2) + 8 * e;
+        tr[mt][e] = rr * D + (((cb >> 3) ^ TT::swz(rr)) << 3) + (cb & 7);
+      }
+    }
+  }
+  // operand with K slots along row r0 + l32 (r0 a multiple of 16), K step n
+  __device__ __forceinline__ bf16x8 cols(const bf16* t, int r0, int n) const {
+    return *reinterpret_cast<const bf16x8*>(t + col[n] + r0 * D);
+  }
+  // operand with K slots down column mt*32 + (lane's column), rows of the
+  // 32-row accumulator block at r0 in register order, K step s
+  __device__ __forceinline__ bf16x8 rows(const bf16* t, int r0, int s, int mt) const {
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const bf16* b = t + (r0 + 16 * s) * D;
+    i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(b + tr[mt][0]));
+    i16x4 c = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(b + tr[mt][1]));
+    bf16x4 fa = __builtin_bit_cast(bf16x4, a);
+    bf16x4 fc = __builtin_bit_cast(bf16x4, c);
+    return bf16x8{fa[0], fa[1], fa[2], fa[3], fc[0], fc[1], fc[2], fc[3]};
   }
 };
 

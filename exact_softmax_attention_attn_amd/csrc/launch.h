@@ -41,5 +41,7 @@ hipError_t launch_bwd_preprocess(const void* O, const void* dO, const float* L, 
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_lse(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_dkdv_bf16_pipe(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_dq_bf16_pipe(const BwdArgs& a, hipStream_t stream);
 
 }  // namespace attn
