@@ -102,7 +102,7 @@ def _check_rows(t: torch.Tensor, B: int, H: int, N: int, device, lead=()):
 
 
 def new_workspace(B: int, H: int, N: int, device) -> torch.Tensor:
-    """Workspace for attn_bwd: [2, B, H, N] float32 (D, then L * log2(e))."""
+    """Workspace for attn_bwd: [2, B, H, N] float32 (-D, then -L * log2(e))."""
     return torch.empty((2, B, H, N), dtype=torch.float32, device=device)
 
 
@@ -137,7 +137,7 @@ def attn_fwd_lse(q, k, v, causal: bool = True, scale: float | None = None, o=Non
 
 def attn_bwd(q, k, v, o, do, lse, causal: bool = True, scale: float | None = None,
              dq=None, dk=None, dv=None, workspace=None):
-    """dQ, dK, dV [B, N, H, d]; workspace ([2, B, H, N] float32) ends up holding D, L*log2(e)."""
+    """dQ, dK, dV [B, N, H, d]; workspace ([2, B, H, N] float32) ends up holding -D, -L*log2(e)."""
     _check_bnhd(q, k, v, o, do)
     B, N, H, d = q.shape
     _check_rows(lse, B, H, N, q.device)

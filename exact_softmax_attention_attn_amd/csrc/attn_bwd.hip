@@ -20,7 +20,9 @@ template <bool B> using bool_c = std::integral_constant<bool, B>;
 // Preprocess.  D[b, h, n] = sum_c dO[b, n, h, c] * O[b, n, h, c] in float32
 // (the softmax-weighted sum of dP, since sum_j P_ij dP_ij = dO_i . O_i), and
 // L2[b, h, n] = L[b, h, n] * log2(e), the row scalar in the base-2 units the
-// kernels exponentiate in.  16 lanes per row, 16 rows per 256-thread block.
+// kernels exponentiate in.  Both are stored negated (-D, -L2): the kernels
+// add them, which lets them enter a matrix instruction as its C input.
+// 16 lanes per row, 16 rows per 256-thread block.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_preprocess_kernel(const T* __restrict__ O,
@@ -59,8 +61,8 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(const T* __restrict
     const int n = (int)(bn % N);
     const int b = (int)(bn / N);
     const long i = ((long)b * H + h) * N + n;
-    Dout[i] = acc;
-    L2out[i] = L[i] * kLog2e;
+    Dout[i] = -acc;
+    L2out[i] = -L[i] * kLog2e;
   }
 }
 
@@ -128,8 +130,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     fill_sync(QT{B.o}, dO + base, rs, q0, N, d, tid);
     if (tid < BQ) {
       const int q = q0 + tid;
-      B.l[tid] = q < N ? Lh[q] : __builtin_inff();   // padded rows: P = 0
-      B.dd[tid] = q < N ? Dh[q] : 0.f;
+      B.l[tid] = q < N ? Lh[q] : -__builtin_inff();   // padded rows: P = 0 (-L2 stored)
+      B.dd[tid] = q < N ? Dh[q] : 0.f;                // -D stored
     }
   };
 
@@ -158,7 +160,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 4 * g + i;
-          float p = fast_exp2(__builtin_fmaf(s[r], scale_log2, -lg[i]));
+          float p = fast_exp2(__builtin_fmaf(s[r], scale_log2, lg[i]));
           if (MASKED && kv > qa + acc_row(r, h)) p = 0.f;
           s[r] = p;
         }
@@ -177,7 +179,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       for (int g = 0; g < 4; ++g) {
         const f32x4 dg = *reinterpret_cast<const f32x4*>(&B.dd[st * 32 + 8 * g + 4 * h]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dp[4 * g + i] = s[4 * g + i] * (dp[4 * g + i] - dg[i]);
+        for (int i = 0; i < 4; ++i) dp[4 * g + i] = s[4 * g + i] * (dp[4 * g + i] + dg[i]);
       }
       frag bds[RS];
 #pragma unroll
@@ -255,8 +257,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
   frag qf[KS], of[KS];
   load_row_frags<T, D>(qf, Q + base, rs, q, N, d, h);
   load_row_frags<T, D>(of, dO + base, rs, q, N, d, h);
-  const float Lq = q < N ? Lh[q] : __builtin_inff();
-  const float Dq = q < N ? Dh[q] : 0.f;
+  const float Lq = q < N ? Lh[q] : -__builtin_inff();   // -L2 stored; padded rows: P = 0
+  const float Dq = q < N ? Dh[q] : 0.f;                  // -D stored
 
   f32x16 acc[MT];
 #pragma unroll
@@ -298,9 +300,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
       // register r = key row ka + acc_row(r, h), column = query row q
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float p = fast_exp2(__builtin_fmaf(s[r], scale_log2, -Lq));
+        float p = fast_exp2(__builtin_fmaf(s[r], scale_log2, Lq));
         if (MASKED && ka + acc_row(r, h) > q) p = 0.f;
-        dp[r] = p * (dp[r] - Dq);
+        dp[r] = p * (dp[r] + Dq);
       }
       frag bds[RS];
 #pragma unroll

@@ -37,55 +37,73 @@ __device__ __forceinline__ f32x4 lds_f32x4(const float* p) {
 
 // ---------------------------------------------------------------------------
 // dK, dV (bf16).  Workgroup = 4 waves = 128 key rows of one (b, h); wave w
-// owns key rows kv0 + [0, 32) (K, V in registers; dV^T, dK^T accumulators).
-// Stage A(k): S = Q K^T and dP = dO V^T for the 32 query rows of sub-tile k.
-// Stage B(k): P = exp2(S scale log2e - L2) (masked on diagonal sub-tiles),
-//             dV^T += dO^T P, dS = P o (dP - D), dK^T += Q^T dS.
+// owns key rows kv0 + [0, 32).  Its K rows (pre-multiplied by scale log2e)
+// and V rows sit in AGPRs as the B operands of S = Q K^T and dP = dO V^T
+// (column n = key row), so the results hold query rows along the registers:
+// the row scalars -L log2e and -D then enter as the MFMA's C input, read from
+// LDS straight into the accumulator registers, and
+//   S' = Q (c K)^T - L2 = log2 of P,   dP' = dO V^T - D
+// leave one exp2 and one multiply per element:  P = exp2(S'), dS = P o dP'.
+// dV^T += dO^T P and dK^T += Q^T dS accumulate in AGPRs (asm MFMA).  Query
+// tiles of 64 rows ping-pong between two separately named LDS buffers; the
+// operand reads (Q, dO along the head dim; dO, Q across positions) run AH
+// fragments ahead through a whole tile.  Causal: the walk starts at the
+// diagonal; only its first two tiles carry the element mask.
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    const bf16* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dws,
+    const bf16* __restrict__ dO, const float* __restrict__ nL2, const float* __restrict__ nD,
     bf16* __restrict__ dK, bf16* __restrict__ dV, int H, int N, int d, float scale_log2,
     float scale) {
   using M = Mma<bf16>;
   using frag = bf16x8;
-  constexpr int BKV = 128, BQ = 64, KS = D / 16, MT = D / 32, NB = 3;
-  static_assert(KS == 2 * MT, "one product over positions per product over the head dim");
+  constexpr int BKV = 128, BQ = 64, KS = D / 16, MT = D / 32, AH = 4;
+  constexpr int OPS = 2 * KS + 4 * MT;         // operand reads per 32-row sub-tile
   using QT = Tile<bf16, BQ, D>;
   struct __align__(16) Buf {
     bf16 q[QT::ELEMS];
     bf16 o[QT::ELEMS];
-    float l[BQ];
-    float dd[BQ];
+    float l[BQ];      // -L * log2(e)
+    float dd[BQ];     // -D
   };
-  __shared__ Buf buf[NB];
+  __shared__ Buf buf0, buf1;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
   const int jb = blockIdx.x, head = blockIdx.y, b = blockIdx.z;
   const long rs = (long)H * d;
   const long base = ((long)b * N * H + head) * d;
-  const float* Lh = L2 + ((long)b * H + head) * N;
-  const float* Dh = Dws + ((long)b * H + head) * N;
+  const float* Lh = nL2 + ((long)b * H + head) * N;
+  const float* Dh = nD + ((long)b * H + head) * N;
 
   const int kvb = jb * BKV;
   const int kv0 = kvb + wave * 32;
   const int kv = kv0 + l32;
+  const LanePlan<D> plan(lane);
   frag kf[KS], vf[KS];
   load_row_frags<bf16, D>(kf, K + base, rs, kv, N, d, h);
   load_row_frags<bf16, D>(vf, V + base, rs, kv, N, d, h);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) kf[ks][t] = (bf16)((float)kf[ks][t] * scale_log2);
+    pin_agpr(kf[ks]);
+    pin_agpr(vf[ks]);
+  }
 
   f32x16 dv_acc[MT], dk_acc[MT];
 #pragma unroll
-  for (int i = 0; i < MT; ++i) { dv_acc[i] = zero16(); dk_acc[i] = zero16(); }
+  for (int i = 0; i < MT; ++i) {
+    dv_acc[i] = zero16(); pin_agpr(dv_acc[i]);
+    dk_acc[i] = zero16(); pin_agpr(dk_acc[i]);
+  }
 
   const int nqt = (N + BQ - 1) / BQ;
   const int qt0 = CAUSAL ? kvb / BQ : 0;
   const int ntiles = nqt - qt0;
-  const int nsub = 2 * ntiles;
 
-  auto fill = [&](Buf& B, int qt) ATTN_INLINE {
-    const int q0 = qt * BQ;
+  auto fill = [&](Buf& B, int t) ATTN_INLINE {
+    const int q0 = (qt0 + t) * BQ;
     if (q0 + BQ <= N && d == D) {
       fill_async(QT{B.q}, Q + base, rs, q0, wave, lane);
       fill_async(QT{B.o}, dO + base, rs, q0, wave, lane);
@@ -96,162 +114,130 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
       fill_sync(QT{B.o}, dO + base, rs, q0, N, d, tid);
       if (tid < BQ) {
         const int q = q0 + tid;
-        B.l[tid] = q < N ? Lh[q] : __builtin_inff();   // padded rows: P = 0
+        B.l[tid] = q < N ? Lh[q] : -__builtin_inff();   // padded rows: P = 0
         B.dd[tid] = q < N ? Dh[q] : 0.f;
       }
     }
   };
 
-  // S / dP accumulators of two consecutive sub-tiles; the roles (stage A
-  // output, stage B input) alternate from step to step.
-  f32x16 s0, p0, s1, p1;
-
-  // One step.  HAS_A / HAS_B select the stages; MASK_B applies the causal
-  // element mask to stage B's sub-tile (k - 1).  sa/pa receive stage A's
-  // products; sb/pb hold stage B's (overwritten with P and dS).
-  auto step = [&](int k, f32x16& sa, f32x16& pa, f32x16& sb, f32x16& pb, auto has_a_c,
-                  auto has_b_c, auto mask_b_c) ATTN_INLINE {
-    constexpr bool HAS_A = decltype(has_a_c)::value;
-    constexpr bool HAS_B = decltype(has_b_c)::value;
-    constexpr bool MASK_B = decltype(mask_b_c)::value;
-    const int kb = k > 0 ? k - 1 : 0;
-    const Buf& BA = buf[(k >> 1) % NB];
-    const Buf& BB = buf[(kb >> 1) % NB];
-    const QT tqa{const_cast<bf16*>(BA.q)}, toa{const_cast<bf16*>(BA.o)};
-    const QT tqb{const_cast<bf16*>(BB.q)}, tob{const_cast<bf16*>(BB.o)};
-    const int ra = (k & 1) * 32;              // sub-tile k's first row in its tile
-    const int rb = (kb & 1) * 32;             // sub-tile k-1's first row in its tile
-    const int qab = (qt0 + (kb >> 1)) * BQ + rb;   // absolute first query row, stage B
-
-    frag aq[KS], ao[KS], tv[KS], tk[KS];
-    frag bp[2], bds[2];
-    constexpr int AHEAD = 2;                  // operand reads issued this many products ahead
-    constexpr int PER = 16 / KS;              // P / dS registers handled per product
-
-    // ---- preamble: first operands of both stages
-    if constexpr (HAS_A) {
+  auto tile_body = [&](int t, const Buf& B, auto masked_c) ATTN_INLINE {
+    constexpr bool MASKED = decltype(masked_c)::value;
+    // operand n of the tile: sub-tile n / OPS; within it Q cols, dO cols,
+    // dO rows (dV), Q rows (dK)
+    auto opnd = [&](int n) ATTN_INLINE -> frag {
+      const int r0 = (n / OPS) * 32, m = n % OPS;
+      if (m < KS) return plan.cols(B.q, r0, m);
+      if (m < 2 * KS) return plan.cols(B.o, r0, m - KS);
+      if (m < 2 * KS + 2 * MT) {
+        const int i = m - 2 * KS;
+        return plan.rows(B.o, r0, i / MT, i % MT);
+      }
+      const int i = m - 2 * KS - 2 * MT;
+      return plan.rows(B.q, r0, i / MT, i % MT);
+    };
+    frag ring[AH];
 #pragma unroll
-      for (int i = 0; i < AHEAD; ++i) aq[i] = tqa.along_cols(ra + l32, i, h);
-    }
-    if constexpr (HAS_B) {
-#pragma unroll
-      for (int i = 0; i < AHEAD; ++i) tv[i] = tob.along_rows((i % MT) * 32 + l32, rb, i / MT, h);
-    }
+    for (int n = 0; n < AH; ++n) ring[n] = opnd(n);
     fence();
-    // ---- phase 1: S(k) chain | P(k-1) on the VALU
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if constexpr (HAS_A) {
-        if (ks == 0) sa = M::mma(aq[0], kf[0], zero16());
-        else sa = M::mma(aq[ks], kf[ks], sa);
-        if (ks + AHEAD < KS) aq[ks + AHEAD] = tqa.along_cols(ra + l32, ks + AHEAD, h);
-      }
-      if constexpr (HAS_B) {
-        // registers 4g .. 4g+3 share one 16-byte read of L2 (rows 8g + 4h + 0..3)
+    for (int st = 0; st < 2; ++st) {
+      const int r0 = st * 32;
+      const int qa = (qt0 + t) * BQ + r0;        // absolute first query row of the sub-tile
+      const int n0 = st * OPS;
+      // C inputs: -L2 and -D of the sub-tile's rows, in accumulator order
+      f32x16 sc, pc;
 #pragma unroll
-        for (int j = 0; j < PER; ++j) {
-          const int r = ks * PER + j;
-          const f32x4 lg = lds_f32x4(&BB.l[rb + 8 * (r >> 2) + 4 * h]);
-          float p = fast_exp2(__builtin_fmaf(sb[r], scale_log2, -lg[r & 3]));
-          if (MASK_B && kv > qab + acc_row(r, h)) p = 0.f;
-          sb[r] = p;
-        }
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 lv = *reinterpret_cast<const f32x4*>(&B.l[r0 + 8 * g + 4 * h]);
+        const f32x4 dv = *reinterpret_cast<const f32x4*>(&B.dd[r0 + 8 * g + 4 * h]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { sc[4 * g + i] = lv[i]; pc[4 * g + i] = dv[i]; }
       }
+      // S' = Q (c K)^T - L2
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int n = n0 + ks;
+        const frag a = ring[n % AH];
+        if (n + AH < 2 * OPS) ring[n % AH] = opnd(n + AH);
+        sc = M::mma(a, kf[ks], sc);
+        fence();
+      }
+      // dP' = dO V^T - D  |  P = exp2(S') on the VALU
+      constexpr int PER = 16 / KS;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int n = n0 + KS + ks;
+        const frag a = ring[n % AH];
+        if (n + AH < 2 * OPS) ring[n % AH] = opnd(n + AH);
+        pc = M::mma(a, vf[ks], pc);
+#pragma unroll
+        for (int e = 0; e < PER; ++e) sc[ks * PER + e] = fast_exp2(sc[ks * PER + e]);
+        fence();
+      }
+      if constexpr (CAUSAL && MASKED) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (kv > qa + acc_row(r, h)) sc[r] = 0.f;
+      }
+      frag bp[2];
+      bp[0] = M::pack(sc, 0);
+      bp[1] = M::pack(sc, 1);
       fence();
-    }
-    if constexpr (HAS_B) {
-      bp[0] = M::pack(sb, 0);
-      bp[1] = M::pack(sb, 1);
-    }
-    if constexpr (HAS_A) {
+      // dV^T += dO^T P  |  dS = P o dP' on the VALU
+      constexpr int PER2 = 16 / (2 * MT);
+      frag bds[2];
 #pragma unroll
-      for (int i = 0; i < AHEAD; ++i) ao[i] = toa.along_cols(ra + l32, i, h);
-    }
-    fence();
-    // ---- phase 2: dV(k-1) chain | dS(k-1) on the VALU
+      for (int i = 0; i < 2 * MT; ++i) {
+        const int n = n0 + 2 * KS + i;
+        const frag a = ring[n % AH];
+        if (n + AH < 2 * OPS) ring[n % AH] = opnd(n + AH);
+        mma_acc_agpr(dv_acc[i % MT], a, bp[i / MT]);
 #pragma unroll
-    for (int i = 0; i < KS; ++i) {
-      if constexpr (HAS_B) {
-        const int ss = i / MT, mt = i % MT;
-        dv_acc[mt] = M::mma(tv[i], bp[ss], dv_acc[mt]);
-        if (i + AHEAD < KS) {
-          const int n = i + AHEAD;
-          tv[n] = tob.along_rows((n % MT) * 32 + l32, rb, n / MT, h);
-        } else {
-          const int n = i + AHEAD - KS;       // first dK operands
-          tk[n] = tqb.along_rows((n % MT) * 32 + l32, rb, n / MT, h);
-        }
-#pragma unroll
-        for (int j = 0; j < PER; ++j) {
-          const int r = i * PER + j;
-          const f32x4 dg = lds_f32x4(&BB.dd[rb + 8 * (r >> 2) + 4 * h]);
-          pb[r] = sb[r] * (pb[r] - dg[r & 3]);
-        }
+        for (int e = 0; e < PER2; ++e) pc[i * PER2 + e] = sc[i * PER2 + e] * pc[i * PER2 + e];
+        fence();
       }
+      bds[0] = M::pack(pc, 0);
+      bds[1] = M::pack(pc, 1);
       fence();
-    }
-    if constexpr (HAS_B) {
-      bds[0] = M::pack(pb, 0);
-      bds[1] = M::pack(pb, 1);
-    }
-    fence();
-    // ---- phase 3: dP(k) chain | dK(k-1) chain, interleaved
+      // dK^T += Q^T dS
 #pragma unroll
-    for (int i = 0; i < KS; ++i) {
-      if constexpr (HAS_A) {
-        if (i == 0) pa = M::mma(ao[0], vf[0], zero16());
-        else pa = M::mma(ao[i], vf[i], pa);
-        if (i + AHEAD < KS) ao[i + AHEAD] = toa.along_cols(ra + l32, i + AHEAD, h);
+      for (int i = 0; i < 2 * MT; ++i) {
+        const int n = n0 + 2 * KS + 2 * MT + i;
+        const frag a = ring[n % AH];
+        if (n + AH < 2 * OPS) ring[n % AH] = opnd(n + AH);
+        mma_acc_agpr(dk_acc[i % MT], a, bds[i / MT]);
+        fence();
       }
-      if constexpr (HAS_B) {
-        const int ss = i / MT, mt = i % MT;
-        dk_acc[mt] = M::mma(tk[i], bds[ss], dk_acc[mt]);
-        if (i + AHEAD < KS) {
-          const int n = i + AHEAD;
-          tk[n] = tqb.along_rows((n % MT) * 32 + l32, rb, n / MT, h);
-        }
-      }
-      fence();
     }
   };
 
-  const bool_c<true> Y{};
-  const bool_c<false> F{};
-  // entering tile t: its copy was issued two sub-steps ago; start tile t + 1's
-  auto boundary = [&](int t) ATTN_INLINE {
+  // tile t + 1 is copied into the other buffer while tile t is consumed
+  auto run_tile = [&](int t, const Buf& cur, Buf& nxt, auto masked_c) ATTN_INLINE {
     wait_async_fills();
     __syncthreads();
-    if (t + 1 < ntiles) fill(buf[(t + 1) % NB], qt0 + t + 1);
-  };
-  // tile t = steps 2t (stage B on sub-tile 2t - 1) and 2t + 1 (on sub-tile 2t)
-  auto tile = [&](int t, auto mask_first, auto mask_second) ATTN_INLINE {
-    boundary(t);
-    step(2 * t, s0, p0, s1, p1, Y, Y, mask_first);
-    step(2 * t + 1, s1, p1, s0, p0, Y, Y, mask_second);
+    if (t + 1 < ntiles) fill(nxt, t + 1);
+    tile_body(t, cur, masked_c);
   };
 
-  // ---- prologue: two tiles in flight, stage A of sub-tile 0
-  fill(buf[0], qt0);
-  if (ntiles > 1) fill(buf[1], qt0 + 1);
-  wait_async_fills();
-  __syncthreads();
-  step(0, s0, p0, s1, p1, Y, F, F);
-  // Causal: stage B of sub-tiles 0..3 (steps 1..4) crosses the diagonal and is
-  // peeled off; the loop that follows carries no mask and no branch.
-  int t0 = 1;
-  step(1, s1, p1, s0, p0, Y, Y, bool_c<CAUSAL>{});
-  if constexpr (CAUSAL) {
-    if (ntiles > 1) tile(1, Y, Y);
-    if (ntiles > 2) tile(2, Y, F);
-    t0 = 3;
+  // causal: tiles 0 and 1 of the walk straddle the diagonal (BKV = 2 BQ)
+  const int nmask = CAUSAL ? min(2, ntiles) : 0;
+  fill(buf0, 0);
+  int t = 0;
+  if (nmask > 0) {
+    run_tile(0, buf0, buf1, bool_c<true>{});
+    if (nmask > 1) run_tile(1, buf1, buf0, bool_c<true>{});
+    t = nmask;
   }
-  for (int t = t0; t < ntiles; ++t) tile(t, F, F);
-  // drain: stage B of the last sub-tile (held in s1, p1)
-  if (CAUSAL && ntiles <= 2)
-    step(nsub, s0, p0, s1, p1, F, Y, Y);
-  else
-    step(nsub, s0, p0, s1, p1, F, Y, F);
+  if ((t & 1) && t < ntiles) {               // keep even tiles in buf0
+    run_tile(t, buf1, buf0, bool_c<false>{});
+    ++t;
+  }
+  for (; t < ntiles; t += 2) {
+    run_tile(t, buf0, buf1, bool_c<false>{});
+    if (t + 1 < ntiles) run_tile(t + 1, buf1, buf0, bool_c<false>{});
+  }
 
+  mma_acc_drain();
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     store_acc_transposed<bf16>(dv_acc[mt], dV + base, rs, kv0, mt * 32, N, d, 1.f, lane);
@@ -260,29 +246,31 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// dQ (bf16).  Workgroup = 4 waves = 256 query rows of one (b, h); wave w owns
-// query rows qw + [0, 64) as two 32-row halves c = 0, 1.  Q and dO of both
-// halves and the dQ^T accumulators live in AGPRs for the whole kernel; L2 and
-// D are two scalars per lane.  Each LDS operand fragment feeds one product
-// per half (two matrix instructions per read).
-//
-// Key sub-tiles of 32 rows are software-pipelined, step j:
-//   phase 1: S^T(j) = K Q^T          | VALU: P(j-1) = exp2(S scale log2e - L2)
-//   phase 2: dP^T(j) = V dO^T        | VALU: dS(j-1) = P o (dP - D), packed
-//   phase 3: dQ^T += K^T dS^T (j-1)
-// Operand reads run AH fragments ahead and across phase boundaries.  Key
-// tiles of 64 rows rotate through four LDS buffers, copied two tiles ahead,
-// so the tile of sub-tile j-1 is still resident while step j reads it.
+// dQ (bf16).  Workgroup = NW waves = 256 query rows of one (b, h); wave w owns
+// query rows qw + [0, WQ) as WQ / 32 halves of 32 rows.  Q and dO of the
+// wave's rows and its dQ^T accumulators live in AGPRs for the whole kernel;
+// L2 and D are one scalar per lane and half.  With two halves each LDS
+// operand fragment feeds two matrix instructions; with 8 waves (two per
+// SIMD) one wave's softmax VALU work and LDS reads overlap the other's
+// matrix instructions.  Per key sub-tile of 32 rows:
+//   S^T = K Q^T, dP^T = V dO^T (with P = exp2(S scale log2e - L2) on the
+//   VALU under the dP^T chain), dS = P o (dP - D), dQ^T += K^T dS^T.
+// Operand reads run AH fragments ahead through a whole 64-row key tile.  Key
+// tiles ping-pong between two separately named LDS buffers (so the
+// transposing reads provably do not overlap the copy in flight).  No atomics.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void bwd_dq_bf16_kernel(
+template <int D, bool CAUSAL, int WQ, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    const bf16* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dws,
+    const bf16* __restrict__ dO, const float* __restrict__ nL2, const float* __restrict__ nD,
     bf16* __restrict__ dQ, int H, int N, int d, float scale_log2, float scale) {
   using M = Mma<bf16>;
   using frag = bf16x8;
-  constexpr int BQ = 256, WQ = 64, BKV = 64, KS = D / 16, MT = D / 32, AH = 4;
-  constexpr int PER = 16 / KS;      // elements per half handled per phase iteration
+  constexpr int NH = WQ / 32;                  // 32-row halves per wave
+  constexpr int BQ = NW * WQ, BKV = 64, KS = D / 16, MT = D / 32, AH = 4;
+  constexpr int NT = NW * 64;
+  constexpr int PER = 16 / KS;                 // elements per half handled per dP step
+  static_assert(NH == 1 || NH == 2, "32 or 64 query rows per wave");
   using KT = Tile<bf16, BKV, D>;
   struct __align__(16) Buf {
     bf16 k[KT::ELEMS];
@@ -299,28 +287,28 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_bf16_kernel(
   const int head = blockIdx.y, b = blockIdx.z;
   const long rs = (long)H * d;
   const long base = ((long)b * N * H + head) * d;
-  const float* Lh = L2 + ((long)b * H + head) * N;
-  const float* Dh = Dws + ((long)b * H + head) * N;
+  const float* Lh = nL2 + ((long)b * H + head) * N;   // -L * log2(e)
+  const float* Dh = nD + ((long)b * H + head) * N;    // -D
 
   const int qb = ib * BQ;
   const int qw = qb + wave * WQ;               // this wave's first query row
   const LanePlan<D> plan(lane);
-  frag qf[2][KS], of[2][KS];
-  float Lq[2], Dq[2];
+  frag qf[NH][KS], of[NH][KS];
+  float Lq[NH], Dq[NH];
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
+  for (int c = 0; c < NH; ++c) {
     const int q = qw + 32 * c + l32;
     load_row_frags<bf16, D>(qf[c], Q + base, rs, q, N, d, h);
     load_row_frags<bf16, D>(of[c], dO + base, rs, q, N, d, h);
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) { pin_agpr(qf[c][kk]); pin_agpr(of[c][kk]); }
-    Lq[c] = q < N ? Lh[q] : __builtin_inff();
+    Lq[c] = q < N ? Lh[q] : -__builtin_inff();        // padded rows: P = 0
     Dq[c] = q < N ? Dh[q] : 0.f;
   }
 
-  f32x16 acc[2][MT];
+  f32x16 acc[NH][MT];
 #pragma unroll
-  for (int c = 0; c < 2; ++c)
+  for (int c = 0; c < NH; ++c)
 #pragma unroll
     for (int i = 0; i < MT; ++i) { acc[c][i] = zero16(); pin_agpr(acc[c][i]); }
 
@@ -332,11 +320,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_bf16_kernel(
   auto fill = [&](Buf& B, int kt) ATTN_INLINE {
     const int k0 = kt * BKV;
     if (k0 + BKV <= N && d == D) {
-      fill_async(KT{B.k}, K + base, rs, k0, wave, lane);
-      fill_async(KT{B.v}, V + base, rs, k0, wave, lane);
+      fill_async<BKV, D, NW>(KT{B.k}, K + base, rs, k0, wave, lane);
+      fill_async<BKV, D, NW>(KT{B.v}, V + base, rs, k0, wave, lane);
     } else {
-      fill_sync(KT{B.k}, K + base, rs, k0, N, d, tid);
-      fill_sync(KT{B.v}, V + base, rs, k0, N, d, tid);
+      fill_sync<bf16, BKV, D, NT>(KT{B.k}, K + base, rs, k0, N, d, tid);
+      fill_sync<bf16, BKV, D, NT>(KT{B.v}, V + base, rs, k0, N, d, tid);
     }
   };
 
@@ -344,7 +332,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_bf16_kernel(
   // sub-tile is K (head dim), V (head dim), K^T (positions); reads run AH
   // operands ahead through the whole tile.
   constexpr int OPS = 2 * KS + 2 * MT;          // operands per sub-tile
-  auto tile_body = [&](int kt, const Buf& B, bool masked) ATTN_INLINE {
+  auto tile_body = [&](int kt, const Buf& B, auto masked_c) ATTN_INLINE {
+    constexpr bool MASKED = decltype(masked_c)::value;
     auto opnd = [&](int n) ATTN_INLINE -> frag {
       const int r0 = (n / OPS) * 32, m = n % OPS;
       if (m < KS) return plan.cols(B.k, r0, m);
@@ -360,40 +349,40 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_bf16_kernel(
     for (int st = 0; st < 2; ++st) {
       const int ka = kt * BKV + st * 32;          // absolute first key row of the sub-tile
       const int n0 = st * OPS;
-      f32x16 sc[2], pc[2];
-      // S^T = K Q^T (both halves)
+      f32x16 sc[NH], pc[NH];
+      // S^T = K Q^T
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
         const int n = n0 + kk;
         const frag a = ring[n % AH];
         if (n + AH < 2 * OPS) ring[n % AH] = opnd(n + AH);
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
+        for (int c = 0; c < NH; ++c)
           sc[c] = kk == 0 ? M::mma(a, qf[c][0], zero16()) : M::mma(a, qf[c][kk], sc[c]);
         fence();
       }
-      // dP^T = V dO^T (both halves) | P = exp2(S scale log2e - L2) on the VALU
+      // dP^T = V dO^T | P = exp2(S scale log2e - L2) on the VALU
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
         const int n = n0 + KS + kk;
         const frag a = ring[n % AH];
         if (n + AH < 2 * OPS) ring[n % AH] = opnd(n + AH);
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
+        for (int c = 0; c < NH; ++c)
           pc[c] = kk == 0 ? M::mma(a, of[c][0], zero16()) : M::mma(a, of[c][kk], pc[c]);
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
+        for (int c = 0; c < NH; ++c)
 #pragma unroll
           for (int e = 0; e < PER; ++e) {
             const int r = kk * PER + e;
-            sc[c][r] = fast_exp2(__builtin_fmaf(sc[c][r], scale_log2, -Lq[c]));
+            sc[c][r] = fast_exp2(__builtin_fmaf(sc[c][r], scale_log2, Lq[c]));
           }
         fence();
       }
       // causal element mask, only on tiles that cross the diagonal
-      if (masked) {
+      if constexpr (CAUSAL && MASKED) {
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
+        for (int c = 0; c < NH; ++c) {
           const int q = qw + 32 * c + l32;
 #pragma unroll
           for (int r = 0; r < 16; ++r)
@@ -401,10 +390,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_bf16_kernel(
         }
       }
       fence();
-      // dS = P o (dP - D): half 0 now, half 1 under half 0's dQ products
-      frag bds[2][2];
+      // dS = P o (dP - D): half 0 now, half 1 (if any) under half 0's dQ products
+      frag bds[NH][2];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) pc[0][r] = sc[0][r] * (pc[0][r] - Dq[0]);
+      for (int r = 0; r < 16; ++r) pc[0][r] = sc[0][r] * (pc[0][r] + Dq[0]);
       bds[0][0] = M::pack(pc[0], 0);
       bds[0][1] = M::pack(pc[0], 1);
       fence();
@@ -416,39 +405,51 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_bf16_kernel(
         t[i] = ring[n % AH];
         if (n + AH < 2 * OPS) ring[n % AH] = opnd(n + AH);
         mma_acc_agpr(acc[0][i % MT], t[i], bds[0][i / MT]);
+        if constexpr (NH == 2) {
 #pragma unroll
-        for (int e = 0; e < PER3; ++e) {
-          const int r = i * PER3 + e;
-          pc[1][r] = sc[1][r] * (pc[1][r] - Dq[1]);
+          for (int e = 0; e < PER3; ++e) {
+            const int r = i * PER3 + e;
+            pc[NH - 1][r] = sc[NH - 1][r] * (pc[NH - 1][r] + Dq[NH - 1]);
+          }
         }
         fence();
       }
-      bds[1][0] = M::pack(pc[1], 0);
-      bds[1][1] = M::pack(pc[1], 1);
-      fence();
+      if constexpr (NH == 2) {
+        bds[1][0] = M::pack(pc[1], 0);
+        bds[1][1] = M::pack(pc[1], 1);
+        fence();
 #pragma unroll
-      for (int i = 0; i < 2 * MT; ++i) mma_acc_agpr(acc[1][i % MT], t[i], bds[1][i / MT]);
-      fence();
+        for (int i = 0; i < 2 * MT; ++i) mma_acc_agpr(acc[1][i % MT], t[i], bds[1][i / MT]);
+        fence();
+      }
     }
   };
 
   // tile kt + 1 is copied into the other buffer while tile kt is consumed
-  auto run_tile = [&](int kt, const Buf& cur, Buf& nxt) ATTN_INLINE {
+  auto run_tile = [&](int kt, const Buf& cur, Buf& nxt, auto masked_c) ATTN_INLINE {
     wait_async_fills();
     __syncthreads();
     if (kt + 1 < ntiles) fill(nxt, kt + 1);
-    tile_body(kt, cur, kt >= diag0);
+    tile_body(kt, cur, masked_c);
   };
 
+  // even tiles use buf0, odd tiles buf1; the masked walk starts at an even
+  // tile (a tile or so before the diagonal also takes the mask: harmless)
+  const int split = diag0 & ~1;
   fill(buf0, 0);
-  for (int kt = 0; kt < ntiles; kt += 2) {
-    run_tile(kt, buf0, buf1);
-    if (kt + 1 < ntiles) run_tile(kt + 1, buf1, buf0);
+  int kt = 0;
+  for (; kt < split; kt += 2) {
+    run_tile(kt, buf0, buf1, bool_c<false>{});
+    run_tile(kt + 1, buf1, buf0, bool_c<false>{});
+  }
+  for (; kt < ntiles; kt += 2) {
+    run_tile(kt, buf0, buf1, bool_c<true>{});
+    if (kt + 1 < ntiles) run_tile(kt + 1, buf1, buf0, bool_c<true>{});
   }
 
   mma_acc_drain();
 #pragma unroll
-  for (int c = 0; c < 2; ++c)
+  for (int c = 0; c < NH; ++c)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
       store_acc_transposed<bf16>(acc[c][mt], dQ + base, rs, qw + 32 * c, mt * 32, N, d, scale,
@@ -471,10 +472,15 @@ static hipError_t dkdv_pipe_go(const BwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// 256 query rows per workgroup as DQ_NW waves of 256 / DQ_NW rows
+#ifndef ATTN_DQ_NW
+#define ATTN_DQ_NW 4
+#endif
 template <int D, bool C>
 static hipError_t dq_pipe_go(const BwdArgs& a, hipStream_t stream) {
+  constexpr int NW = ATTN_DQ_NW, WQ = 256 / NW;
   dim3 grid((a.N + 255) / 256, a.H, a.B);
-  hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, C>), grid, dim3(256), 0, stream,
+  hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, C, WQ, NW>), grid, dim3(NW * 64), 0, stream,
                      static_cast<const bf16*>(a.Q), static_cast<const bf16*>(a.K),
                      static_cast<const bf16*>(a.V), static_cast<const bf16*>(a.dO),
                      a.Dws + rows_of(a), a.Dws, static_cast<bf16*>(a.dQ), a.H, a.N, a.d,

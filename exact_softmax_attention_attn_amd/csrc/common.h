@@ -240,16 +240,16 @@ template <int ROWS, int D> struct Tile<float, ROWS, D> {
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int ROWS, int D>
+template <int ROWS, int D, int NWAVES = 4>
 __device__ __forceinline__ void fill_async(const Tile<bf16, ROWS, D>& t, const bf16* g, long rs,
                                            int row0, int wave, int lane) {
   constexpr int CPR = D / 8;              // chunks per row
   constexpr int RPI = 64 / CPR;           // rows per wave instruction
   constexpr int NI = ROWS / RPI;          // wave instructions per tile
-  static_assert(NI % 4 == 0, "tile must split evenly over 4 waves");
+  static_assert(NI % NWAVES == 0, "tile must split evenly over the waves");
 #pragma unroll
-  for (int i = 0; i < NI / 4; ++i) {
-    const int inst = wave * (NI / 4) + i;
+  for (int i = 0; i < NI / NWAVES; ++i) {
+    const int inst = wave * (NI / NWAVES) + i;
     const int r = inst * RPI + lane / CPR;
     const int chunk = (lane % CPR) ^ Tile<bf16, ROWS, D>::swz(r);
     const bf16* src = g + (long)(row0 + r) * rs + chunk * 8;
@@ -268,27 +268,26 @@ __device__ __forceinline__ void wait_async_fills() {
   __builtin_amdgcn_s_waitcnt(0x3F70);
 }
 
-template <typename T, int ROWS, int D>
+template <typename T, int ROWS, int D, int NT = kThreads>
 __device__ __forceinline__ void fill_sync(const Tile<T, ROWS, D>& t, const T* g, long rs, int row0,
                                           int nrows, int ncols, int tid) {
   using chunk = typename Mma<T>::chunk;
   constexpr int CH = Mma<T>::CHUNK;
   constexpr int CPR = D / CH;
-  constexpr int NCH = ROWS * CPR / kThreads;
-  static_assert(ROWS * CPR % kThreads == 0, "tile must split evenly over 256 threads");
+  constexpr int NCH = (ROWS * CPR + NT - 1) / NT;
   chunk v[NCH];
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
-    const int u = tid + kThreads * i;
+    const int u = tid + NT * i;
     const int r = u / CPR, c = (u % CPR) * CH;
     v[i] = chunk{};
-    if (row0 + r < nrows && c < ncols)
+    if (u < ROWS * CPR && row0 + r < nrows && c < ncols)
       v[i] = *reinterpret_cast<const chunk*>(g + (long)(row0 + r) * rs + c);
   }
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
-    const int u = tid + kThreads * i;
-    t.put(u / CPR, u % CPR, v[i]);
+    const int u = tid + NT * i;
+    if (u < ROWS * CPR) t.put(u / CPR, u % CPR, v[i]);
   }
 }
 

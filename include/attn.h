@@ -81,9 +81,9 @@ int attn_fwd_lse(const void* Q, const void* K, const void* V, void* O, float* L,
                  void* stream);
 
 /* Bytes of device workspace attn_bwd needs: 2*B*H*N*sizeof(float).  It holds
- * D [B, H, N] followed by L * log2(e) [B, H, N] (the row scalar in the base-2
- * units the kernels exponentiate in).  Returns 0 when a size is < 1 or the
- * sizes are unsupported. */
+ * -D [B, H, N] followed by -L * log2(e) [B, H, N] (the row scalars negated and,
+ * for L, in the base-2 units the kernels exponentiate in).  Returns 0 when a
+ * size is < 1 or the sizes are unsupported. */
 size_t attn_bwd_workspace_bytes(int B, int H, int N, int d);
 
 /*
@@ -93,7 +93,7 @@ size_t attn_bwd_workspace_bytes(int B, int H, int N, int d);
  *        by attn_fwd_lse (or any L_i = log sum_j exp(S_ij) of the same kept set)
  *   out: dQ, dK, dV     [B, N, H, d] (dtype)
  *   workspace: >= attn_bwd_workspace_bytes(B, H, N, d) bytes of device memory,
- *        16-byte aligned; overwritten with D and L * log2(e).
+ *        16-byte aligned; overwritten with -D and -L * log2(e).
  * PR #162 ("perf(ddx-ad): transpose causal attention's contractions without
  * their joins", section "What changed") names the plan: transpose p = w/z per
  * score, then p @ v.
@@ -105,7 +105,7 @@ int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const v
 /*
  * Stage 1 of attn_bwd: D_i = sum_c dO_ic O_ic in float32 (the softmax-weighted
  * sum of dP, issue #243 item 2, since sum_j P_ij dP_ij = dO_i . O_i) and
- * L_i * log2(e), written to workspace as two [B, H, N] float32 arrays.
+ * L_i * log2(e), written negated to workspace as two [B, H, N] float32 arrays.
  */
 int attn_bwd_preprocess(const void* O, const void* dO, const float* L, void* workspace,
                         int B, int H, int N, int d, int dtype, void* stream);
@@ -114,7 +114,7 @@ int attn_bwd_preprocess(const void* O, const void* dO, const float* L, void* wor
  * Stage 2 of attn_bwd: dK and dV.  One workgroup owns a block of key rows,
  * keeps K, V and the dK, dV accumulators on chip, and walks the query blocks
  * that can see them (from the diagonal down when causal), rebuilding S, P,
- * dP and dS per tile.  Reads D and L * log2(e) from workspace (stage 1 must
+ * dP and dS per tile.  Reads -D and -L * log2(e) from workspace (stage 1 must
  * have run on the same workspace).
  */
 int attn_bwd_dkdv(const void* Q, const void* K, const void* V, const void* dO,
@@ -126,7 +126,7 @@ int attn_bwd_dkdv(const void* Q, const void* K, const void* V, const void* dO,
  * Stage 3 of attn_bwd: dQ.  One workgroup owns a block of query rows and walks
  * the key blocks it can see, rebuilding S, P, dP and dS and accumulating
  * dS K on chip.  No atomics: every dQ element is written once by one thread,
- * so results are bitwise repeatable.  Reads D and L * log2(e) from workspace.
+ * so results are bitwise repeatable.  Reads -D and -L * log2(e) from workspace.
  */
 int attn_bwd_dq(const void* Q, const void* K, const void* V, const void* dO,
                 const void* workspace, void* dQ,
