@@ -211,31 +211,40 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     }
   };
 
-  // tile t + 1 is copied into the other buffer while tile t is consumed
-  auto run_tile = [&](int t, const Buf& cur, Buf& nxt, auto masked_c) ATTN_INLINE {
+  // Walk the query tiles from the last one back to the diagonal: every block
+  // of a head starts on the same tiles at the same time, so they are shared
+  // in L2 instead of each block streaming its own stretch.  Step k visits
+  // tile ntiles - 1 - k, in buffer k % 2; the two diagonal tiles (BKV = 2 BQ)
+  // come last and carry the causal mask.
+  const int nmask = CAUSAL ? min(2, ntiles) : 0;
+  const int kend = ntiles - nmask;
+  auto tile_of = [&](int k) ATTN_INLINE { return ntiles - 1 - k; };
+  auto step = [&](int k, const Buf& cur, Buf& nxt, auto masked_c) ATTN_INLINE {
     wait_async_fills();
     __syncthreads();
-    if (t + 1 < ntiles) fill(nxt, t + 1);
-    tile_body(t, cur, masked_c);
+    if (k + 1 < ntiles) fill(nxt, tile_of(k + 1));
+    tile_body(tile_of(k), cur, masked_c);
   };
-
-  // causal: tiles 0 and 1 of the walk straddle the diagonal (BKV = 2 BQ)
-  const int nmask = CAUSAL ? min(2, ntiles) : 0;
-  fill(buf0, 0);
-  int t = 0;
-  if (nmask > 0) {
-    run_tile(0, buf0, buf1, bool_c<true>{});
-    if (nmask > 1) run_tile(1, buf1, buf0, bool_c<true>{});
-    t = nmask;
+  // Buffers are picked statically on every path (a runtime choice between
+  // them makes the compiler shuffle the accumulators between registers, which
+  // it cannot time against the in-flight products): an odd number of unmasked
+  // steps starts in buf1, so the unmasked loop and the masked tail both start
+  // in buf0.
+  int k = 0;
+  if (kend & 1) {
+    fill(buf1, tile_of(0));
+    step(0, buf1, buf0, bool_c<false>{});
+    mma_acc_drain();                         // the join below may copy accumulators
+    k = 1;
+  } else {
+    fill(buf0, tile_of(0));
   }
-  if ((t & 1) && t < ntiles) {               // keep even tiles in buf0
-    run_tile(t, buf1, buf0, bool_c<false>{});
-    ++t;
+  for (; k < kend; k += 2) {
+    step(k, buf0, buf1, bool_c<false>{});
+    step(k + 1, buf1, buf0, bool_c<false>{});
   }
-  for (; t < ntiles; t += 2) {
-    run_tile(t, buf0, buf1, bool_c<false>{});
-    if (t + 1 < ntiles) run_tile(t + 1, buf1, buf0, bool_c<false>{});
-  }
+  if (nmask > 0) step(kend, buf0, buf1, bool_c<true>{});
+  if (nmask > 1) step(kend + 1, buf1, buf0, bool_c<true>{});
 
   mma_acc_drain();
 #pragma unroll

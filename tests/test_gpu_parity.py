@@ -112,6 +112,7 @@ EDGE = [
     (2, 1, 200, 128, "f32", True),
     (1, 2, 129, 8, "bf16", True),
     (1, 2, 300, 40, "bf16", True),
+    (1, 1, 300, 128, "bf16", True),   # odd tile counts per key block
     (1, 2, 300, 100, "f32", True),
     (2, 2, 77, 32, "f32", False),
     (1, 2, 190, 128, "bf16", False),
