@@ -404,9 +404,9 @@ static hipError_t dq_go(const BwdArgs& a, hipStream_t stream) {
     return FN<float, 128, false>(a, stream);                                          \
   } while (0)
 
-// bf16 with a 64- or 128-column head-dim bucket runs the software-pipelined
-// kernels; everything else the generic ones.
-static bool use_pipe(const BwdArgs& a) { return a.dtype == 1 && head_dim_bucket(a.d) >= 64; }
+// bf16 with a head dim of exactly 64 or 128 runs the software-pipelined
+// kernels (they copy whole tiles only); everything else the generic ones.
+static bool use_pipe(const BwdArgs& a) { return a.dtype == 1 && (a.d == 64 || a.d == 128); }
 
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream) {
   if (use_pipe(a)) return launch_bwd_dkdv_bf16_pipe(a, stream);

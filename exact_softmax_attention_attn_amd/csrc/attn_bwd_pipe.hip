@@ -2,20 +2,18 @@
 //
 // Same method as the generic kernels (scores rebuilt per tile from Q, K and
 // the saved row scalar, ddx issue #243 item 2; dS = P o (dP - D) with no
-// row-max term, issue #243 item 1; PR #162's plan p = w/z then p @ v), with
-// one wave per SIMD and the work of consecutive 32-row sub-tiles overlapped
-// by hand:
-//
-//   step k:  stage A of sub-tile k      (the two products over the head dim)
-//            stage B of sub-tile k - 1  (softmax-backward VALU work and the
-//                                        products over positions)
-//
-// The two stages share no registers, so the matrix cores run stage A's
-// chains while the VALU rebuilds P and dS for stage B, and the LDS reads for
-// later products are issued a few instructions ahead of their use.  The
-// instruction order inside a step is fixed with scheduling fences.  Tiles of
-// 64 rows are triple-buffered in LDS and copied global->LDS two sub-steps
-// before they are read.
+// row-max term, issue #243 item 1; PR #162's plan p = w/z then p @ v), shaped
+// for one wave per SIMD:
+//  - the long-lived operands (K, V or Q, dO of the wave's rows) and the
+//    accumulators stay in AGPRs for the whole kernel; products that the VALU
+//    reads next (S, dP) land in VGPRs;
+//  - the streamed tile operands are read from LDS a few fragments ahead of the
+//    product that consumes them, in a fixed order held by scheduling fences;
+//  - the row scalars (-L log2 e and -D) are added by the matrix cores, so the
+//    VALU is left with one exp2 and one multiply per score;
+//  - streamed tiles are copied global->LDS two steps ahead into a ring of
+//    three separately named buffers, with direct-to-LDS copies that the
+//    compiler does not track and explicit waits before each hand-off.
 #include <type_traits>
 
 #include "common.h"
@@ -44,11 +42,10 @@ __device__ __forceinline__ f32x4 lds_f32x4(const float* p) {
 // LDS straight into the accumulator registers, and
 //   S' = Q (c K)^T - L2 = log2 of P,   dP' = dO V^T - D
 // leave one exp2 and one multiply per element:  P = exp2(S'), dS = P o dP'.
-// dV^T += dO^T P and dK^T += Q^T dS accumulate in AGPRs (asm MFMA).  Query
-// tiles of 64 rows ping-pong between two separately named LDS buffers; the
+// dV^T += dO^T P and dK^T += Q^T dS accumulate in AGPRs (asm MFMA).  The
 // operand reads (Q, dO along the head dim; dO, Q across positions) run AH
-// fragments ahead through a whole tile.  Causal: the walk starts at the
-// diagonal; only its first two tiles carry the element mask.
+// fragments ahead through a whole 64-row query tile.  Causal: only the two
+// tiles on the diagonal carry the element mask.
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
@@ -67,9 +64,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     float l[BQ];      // -L * log2(e)
     float dd[BQ];     // -D
   };
-  __shared__ Buf buf0, buf1;
+  __shared__ Buf buf0, buf1, buf2;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+  const int wave = wave_uniform(tid >> 6);
   const int jb = blockIdx.x, head = blockIdx.y, b = blockIdx.z;
   const long rs = (long)H * d;
   const long base = ((long)b * N * H + head) * d;
@@ -102,13 +100,24 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
   const int qt0 = CAUSAL ? kvb / BQ : 0;
   const int ntiles = nqt - qt0;
 
+  unsigned copy_off[AsyncFillShape<BQ, D>::PER];
+  async_fill_plan<BQ, D>(copy_off, rs, wave, lane);
+  // A query tile (Q, dO rows and their two row scalars) into LDS.  Whole
+  // tiles go by direct global->LDS copies: 2 * PER instructions per wave,
+  // plus one for the row scalars on waves 0 and 1.  The walk's first tile may
+  // be the sequence's ragged last one: register path with zero padding.
+  using FS = AsyncFillShape<BQ, D>;
+  auto fill_whole = [&](Buf& B, int t) ATTN_INLINE {
+    const int q0 = (qt0 + t) * BQ;
+    async_fill_untracked<BQ, D>(QT{B.q}, Q + base + q0 * rs, copy_off, wave);
+    async_fill_untracked<BQ, D>(QT{B.o}, dO + base + q0 * rs, copy_off, wave);
+    if (wave == 0) fill_row64_untracked(B.l, Lh + q0, lane);
+    if (wave == 1) fill_row64_untracked(B.dd, Dh + q0, lane);
+  };
   auto fill = [&](Buf& B, int t) ATTN_INLINE {
     const int q0 = (qt0 + t) * BQ;
-    if (q0 + BQ <= N && d == D) {
-      fill_async(QT{B.q}, Q + base, rs, q0, wave, lane);
-      fill_async(QT{B.o}, dO + base, rs, q0, wave, lane);
-      if (wave == 0) fill_async_row64(B.l, Lh + q0);
-      if (wave == 1) fill_async_row64(B.dd, Dh + q0);
+    if (q0 + BQ <= N) {
+      fill_whole(B, t);
     } else {
       fill_sync(QT{B.q}, Q + base, rs, q0, N, d, tid);
       fill_sync(QT{B.o}, dO + base, rs, q0, N, d, tid);
@@ -120,8 +129,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     }
   };
 
-  auto tile_body = [&](int t, const Buf& B, auto masked_c) ATTN_INLINE {
-    constexpr bool MASKED = decltype(masked_c)::value;
+  auto tile_body = [&](int t, const Buf& B, bool masked) ATTN_INLINE {
     // operand n of the tile: sub-tile n / OPS; within it Q cols, dO cols,
     // dO rows (dV), Q rows (dK)
     auto opnd = [&](int n) ATTN_INLINE -> frag {
@@ -174,7 +182,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
         for (int e = 0; e < PER; ++e) sc[ks * PER + e] = fast_exp2(sc[ks * PER + e]);
         fence();
       }
-      if constexpr (CAUSAL && MASKED) {
+      if (CAUSAL && masked) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           if (kv > qa + acc_row(r, h)) sc[r] = 0.f;
@@ -214,37 +222,31 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
   // Walk the query tiles from the last one back to the diagonal: every block
   // of a head starts on the same tiles at the same time, so they are shared
   // in L2 instead of each block streaming its own stretch.  Step k visits
-  // tile ntiles - 1 - k, in buffer k % 2; the two diagonal tiles (BKV = 2 BQ)
-  // come last and carry the causal mask.
-  const int nmask = CAUSAL ? min(2, ntiles) : 0;
-  const int kend = ntiles - nmask;
+  // tile ntiles - 1 - k; causal: the last two steps (the diagonal tiles,
+  // BKV = 2 BQ) apply the element mask.  Tiles are copied two steps ahead
+  // into a ring of three separately named buffers picked statically (the loop
+  // is unrolled by three), so a copy has two steps to land: step k waits only
+  // for tile k's copy, leaving tile k + 1's in flight.  A runtime choice
+  // between buffers would make the compiler shuffle the accumulators between
+  // registers while products are in flight.
   auto tile_of = [&](int k) ATTN_INLINE { return ntiles - 1 - k; };
-  auto step = [&](int k, const Buf& cur, Buf& nxt, auto masked_c) ATTN_INLINE {
-    wait_async_fills();
-    __syncthreads();
-    if (k + 1 < ntiles) fill(nxt, tile_of(k + 1));
-    tile_body(tile_of(k), cur, masked_c);
+  auto step = [&](int k, const Buf& cur, Buf& ahead) ATTN_INLINE {
+    if (k + 1 < ntiles) wait_async_fills_but<2 * FS::PER>();   // tile k + 1's copy may fly
+    else wait_async_fills();
+    lds_barrier();
+    if (k + 2 < ntiles) fill_whole(ahead, tile_of(k + 2));
+    tile_body(tile_of(k), cur, CAUSAL && k + 2 >= ntiles);
   };
-  // Buffers are picked statically on every path (a runtime choice between
-  // them makes the compiler shuffle the accumulators between registers, which
-  // it cannot time against the in-flight products): an odd number of unmasked
-  // steps starts in buf1, so the unmasked loop and the masked tail both start
-  // in buf0.
+  fill(buf0, tile_of(0));
+  if (ntiles > 1) fill_whole(buf1, tile_of(1));
   int k = 0;
-  if (kend & 1) {
-    fill(buf1, tile_of(0));
-    step(0, buf1, buf0, bool_c<false>{});
-    mma_acc_drain();                         // the join below may copy accumulators
-    k = 1;
-  } else {
-    fill(buf0, tile_of(0));
+  for (; k + 3 <= ntiles; k += 3) {
+    step(k, buf0, buf2);
+    step(k + 1, buf1, buf0);
+    step(k + 2, buf2, buf1);
   }
-  for (; k < kend; k += 2) {
-    step(k, buf0, buf1, bool_c<false>{});
-    step(k + 1, buf1, buf0, bool_c<false>{});
-  }
-  if (nmask > 0) step(kend, buf0, buf1, bool_c<true>{});
-  if (nmask > 1) step(kend + 1, buf1, buf0, bool_c<true>{});
+  if (k < ntiles) step(k, buf0, buf2);
+  if (k + 1 < ntiles) step(k + 1, buf1, buf0);
 
   mma_acc_drain();
 #pragma unroll
@@ -256,17 +258,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
 
 // ---------------------------------------------------------------------------
 // dQ (bf16).  Workgroup = NW waves = 256 query rows of one (b, h); wave w owns
-// query rows qw + [0, WQ) as WQ / 32 halves of 32 rows.  Q and dO of the
-// wave's rows and its dQ^T accumulators live in AGPRs for the whole kernel;
-// L2 and D are one scalar per lane and half.  With two halves each LDS
-// operand fragment feeds two matrix instructions; with 8 waves (two per
-// SIMD) one wave's softmax VALU work and LDS reads overlap the other's
-// matrix instructions.  Per key sub-tile of 32 rows:
-//   S^T = K Q^T, dP^T = V dO^T (with P = exp2(S scale log2e - L2) on the
-//   VALU under the dP^T chain), dS = P o (dP - D), dQ^T += K^T dS^T.
-// Operand reads run AH fragments ahead through a whole 64-row key tile.  Key
-// tiles ping-pong between two separately named LDS buffers (so the
-// transposing reads provably do not overlap the copy in flight).  No atomics.
+// query rows qw + [0, WQ) as WQ / 32 halves of 32 rows.  Q (pre-multiplied by
+// scale log2e) and dO of the wave's rows and its dQ^T accumulators live in
+// AGPRs for the whole kernel.  With two halves each LDS operand fragment
+// feeds two matrix instructions.  Per key sub-tile of 32 rows:
+//   S'^T = K (c Q)^T - L2,  dP'^T = V dO^T - D,  P = exp2(S'),
+//   dS = P o dP',  dQ^T += K^T dS^T.
+// The query rows run along the lanes here, so the row scalars cannot enter as
+// a per-register C input; instead each chain starts with one extra product of
+// a constant "ones" fragment and a fragment carrying the row scalar split
+// into two bf16 parts (hi + lo, exact to about 2^-16 relative), which adds the
+// scalar to every element.  That costs one matrix instruction per chain and
+// saves an add per element on the VALU.  Operand reads run AH fragments ahead
+// through a whole 64-row key tile.  Key tiles are copied two steps ahead into
+// a ring of three separately named LDS buffers.  No atomics.
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL, int WQ, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
@@ -285,12 +290,10 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
     bf16 k[KT::ELEMS];
     bf16 v[KT::ELEMS];
   };
-  // Two separately named buffers, each always addressed through its own
-  // name: the transposing LDS reads then provably do not overlap the copy in
-  // flight into the other buffer, and need not wait for it.
-  __shared__ Buf buf0, buf1;
+  __shared__ Buf buf0, buf1, buf2;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+  const int wave = wave_uniform(tid >> 6);
   const int nqb = gridDim.x;
   const int ib = CAUSAL ? (nqb - 1 - (int)blockIdx.x) : (int)blockIdx.x;  // longest first
   const int head = blockIdx.y, b = blockIdx.z;
@@ -303,16 +306,31 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
   const int qw = qb + wave * WQ;               // this wave's first query row
   const LanePlan<D> plan(lane);
   frag qf[NH][KS], of[NH][KS];
-  float Lq[NH], Dq[NH];
+  // bias operands: ones[k] = 1 for k in {0, 1}; bl/bd[k] = (hi, lo) of the
+  // lane's row scalar for k in {0, 1}; zero elsewhere (K slots 8h .. 8h + 7)
+  frag ones, bl[NH], bd[NH];
+  const bf16 one = (bf16)1.f, zero = (bf16)0.f;
+  ones = h == 0 ? frag{one, one, zero, zero, zero, zero, zero, zero} : frag{};
 #pragma unroll
   for (int c = 0; c < NH; ++c) {
     const int q = qw + 32 * c + l32;
     load_row_frags<bf16, D>(qf[c], Q + base, rs, q, N, d, h);
     load_row_frags<bf16, D>(of[c], dO + base, rs, q, N, d, h);
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) { pin_agpr(qf[c][kk]); pin_agpr(of[c][kk]); }
-    Lq[c] = q < N ? Lh[q] : -__builtin_inff();        // padded rows: P = 0
-    Dq[c] = q < N ? Dh[q] : 0.f;
+    for (int kk = 0; kk < KS; ++kk) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[c][kk][e] = (bf16)((float)qf[c][kk][e] * scale_log2);
+      pin_agpr(qf[c][kk]);
+      pin_agpr(of[c][kk]);
+    }
+    // padded rows (q >= N): S' = -inf so P = 0 (lo part 0, never inf - inf)
+    const float lq = q < N ? Lh[q] : -__builtin_inff();
+    const float dq = q < N ? Dh[q] : 0.f;
+    const bf16 lhi = (bf16)lq, dhi = (bf16)dq;
+    const bf16 llo = q < N ? (bf16)(lq - (float)lhi) : zero;
+    const bf16 dlo = (bf16)(dq - (float)dhi);
+    bl[c] = h == 0 ? frag{lhi, llo, zero, zero, zero, zero, zero, zero} : frag{};
+    bd[c] = h == 0 ? frag{dhi, dlo, zero, zero, zero, zero, zero, zero} : frag{};
   }
 
   f32x16 acc[NH][MT];
@@ -326,11 +344,17 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
   // first tile holding key rows above some of the block's query rows
   const int diag0 = CAUSAL ? max(0, min(ntiles, qb / BKV)) : ntiles;
 
+  // A key tile (K and V rows) into LDS: whole tiles by direct copies (2 * PER
+  // instructions per wave), the sequence's ragged last tile by the register
+  // path with zero padding.
+  using FS = AsyncFillShape<BKV, D, NW>;
+  unsigned copy_off[FS::PER];
+  async_fill_plan<BKV, D, NW>(copy_off, rs, wave, lane);
   auto fill = [&](Buf& B, int kt) ATTN_INLINE {
     const int k0 = kt * BKV;
-    if (k0 + BKV <= N && d == D) {
-      fill_async<BKV, D, NW>(KT{B.k}, K + base, rs, k0, wave, lane);
-      fill_async<BKV, D, NW>(KT{B.v}, V + base, rs, k0, wave, lane);
+    if (k0 + BKV <= N) {
+      async_fill_untracked<BKV, D, NW>(KT{B.k}, K + base + k0 * rs, copy_off, wave);
+      async_fill_untracked<BKV, D, NW>(KT{B.v}, V + base + k0 * rs, copy_off, wave);
     } else {
       fill_sync<bf16, BKV, D, NT>(KT{B.k}, K + base, rs, k0, N, d, tid);
       fill_sync<bf16, BKV, D, NT>(KT{B.v}, V + base, rs, k0, N, d, tid);
@@ -341,8 +365,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
   // sub-tile is K (head dim), V (head dim), K^T (positions); reads run AH
   // operands ahead through the whole tile.
   constexpr int OPS = 2 * KS + 2 * MT;          // operands per sub-tile
-  auto tile_body = [&](int kt, const Buf& B, auto masked_c) ATTN_INLINE {
-    constexpr bool MASKED = decltype(masked_c)::value;
+  auto tile_body = [&](int kt, const Buf& B, bool masked) ATTN_INLINE {
     auto opnd = [&](int n) ATTN_INLINE -> frag {
       const int r0 = (n / OPS) * 32, m = n % OPS;
       if (m < KS) return plan.cols(B.k, r0, m);
@@ -359,37 +382,39 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
       const int ka = kt * BKV + st * 32;          // absolute first key row of the sub-tile
       const int n0 = st * OPS;
       f32x16 sc[NH], pc[NH];
-      // S^T = K Q^T
+      // S'^T = ones bl^T + K (c Q)^T
+#pragma unroll
+      for (int c = 0; c < NH; ++c) sc[c] = M::mma(ones, bl[c], zero16());
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
         const int n = n0 + kk;
         const frag a = ring[n % AH];
         if (n + AH < 2 * OPS) ring[n % AH] = opnd(n + AH);
 #pragma unroll
-        for (int c = 0; c < NH; ++c)
-          sc[c] = kk == 0 ? M::mma(a, qf[c][0], zero16()) : M::mma(a, qf[c][kk], sc[c]);
+        for (int c = 0; c < NH; ++c) sc[c] = M::mma(a, qf[c][kk], sc[c]);
         fence();
       }
-      // dP^T = V dO^T | P = exp2(S scale log2e - L2) on the VALU
+      // dP'^T = ones bd^T + V dO^T | P = exp2(S') on the VALU
+#pragma unroll
+      for (int c = 0; c < NH; ++c) pc[c] = M::mma(ones, bd[c], zero16());
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
         const int n = n0 + KS + kk;
         const frag a = ring[n % AH];
         if (n + AH < 2 * OPS) ring[n % AH] = opnd(n + AH);
 #pragma unroll
-        for (int c = 0; c < NH; ++c)
-          pc[c] = kk == 0 ? M::mma(a, of[c][0], zero16()) : M::mma(a, of[c][kk], pc[c]);
+        for (int c = 0; c < NH; ++c) pc[c] = M::mma(a, of[c][kk], pc[c]);
 #pragma unroll
         for (int c = 0; c < NH; ++c)
 #pragma unroll
           for (int e = 0; e < PER; ++e) {
             const int r = kk * PER + e;
-            sc[c][r] = fast_exp2(__builtin_fmaf(sc[c][r], scale_log2, Lq[c]));
+            sc[c][r] = fast_exp2(sc[c][r]);
           }
         fence();
       }
       // causal element mask, only on tiles that cross the diagonal
-      if constexpr (CAUSAL && MASKED) {
+      if (CAUSAL && masked) {
 #pragma unroll
         for (int c = 0; c < NH; ++c) {
           const int q = qw + 32 * c + l32;
@@ -399,10 +424,10 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
         }
       }
       fence();
-      // dS = P o (dP - D): half 0 now, half 1 (if any) under half 0's dQ products
+      // dS = P o dP': half 0 now, half 1 (if any) under half 0's dQ products
       frag bds[NH][2];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) pc[0][r] = sc[0][r] * (pc[0][r] + Dq[0]);
+      for (int r = 0; r < 16; ++r) pc[0][r] = sc[0][r] * pc[0][r];
       bds[0][0] = M::pack(pc[0], 0);
       bds[0][1] = M::pack(pc[0], 1);
       fence();
@@ -418,7 +443,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
 #pragma unroll
           for (int e = 0; e < PER3; ++e) {
             const int r = i * PER3 + e;
-            pc[NH - 1][r] = sc[NH - 1][r] * (pc[NH - 1][r] + Dq[NH - 1]);
+            pc[NH - 1][r] = sc[NH - 1][r] * pc[NH - 1][r];
           }
         }
         fence();
@@ -434,27 +459,27 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
     }
   };
 
-  // tile kt + 1 is copied into the other buffer while tile kt is consumed
-  auto run_tile = [&](int kt, const Buf& cur, Buf& nxt, auto masked_c) ATTN_INLINE {
-    wait_async_fills();
-    __syncthreads();
-    if (kt + 1 < ntiles) fill(nxt, kt + 1);
-    tile_body(kt, cur, masked_c);
+  // Key tiles are copied two steps ahead into a ring of three separately
+  // named buffers, picked statically (the loop is unrolled by three): step kt
+  // waits only for tile kt's copy and leaves tile kt + 1's in flight.  Tiles
+  // from diag0 on apply the causal element mask.
+  auto step = [&](int kt, const Buf& cur, Buf& ahead) ATTN_INLINE {
+    if (kt + 1 < ntiles) wait_async_fills_but<2 * FS::PER>();  // tile kt + 1's copy may fly
+    else wait_async_fills();
+    lds_barrier();
+    if (kt + 2 < ntiles) fill(ahead, kt + 2);
+    tile_body(kt, cur, CAUSAL && kt >= diag0);
   };
-
-  // even tiles use buf0, odd tiles buf1; the masked walk starts at an even
-  // tile (a tile or so before the diagonal also takes the mask: harmless)
-  const int split = diag0 & ~1;
   fill(buf0, 0);
+  if (ntiles > 1) fill(buf1, 1);
   int kt = 0;
-  for (; kt < split; kt += 2) {
-    run_tile(kt, buf0, buf1, bool_c<false>{});
-    run_tile(kt + 1, buf1, buf0, bool_c<false>{});
+  for (; kt + 3 <= ntiles; kt += 3) {
+    step(kt, buf0, buf2);
+    step(kt + 1, buf1, buf0);
+    step(kt + 2, buf2, buf1);
   }
-  for (; kt < ntiles; kt += 2) {
-    run_tile(kt, buf0, buf1, bool_c<true>{});
-    if (kt + 1 < ntiles) run_tile(kt + 1, buf1, buf0, bool_c<true>{});
-  }
+  if (kt < ntiles) step(kt, buf0, buf2);
+  if (kt + 1 < ntiles) step(kt + 1, buf1, buf0);
 
   mma_acc_drain();
 #pragma unroll

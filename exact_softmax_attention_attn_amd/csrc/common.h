@@ -60,6 +60,10 @@ __device__ __forceinline__ void mma_acc_agpr(f32x16& acc, const bf16x8& a, const
   asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
+// A value every lane of the wave agrees on, moved to a scalar register (so
+// addresses built from it stay scalar).
+__device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
 // Before the VALU reads AGPR accumulators written by mma_acc_agpr: the last
 // 32x32 matrix instruction must have written its results back (it takes 8
 // passes of 4 cycles plus write-back latency).
@@ -230,7 +234,7 @@ template <int ROWS, int D> struct Tile<float, ROWS, D> {
 // Filling a Tile with rows [row0, row0 + ROWS) x columns [0, D) of a global
 // [pos, row_stride] matrix, by all 256 threads.
 //
-// fill_async (bf16, whole tiles only): global_load_lds_dwordx4 copies 16
+// async_fill (bf16, whole tiles only): global_load_lds_dwordx4 copies 16
 // bytes per lane straight into LDS without passing through registers; one
 // wave instruction fills 1 KB of LDS, lane l landing at byte 16 l.  Each lane
 // therefore fetches the logical chunk that the swizzle stores at its LDS
@@ -240,21 +244,103 @@ template <int ROWS, int D> struct Tile<float, ROWS, D> {
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void;
 
+// The copy plan of one wave, built once per kernel: for each of the wave's
+// copy instructions, the byte offset (from the tile's first row in global
+// memory) of the chunk this lane fetches.  A fill then costs one copy
+// instruction per 1 KB with the tile's base address in scalar registers and
+// the lane's 32-bit offset in a vector register; no per-fill address math.
+// The offsets fit in 32 bits: ROWS <= 128 and rs = H * d <= 65535 * 128.
+template <int ROWS, int D, int NWAVES = 4> struct AsyncFillShape {
+  static constexpr int CPR = D / 8;       // chunks per row
+  static constexpr int RPI = 64 / CPR;    // rows per wave instruction
+  static constexpr int NI = ROWS / RPI;   // wave instructions per tile
+  static constexpr int PER = NI / NWAVES; // instructions per wave
+  static_assert(NI % NWAVES == 0, "tile must split evenly over the waves");
+};
+
+template <int ROWS, int D, int NWAVES = 4>
+__device__ __forceinline__ void async_fill_plan(unsigned* off, long rs, int wave, int lane) {
+  using S = AsyncFillShape<ROWS, D, NWAVES>;
+#pragma unroll
+  for (int i = 0; i < S::PER; ++i) {
+    const int r = (wave * S::PER + i) * S::RPI + lane / S::CPR;
+    const int chunk = (lane % S::CPR) ^ Tile<bf16, ROWS, D>::swz(r);
+    off[i] = (unsigned)(((long)r * rs + chunk * 8) * (long)sizeof(bf16));
+  }
+}
+
+// Copy instruction i (of the wave's PER) of the plan above.
+template <int ROWS, int D, int NWAVES = 4>
+__device__ __forceinline__ void async_fill_one(const Tile<bf16, ROWS, D>& t, const bf16* tile_base,
+                                               const unsigned* off, int wave, int i) {
+  using S = AsyncFillShape<ROWS, D, NWAVES>;
+  __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(tile_base) + off[i],
+                                   (lds_void*)(t.p + (wave * S::PER + i) * 512), 16, 0, 0);
+}
+
+// Rows [row0, row0 + ROWS) of a global matrix into t, by the plan above;
+// tile_base = (address of row row0) is the same in every lane.
+template <int ROWS, int D, int NWAVES = 4>
+__device__ __forceinline__ void async_fill(const Tile<bf16, ROWS, D>& t, const bf16* tile_base,
+                                           const unsigned* off, int wave) {
+  using S = AsyncFillShape<ROWS, D, NWAVES>;
+#pragma unroll
+  for (int i = 0; i < S::PER; ++i) async_fill_one<ROWS, D, NWAVES>(t, tile_base, off, wave, i);
+}
+
+// The same copies written as assembly, for the software-pipelined kernels
+// that keep copies in flight across barriers.  The compiler's wait insertion
+// cannot tell which LDS buffer a tracked copy writes and would drain every
+// copy before the next LDS read; it does not see these, so their users wait
+// explicitly (wait_async_fills*) before reading what they wrote.  M0 (the
+// LDS destination) is saved and restored around each copy.
+__device__ __forceinline__ unsigned lds_address(const void* p) {
+  return (unsigned)(unsigned long)((lds_void*)p);
+}
+__device__ __forceinline__ void lds_dma_b128(const void* sbase, unsigned voff, unsigned lds) {
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\ts_nop 0\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved) : "v"(voff), "s"(sbase), "s"(lds) : "memory");
+}
+__device__ __forceinline__ void lds_dma_b32(const void* sbase, unsigned voff, unsigned lds) {
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+      "global_load_lds_dword %1, %2\n\ts_nop 0\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved) : "v"(voff), "s"(sbase), "s"(lds) : "memory");
+}
+
+// Copy instruction i of the plan (assembly form); tile_base wave-uniform.
+template <int ROWS, int D, int NWAVES = 4>
+__device__ __forceinline__ void async_fill_one_untracked(const Tile<bf16, ROWS, D>& t,
+                                                         const bf16* tile_base, const unsigned* off,
+                                                         int wave, int i) {
+  using S = AsyncFillShape<ROWS, D, NWAVES>;
+  lds_dma_b128(tile_base, off[i], lds_address(t.p + (wave * S::PER + i) * 512));
+}
+template <int ROWS, int D, int NWAVES = 4>
+__device__ __forceinline__ void async_fill_untracked(const Tile<bf16, ROWS, D>& t,
+                                                     const bf16* tile_base, const unsigned* off,
+                                                     int wave) {
+  using S = AsyncFillShape<ROWS, D, NWAVES>;
+#pragma unroll
+  for (int i = 0; i < S::PER; ++i)
+    async_fill_one_untracked<ROWS, D, NWAVES>(t, tile_base, off, wave, i);
+}
+// 64 consecutive floats at g (wave-uniform) into LDS, assembly form.
+__device__ __forceinline__ void fill_row64_untracked(float* lds, const float* g, int lane) {
+  lds_dma_b32(g, (unsigned)lane * 4u, lds_address(lds));
+}
+
+// One-off form for kernels that do not keep a plan.
 template <int ROWS, int D, int NWAVES = 4>
 __device__ __forceinline__ void fill_async(const Tile<bf16, ROWS, D>& t, const bf16* g, long rs,
                                            int row0, int wave, int lane) {
-  constexpr int CPR = D / 8;              // chunks per row
-  constexpr int RPI = 64 / CPR;           // rows per wave instruction
-  constexpr int NI = ROWS / RPI;          // wave instructions per tile
-  static_assert(NI % NWAVES == 0, "tile must split evenly over the waves");
-#pragma unroll
-  for (int i = 0; i < NI / NWAVES; ++i) {
-    const int inst = wave * (NI / NWAVES) + i;
-    const int r = inst * RPI + lane / CPR;
-    const int chunk = (lane % CPR) ^ Tile<bf16, ROWS, D>::swz(r);
-    const bf16* src = g + (long)(row0 + r) * rs + chunk * 8;
-    __builtin_amdgcn_global_load_lds(src, (lds_void*)(t.p + inst * 512), 16, 0, 0);
-  }
+  unsigned off[AsyncFillShape<ROWS, D, NWAVES>::PER];
+  async_fill_plan<ROWS, D, NWAVES>(off, rs, wave, lane);
+  async_fill<ROWS, D, NWAVES>(t, g + (long)row0 * rs, off, wave);
 }
 
 // 64 consecutive floats (one wave instruction, 4 bytes per lane) into LDS.
@@ -262,10 +348,26 @@ __device__ __forceinline__ void fill_async_row64(float* lds, const float* g) {
   __builtin_amdgcn_global_load_lds(g + (threadIdx.x & 63), (lds_void*)lds, 4, 0, 0);
 }
 
+// Workgroup barrier for handing LDS tiles between waves.  __syncthreads()
+// also waits for every vector-memory operation of the wave (its release
+// fence), which would drain the global->LDS copies meant to stay in flight;
+// here the wave's own LDS operations complete, then all waves meet.  Copies
+// that must have landed are waited for explicitly (wait_async_fills*) before.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Wait until every global->LDS copy issued by this wave has landed.
 __device__ __forceinline__ void wait_async_fills() {
   // vmcnt = 0; expcnt and lgkmcnt left at their maxima (no wait)
   __builtin_amdgcn_s_waitcnt(0x3F70);
+}
+
+// Wait until at most N of this wave's vector-memory operations are still in
+// flight (they complete in issue order, so all but the last N have landed).
+template <int N> __device__ __forceinline__ void wait_async_fills_but() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt(0x3F70 | (N & 15) | ((N >> 4) << 14));
 }
 
 template <typename T, int ROWS, int D, int NT = kThreads>

@@ -55,6 +55,16 @@ def test_library_never_allocates_device_memory(lib):
     assert bad == []
 
 
+def test_every_kernel_launched_has_its_host_stub(lib):
+    # a kernel template whose host-side instantiation was dropped leaves its
+    # launch stub undefined; the library would then fail to load at run time
+    from exact_softmax_attention_attn_amd import binding
+    out = subprocess.run(["nm", "-D", "--undefined-only", binding.LIB_PATH],
+                         stdout=subprocess.PIPE, text=True, check=True).stdout
+    missing = [line.split()[-1] for line in out.splitlines() if "__device_stub__" in line]
+    assert missing == []
+
+
 def test_status_strings(lib):
     assert lib.attn_status_string(0) == b"ok"
     assert lib.attn_status_string(1) == b"invalid argument"
