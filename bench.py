@@ -11,7 +11,8 @@ Prints one JSON line.  `value` is attn_bwd TFLOP/s with FLOPs counted as
 the dominant kernel (dK/dV): its algorithmic FLOPs (8 * d * pairs: S, dP,
 dV, dK) over its mean duration from HIP events recorded around it on the
 launch stream, against the bf16 dense MFMA peak.  `cpu_baseline` times the
-fp64 oracle on one (batch, head) of the same workload on the host cores.
+fp64 oracle on whole (batch, head) slices of the same workload on the host
+cores (a bounded sample of about CPU_BASELINE_SECONDS).
 """
 
 from __future__ import annotations
@@ -31,8 +32,11 @@ METRIC = "causal attention bwd TFLOP/s and % of bf16 MFMA peak at N=16K, d=128"
 PEAK = {"bf16": 2516.6, "f32": 157.3}          # dense MFMA TFLOP/s, MI355X spec
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dkdv_c5_long_traffic.json")
-KERNEL_SOURCES = ("exact_softmax_attention_attn_amd/csrc/attn_bwd.hip",
+# the dominant kernel at the bench workload and the sources it is built from
+DOMINANT_KERNEL = "bwd_dkdv_bf16_kernel"
+KERNEL_SOURCES = ("exact_softmax_attention_attn_amd/csrc/attn_bwd_pipe.hip",
                   "exact_softmax_attention_attn_amd/csrc/common.h")
+CPU_BASELINE_SECONDS = 12.0    # the oracle runs whole heads until this much time has passed
 
 
 def kernel_source_hash() -> str:
@@ -59,7 +63,12 @@ def traffic_record():
 
 
 def cpu_baseline(w, x):
-    """The oracle as it stands, on one (batch, head) of the workload."""
+    """The oracle as it stands, on whole (batch, head) slices of the workload.
+
+    Heads run one after another until CPU_BASELINE_SECONDS have passed (at
+    least one), so the sample stays bounded; the rate is scaled by the FLOPs
+    of the heads actually run.
+    """
     import numpy as np
     from oracle import attn_oracle as orc
     try:
@@ -68,15 +77,63 @@ def cpu_baseline(w, x):
                        if p.get("user_api") == "blas"] or [os.cpu_count()])
     except Exception:  # pragma: no cover - threadpoolctl missing
         threads = os.cpu_count()
-    q, k, v, do = (x[n][:1, :, :1].astype(np.float64) for n in ("q", "k", "v", "do"))
-    t0 = time.perf_counter()
-    orc.attn_bwd(q, k, v, do, w.scale, w.causal)
-    dt = time.perf_counter() - t0
-    flops = 10 * w.d * pairs(1, 1, w.N, w.causal)
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+    done, spent = 0, 0.0
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    for b, h in heads:
+        q, k, v, do = (x[n][b:b + 1, :, h:h + 1].astype(np.float64) for n in ("q", "k", "v", "do"))
+        t0 = time.perf_counter()
+        orc.attn_bwd(q, k, v, do, w.scale, w.causal)
+        spent += time.perf_counter() - t0
+        done += 1
+        if spent >= CPU_BASELINE_SECONDS:
+            break
+    flops = 10 * w.d * pairs(1, 1, w.N, w.causal) * done
+    return {"value": round(flops / spent / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"one (batch, head) of {w.name} (N={w.N}, d={w.d}, causal), fp64 numpy, "
-                      f"{dt:.1f} s; scaled by its own FLOP count"}
+            "sample": f"{done} of {len(heads)} (batch, head) slices of {w.name} (N={w.N}, d={w.d}, "
+                      f"{'causal' if w.causal else 'full'}), fp64 numpy oracle attn_bwd, "
+                      f"{spent:.1f} s; TFLOP/s from 10*d*pairs of the slices run"}
+
+
+def summarize_pmc(fetch_dirs, write_dirs, calib_mib):
+    """HBM bytes per dK/dV launch from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs.
+
+    Each counter is read in KiB per dispatch.  The run's calibration kernel (a
+    dtype-cast copy of calib_mib MiB in, calib_mib MiB out, the largest
+    'copy' dispatch of the run) gives the factor from counter KiB to bytes.
+    """
+    import csv
+    import glob
+
+    def per_dispatch(dirs, counter):
+        rows = {}
+        for d in dirs:
+            for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+                for r in csv.DictReader(open(f)):
+                    if r["Counter_Name"] != counter:
+                        continue
+                    key = (f, r["Dispatch_Id"])
+                    rows[key] = (r["Kernel_Name"], float(r["Counter_Value"]))
+        return list(rows.values())
+
+    out = {}
+    for counter, dirs in (("FETCH_SIZE", fetch_dirs), ("WRITE_SIZE", write_dirs)):
+        rows = per_dispatch(dirs, counter)
+        dk = [v for n, v in rows if DOMINANT_KERNEL in n]
+        cp = [v for n, v in rows if "copy" in n.lower()]
+        if not dk or not cp:
+            raise SystemExit(f"{counter}: no {DOMINANT_KERNEL} or copy dispatch found")
+        factor = calib_mib * (1 << 20) / max(cp)          # bytes per counter unit
+        out[counter] = {"kernel_kib_mean": sum(dk) / len(dk), "dispatches": len(dk),
+                        "copy_kib": max(cp), "bytes_per_unit": factor,
+                        "bytes_per_launch": sum(dk) / len(dk) * factor}
+    rec = {"kernel": DOMINANT_KERNEL, "kernel_source_sha256": kernel_source_hash(),
+           "calibration_copy_mib": calib_mib,
+           "fetch_bytes_per_launch": round(out["FETCH_SIZE"]["bytes_per_launch"]),
+           "write_bytes_per_launch": round(out["WRITE_SIZE"]["bytes_per_launch"]),
+           "counters": out}
+    rec["bytes_per_launch"] = rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
+    return rec
 
 
 def main(argv=None):
@@ -88,12 +145,23 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain copy of this many MiB (counter calibration runs)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the dK/dV traffic record from two rocprofv3 --pmc output dirs "
+                         "(FETCH_SIZE run, WRITE_SIZE run, both with --copy-calibration-mib)")
     args = ap.parse_args(argv)
 
+    if args.summarize_pmc:
+        rec = summarize_pmc([args.summarize_pmc[0]], [args.summarize_pmc[1]],
+                            args.copy_calibration_mib or 1024)
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(rec, f, indent=1)
+        print(json.dumps(rec))
+        return 0
+
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(every (batch, head) is independent, see the sharding note in the design doc)",
-              file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: this build "
+              "runs on a single GPU (every (batch, head) is independent, so heads would shard "
+              "across GPUs with no communication, one process per GPU)", file=sys.stderr)
         return 2
 
     import numpy as np
@@ -153,11 +221,14 @@ def main(argv=None):
     peak = PEAK[w.dtype]
 
     if args.copy_calibration_mib:
+        # a cast copy runs as a kernel (a same-type copy may go to a DMA engine):
+        # it reads and writes exactly n * 4 bytes
         n = args.copy_calibration_mib * (1 << 20) // 4
         a = torch.ones(n, dtype=torch.float32, device=dev)
-        b = torch.empty_like(a)
+        b = torch.empty(n, dtype=torch.int32, device=dev)
         b.copy_(a)
         torch.cuda.synchronize()
+        del a, b
 
     esz = 2 if w.dtype == "bf16" else 4
     alg_bytes = 8 * w.B * w.N * w.H * w.d * esz + 4 * w.B * w.H * w.N
@@ -180,12 +251,12 @@ def main(argv=None):
         "pct_of_peak": round(100 * value / peak, 2),
         "stages_ms": {"preprocess": round(pre, 4), "dkdv": round(dkdv, 4), "dq": round(dqk, 4)},
         "hbm_gbs_algorithmic": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
-        "roofline": {"kernel": "bwd_dkdv_kernel", "bound": "mfma", "achieved": round(achieved, 3),
+        "roofline": {"kernel": DOMINANT_KERNEL, "bound": "mfma", "achieved": round(achieved, 3),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic_record()},
     }
     if not args.no_cpu_baseline:
-        print("[bench] cpu baseline (oracle, one head)", file=sys.stderr, flush=True)
+        print("[bench] cpu baseline (oracle, whole heads, bounded)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w, x)
     print(json.dumps(line), flush=True)
     return 0
