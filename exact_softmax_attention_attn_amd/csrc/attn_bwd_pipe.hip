@@ -275,28 +275,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// dQ (bf16).  Workgroup = NW waves = NW * 64 query rows of one (b, h); wave w
-// owns query rows qw + [0, 64) as two halves of 32.  Q (pre-multiplied by
+// dQ (bf16).  Workgroup = NW waves = 256 query rows of one (b, h); wave w owns
+// query rows qw + [0, WQ) as WQ / 32 halves of 32 rows.  Q (pre-multiplied by
 // scale log2e) and dO of the wave's rows and its dQ^T accumulators live in
-// AGPRs for the whole kernel; each LDS operand fragment feeds two matrix
-// instructions (one per half).  Per key sub-tile j of 32 rows:
+// AGPRs for the whole kernel.  With two halves each LDS operand fragment
+// feeds two matrix instructions.  Per key sub-tile of 32 rows:
 //   S'^T = K (c Q)^T - L2,  dP'^T = V dO^T - D,  P = exp2(S'),
 //   dS = P o dP',  dQ^T += K^T dS^T.
-// The query rows run along the lanes, so the row scalars enter through one
-// extra product per chain: a constant "ones" fragment times a fragment that
-// carries the lane's scalar split into two bf16 parts (hi + lo, exact to
-// about 2^-16 relative).
-//
-// The sub-tiles are software-pipelined so that the VALU work of one overlaps
-// the matrix instructions of another; iteration j runs
-//   A: S'(j) chains          | VALU: dS(j-1) = P(j-1) o dP'(j-1), packed to bf16
-//   C: dQ^T += K^T dS^T (j-1) | VALU: P(j) = exp2(S'(j))
-//   B: dP'(j) chains         | VALU: causal mask of P(j) (diagonal tiles only)
-// so no VALU step waits on the products it follows.  Phase C of iteration j
-// reads the key rows of sub-tile j - 1, which for the first sub-tile of a
-// tile lie in the previous tile
-// separately named LDS buffers, copied two tiles ahead.  Operand reads run AH
-// fragments ahead through a whole tile.  No atomics.
+// The query rows run along the lanes here, so the row scalars cannot enter as
+// a per-register C input; instead each chain starts with one extra product of
+// a constant "ones" fragment and a fragment carrying the row scalar split
+// into two bf16 parts (hi + lo, exact to about 2^-16 relative), which adds the
+// scalar to every element.  That costs one matrix instruction per chain and
+// saves an add per element on the VALU.  Operand reads run AH fragments ahead
+// through a whole 64-row key tile.  Key tiles are copied two steps ahead into
+// a ring of three separately named LDS buffers.  No atomics.
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL, int WQ, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
@@ -308,15 +301,14 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
   constexpr int NH = WQ / 32;                  // 32-row halves per wave
   constexpr int BQ = NW * WQ, BKV = 64, KS = D / 16, MT = D / 32, AH = 4;
   constexpr int NT = NW * 64;
-  constexpr int SEG = KS;                      // operands per phase (K cols, K rows, V cols)
-  static_assert(NH == 2, "64 query rows per wave");
-  static_assert(2 * MT == SEG, "the three phases read equally many operands");
+  constexpr int PER = 16 / KS;                 // elements per half handled per dP step
+  static_assert(NH == 1 || NH == 2, "32 or 64 query rows per wave");
   using KT = Tile<bf16, BKV, D>;
   struct __align__(16) Buf {
     bf16 k[KT::ELEMS];
     bf16 v[KT::ELEMS];
   };
-  __shared__ Buf bufs[3];
+  __shared__ Buf buf0, buf1, buf2;
 
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
   const int wave = wave_uniform(tid >> 6);
@@ -371,201 +363,144 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
   // first tile holding key rows above some of the block's query rows
   const int diag0 = CAUSAL ? max(0, min(ntiles, qb / BKV)) : ntiles;
 
-  // A key tile (K and V rows) into LDS by direct copies, 2 * PER instructions
-  // per wave whether or not the tile exists (see async_fill_switched).  The
-  // sequence's ragged last tile fetches row N - 1 in place of the rows past
-  // the end; those key rows are masked out of P.
+  // A key tile (K and V rows) into LDS: whole tiles by direct copies (2 * PER
+  // instructions per wave), the sequence's ragged last tile by the register
+  // path with zero padding.
   using FS = AsyncFillShape<BKV, D, NW>;
-  const int last_tile = (N - 1) / BKV;
-  unsigned copy_off[FS::PER], rag_off[FS::PER];
+  unsigned copy_off[FS::PER];
   async_fill_plan<BKV, D, NW>(copy_off, rs, wave, lane);
-  async_fill_plan_clamped<BKV, D, NW>(rag_off, rs, wave, lane, N - 1 - last_tile * BKV);
   auto fill = [&](Buf& B, int kt) ATTN_INLINE {
-    const int on = kt < ntiles;
-    const int kc = on ? kt : ntiles - 1;       // an in-range tile when switched off
-    const bool rag = kc == last_tile;
-    unsigned off[FS::PER];
-#pragma unroll
-    for (int i = 0; i < FS::PER; ++i) off[i] = rag ? rag_off[i] : copy_off[i];
-    const long k0 = (long)kc * BKV;
-    async_fill_switched<BKV, D, NW>(KT{B.k}, K + base + k0 * rs, off, wave, on);
-    async_fill_switched<BKV, D, NW>(KT{B.v}, V + base + k0 * rs, off, wave, on);
-  };
-  // Entering tile kt: its copy must have landed; tile kt + 1's (always
-  // 2 * PER instructions, issued later) may still be in flight.
-  auto enter = [&](int kt) ATTN_INLINE {
-    (void)kt;
-    wait_async_fills_but<2 * FS::PER>();
-    lds_barrier();
-  };
-
-  // pipeline state carried from one sub-tile to the next; zero before the
-  // first, so its "previous" products add exact zeros
-  f32x16 sp[NH], dpv[NH];       // P(j-1) and dP'(j-1)
-#pragma unroll
-  for (int c = 0; c < NH; ++c) { sp[c] = zero16(); dpv[c] = zero16(); }
-  frag bds[NH][2];              // dS(j-1) packed
-
-  auto opnd = [&](const Buf& B, int kind, int st, int i) ATTN_INLINE -> frag {
-    const int r0 = st * 32;
-    if (kind == 0) return plan.cols(B.k, r0, i);           // K along the head dim (S chain)
-    if (kind == 2) return plan.cols(B.v, r0, i);           // V along the head dim (dP chain)
-    return plan.rows(B.k, r0, i / MT, i % MT);             // K across positions (dQ)
-  };
-
-  // P = 0 for key rows after the query row (causal) or past the end
-  auto mask_p = [&](f32x16 (&p)[NH], int ka) ATTN_INLINE {
-#pragma unroll
-    for (int c = 0; c < NH; ++c) {
-      const int q = qw + 32 * c + l32;
-      const int lim = CAUSAL ? q : N - 1;
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (ka + acc_row(r, h) > lim) p[c][r] = 0.f;
+    const int k0 = kt * BKV;
+    if (k0 + BKV <= N) {
+      async_fill_untracked<BKV, D, NW>(KT{B.k}, K + base + k0 * rs, copy_off, wave);
+      async_fill_untracked<BKV, D, NW>(KT{B.v}, V + base + k0 * rs, copy_off, wave);
+    } else {
+      fill_sync<bf16, BKV, D, NT>(KT{B.k}, K + base, rs, k0, N, d, tid);
+      fill_sync<bf16, BKV, D, NT>(KT{B.v}, V + base, rs, k0, N, d, tid);
     }
   };
 
-  // One key tile kt in Bc: sub-tiles 2 kt (st 0) and 2 kt + 1 (st 1), with
-  // the previous sub-tile's dS and dQ products, whose key rows are in Bp.
-  // Once those are read, a barrier frees Bp for the copy of tile kt + 2.  The
-  // operand stream of the tile is
-  //   [A st0: K cols] [C prev: K rows of Bp st1] [B st0: V cols]
-  //   [A st1: K cols] [C st0: K rows]            [B st1: V cols]
-  // and the ring reads it AH operands ahead, never past the tile's end.
-  auto tile = [&](int kt, const Buf& Bc, Buf& Bp) ATTN_INLINE {
-    constexpr int TOTAL = 6 * SEG;
-    const bool masked = (CAUSAL && kt >= diag0) || (kt + 1) * BKV > N;
-    auto stream = [&](int n) ATTN_INLINE -> frag {
-      const int sg = n / SEG, i = n % SEG;
-      switch (sg) {
-        case 0: return opnd(Bc, 0, 0, i);
-        case 1: return opnd(Bp, 1, 1, i);
-        case 2: return opnd(Bc, 2, 0, i);
-        case 3: return opnd(Bc, 0, 1, i);
-        case 4: return opnd(Bc, 1, 0, i);
-        default: return opnd(Bc, 2, 1, i);
-      }
+  // One key tile (two sub-tiles of 32 rows).  The operand stream of a
+  // sub-tile is K (head dim), V (head dim), K^T (positions); reads run AH
+  // operands ahead through the whole tile.
+  constexpr int OPS = 2 * KS + 2 * MT;          // operands per sub-tile
+  auto tile_body = [&](int kt, const Buf& B, bool masked) ATTN_INLINE {
+    auto opnd = [&](int n) ATTN_INLINE -> frag {
+      const int r0 = (n / OPS) * 32, m = n % OPS;
+      if (m < KS) return plan.cols(B.k, r0, m);
+      if (m < 2 * KS) return plan.cols(B.v, r0, m - KS);
+      const int i = m - 2 * KS;                   // (ss, mt) = (i / MT, i % MT)
+      return plan.rows(B.k, r0, i / MT, i % MT);
     };
     frag ring[AH];
 #pragma unroll
-    for (int n = 0; n < AH; ++n) ring[n] = stream(n);
+    for (int n = 0; n < AH; ++n) ring[n] = opnd(n);
     fence();
-    auto take = [&](int n) ATTN_INLINE -> frag {    // operand n of the stream
-      const frag a = ring[n % AH];
-      if (n + AH < TOTAL) ring[n % AH] = stream(n + AH);
-      return a;
-    };
-
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
-      const int ka = kt * BKV + st * 32;
+      const int ka = kt * BKV + st * 32;          // absolute first key row of the sub-tile
+      const int n0 = st * OPS;
       f32x16 sc[NH], pc[NH];
-      // ---- A: S'(j) chains | dS(j-1) and its bf16 packing -----------------
+      // S'^T = ones bl^T + K (c Q)^T
 #pragma unroll
       for (int c = 0; c < NH; ++c) sc[c] = M::mma(ones, bl[c], zero16());
-      fence();
-      constexpr int MPK = 16 * NH / KS;         // dS elements per K step
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
-        const frag a = take(3 * st * SEG + kk);
+        const int n = n0 + kk;
+        const frag a = ring[n % AH];
+        if (n + AH < 2 * OPS) ring[n % AH] = opnd(n + AH);
 #pragma unroll
         for (int c = 0; c < NH; ++c) sc[c] = M::mma(a, qf[c][kk], sc[c]);
+        fence();
+      }
+      // dP'^T = ones bd^T + V dO^T | P = exp2(S') on the VALU
 #pragma unroll
-        for (int e = 0; e < MPK; ++e) {
-          const int x = kk * MPK + e, c = x / 16, r = x % 16;
-          dpv[c][r] = sp[c][r] * dpv[c][r];
-        }
-        // pack an 8-element half as soon as all of it is ready
+      for (int c = 0; c < NH; ++c) pc[c] = M::mma(ones, bd[c], zero16());
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        const int n = n0 + KS + kk;
+        const frag a = ring[n % AH];
+        if (n + AH < 2 * OPS) ring[n % AH] = opnd(n + AH);
+#pragma unroll
+        for (int c = 0; c < NH; ++c) pc[c] = M::mma(a, of[c][kk], pc[c]);
 #pragma unroll
         for (int c = 0; c < NH; ++c)
 #pragma unroll
-          for (int hf = 0; hf < 2; ++hf)
-            if ((kk + 1) * MPK >= c * 16 + hf * 8 + 8 && kk * MPK < c * 16 + hf * 8 + 8)
-              bds[c][hf] = M::pack(dpv[c], hf);
+          for (int e = 0; e < PER; ++e) {
+            const int r = kk * PER + e;
+            sc[c][r] = fast_exp2(sc[c][r]);
+          }
         fence();
       }
-      // ---- C: dQ(j-1) | P(j) = exp2(S'(j)) -----------------------------------
-      constexpr int EPC = 16 * NH / (2 * MT);   // exps per dQ step
+      // causal element mask, only on tiles that cross the diagonal
+      if (CAUSAL && masked) {
+#pragma unroll
+        for (int c = 0; c < NH; ++c) {
+          const int q = qw + 32 * c + l32;
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (ka + acc_row(r, h) > q) sc[c][r] = 0.f;
+        }
+      }
+      fence();
+      // dS = P o dP': half 0 now, half 1 (if any) under half 0's dQ products
+      frag bds[NH][2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) pc[0][r] = sc[0][r] * pc[0][r];
+      bds[0][0] = M::pack(pc[0], 0);
+      bds[0][1] = M::pack(pc[0], 1);
+      fence();
+      frag t[2 * MT];
+      constexpr int PER3 = 16 / (2 * MT);
 #pragma unroll
       for (int i = 0; i < 2 * MT; ++i) {
-        const frag a = take((3 * st + 1) * SEG + i);
+        const int n = n0 + 2 * KS + i;
+        t[i] = ring[n % AH];
+        if (n + AH < 2 * OPS) ring[n % AH] = opnd(n + AH);
+        mma_acc_agpr(acc[0][i % MT], t[i], bds[0][i / MT]);
+        if constexpr (NH == 2) {
 #pragma unroll
-        for (int c = 0; c < NH; ++c) mma_acc_agpr(acc[c][i % MT], a, bds[c][i / MT]);
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) {
-          const int x = i * EPC + e, c = x / 16, r = x % 16;
-          sc[c][r] = fast_exp2(sc[c][r]);
+          for (int e = 0; e < PER3; ++e) {
+            const int r = i * PER3 + e;
+            pc[NH - 1][r] = sc[NH - 1][r] * pc[NH - 1][r];
+          }
         }
         fence();
       }
-      if (st == 0) {
-        // Bp's key rows are consumed: once every wave is past them, the copy
-        // of tile kt + 2 may overwrite it
-        lds_barrier();
-        fill(Bp, kt + 2);
+      if constexpr (NH == 2) {
+        bds[1][0] = M::pack(pc[1], 0);
+        bds[1][1] = M::pack(pc[1], 1);
+        fence();
+#pragma unroll
+        for (int i = 0; i < 2 * MT; ++i) mma_acc_agpr(acc[1][i % MT], t[i], bds[1][i / MT]);
         fence();
       }
-      // ---- B: dP'(j) chains | causal mask ------------------------------------
-#pragma unroll
-      for (int c = 0; c < NH; ++c) pc[c] = M::mma(ones, bd[c], zero16());
-      fence();
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
-        const frag a = take((3 * st + 2) * SEG + kk);
-#pragma unroll
-        for (int c = 0; c < NH; ++c) pc[c] = M::mma(a, of[c][kk], pc[c]);
-        fence();
-      }
-      if (masked) mask_p(sc, ka);
-      fence();
-#pragma unroll
-      for (int c = 0; c < NH; ++c) { sp[c] = sc[c]; dpv[c] = pc[c]; }
     }
   };
 
-  // The last sub-tile's dS and dQ products, reading its key rows from Bc.
-  auto finish = [&](const Buf& Bc) ATTN_INLINE {
-    frag ring[AH];
-#pragma unroll
-    for (int i = 0; i < AH; ++i) ring[i] = opnd(Bc, 1, 1, i);
-#pragma unroll
-    for (int c = 0; c < NH; ++c) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) dpv[c][r] = sp[c][r] * dpv[c][r];
-      bds[c][0] = M::pack(dpv[c], 0);
-      bds[c][1] = M::pack(dpv[c], 1);
-    }
-    fence();
-#pragma unroll
-    for (int i = 0; i < 2 * MT; ++i) {
-      const frag a = ring[i % AH];
-      if (i + AH < 2 * MT) ring[i % AH] = opnd(Bc, 1, 1, i + AH);
-#pragma unroll
-      for (int c = 0; c < NH; ++c) mma_acc_agpr(acc[c][i % MT], a, bds[c][i / MT]);
-      fence();
-    }
-    mma_acc_drain();                           // the exits join below
+  // Key tiles are copied two steps ahead into a ring of three separately
+  // named buffers, picked statically (the loop is unrolled by three): step kt
+  // waits only for tile kt's copy and leaves tile kt + 1's in flight.  Tiles
+  // from diag0 on apply the causal element mask.
+  // tile kt + 1's copy may still fly, unless it went by the register path
+  // (the ragged last tile), which leaves nothing to count against
+  auto step = [&](int kt, const Buf& cur, Buf& ahead) ATTN_INLINE {
+    if (kt + 1 < ntiles && (kt + 2) * BKV <= N) wait_async_fills_but<2 * FS::PER>();
+    else wait_async_fills();
+    lds_barrier();
+    if (kt + 2 < ntiles) fill(ahead, kt + 2);
+    tile_body(kt, cur, CAUSAL && kt >= diag0);
   };
-
-  // Tile kt lives in buffer kt % 3.  The copies are untracked by the
-  // compiler, so indexing the buffers at run time costs no extra waits.
-  // Before the first tile, buffer 2 stands in for the previous tile: its key
-  // rows are zeroed so the zero "previous" dS meets finite values.
-  {
-    const uint4 z = {0u, 0u, 0u, 0u};
-    for (int i = tid; i < (int)(sizeof(bufs[2].k) / 16); i += NT)
-      reinterpret_cast<uint4*>(bufs[2].k)[i] = z;
+  fill(buf0, 0);
+  if (ntiles > 1) fill(buf1, 1);
+  int kt = 0;
+  for (; kt + 3 <= ntiles; kt += 3) {
+    step(kt, buf0, buf2);
+    step(kt + 1, buf1, buf0);
+    step(kt + 2, buf2, buf1);
   }
-  fill(bufs[0], 0);
-  fill(bufs[1], 1);
-  int cur = 0, prv = 2;
-  for (int kt = 0; kt < ntiles; ++kt) {
-    enter(kt);
-    tile(kt, bufs[cur], bufs[prv]);
-    prv = cur;
-    cur = cur == 2 ? 0 : cur + 1;
-  }
-  finish(bufs[prv]);
+  if (kt < ntiles) step(kt, buf0, buf2);
+  if (kt + 1 < ntiles) step(kt + 1, buf1, buf0);
 
   mma_acc_drain();
 #pragma unroll
