@@ -220,6 +220,19 @@ def main(argv=None):
     achieved = dkdv_flops / (dkdv * 1e-3) / 1e12
     peak = PEAK[w.dtype]
 
+    # the forward (the step that supplies O and L), timed on its own after the
+    # backward's timed region: 4 d FLOPs per kept pair (S and P V)
+    fev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    binding.attn_fwd_lse(q, k, v, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    fwd_runs = 5
+    fev[0].record()
+    for _ in range(fwd_runs):
+        binding.attn_fwd_lse(q, k, v, causal=w.causal, scale=w.scale)
+    fev[1].record()
+    torch.cuda.synchronize()
+    fwd_ms = fev[0].elapsed_time(fev[1]) / fwd_runs
+
     if args.copy_calibration_mib:
         # a cast copy runs as a kernel (a same-type copy may go to a DMA engine):
         # it reads and writes exactly n * 4 bytes
@@ -251,6 +264,8 @@ def main(argv=None):
         "pct_of_peak": round(100 * value / peak, 2),
         "stages_ms": {"preprocess": round(pre, 4), "dkdv": round(dkdv, 4), "dq": round(dqk, 4)},
         "hbm_gbs_algorithmic": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
+        "fwd_lse": {"ms": round(fwd_ms, 4),
+                    "tflops": round(4 * w.d * P / (fwd_ms * 1e-3) / 1e12, 3)},
         "roofline": {"kernel": DOMINANT_KERNEL, "bound": "mfma", "achieved": round(achieved, 3),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic_record()},

@@ -95,7 +95,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   __shared__ Buf bufA, bufB;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
-  const int jb = blockIdx.x, head = blockIdx.y, b = blockIdx.z;
+  const BlockOrder bo = block_order();
+  const int jb = bo.rank, head = bo.head, b = bo.b;   // rank 0 = longest walk
   const long rs = (long)H * d;                       // elements between positions
   const long base = ((long)b * N * H + head) * d;    // (b, 0, head, 0)
   const float* Lh = L2 + ((long)b * H + head) * N;
@@ -244,8 +245,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
   const int nqb = gridDim.x;
-  const int ib = CAUSAL ? (nqb - 1 - (int)blockIdx.x) : (int)blockIdx.x;  // longest first
-  const int head = blockIdx.y, b = blockIdx.z;
+  const BlockOrder bo = block_order();
+  const int ib = CAUSAL ? (nqb - 1 - bo.rank) : bo.rank;   // longest first
+  const int head = bo.head, b = bo.b;
   const long rs = (long)H * d;
   const long base = ((long)b * N * H + head) * d;
   const float* Lh = L2 + ((long)b * H + head) * N;

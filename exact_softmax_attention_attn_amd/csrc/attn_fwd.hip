@@ -36,8 +36,9 @@ __global__ __launch_bounds__(256, 1) void fwd_lse_kernel(const T* __restrict__ Q
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
   const int nqb = gridDim.x;
-  const int ib = CAUSAL ? (nqb - 1 - (int)blockIdx.x) : (int)blockIdx.x;  // longest first
-  const int head = blockIdx.y, b = blockIdx.z;
+  const BlockOrder bo = block_order();
+  const int ib = CAUSAL ? (nqb - 1 - bo.rank) : bo.rank;   // longest first
+  const int head = bo.head, b = bo.b;
   const long rs = (long)H * d;
   const long base = ((long)b * N * H + head) * d;
 
@@ -79,33 +80,40 @@ __global__ __launch_bounds__(256, 1) void fwd_lse_kernel(const T* __restrict__ Q
       f32x16 s = zero16();
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) s = M::mma(kt_.along_cols(st * 32 + l32, kk, h), qf[kk], s);
-      // register r = key row ka + acc_row(r, h), column = query row q
+      // register r = key row ka + acc_row(r, h), column = query row q.  The
+      // row max is taken on the raw scores (scale > 0 keeps the order).
       float mx = -__builtin_inff();
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float x = s[r] * scale_log2;
         if (MASKED) {
           const int kv = ka + acc_row(r, h);
-          if ((CAUSAL && kv > q) || kv >= N) x = -__builtin_inff();
+          if ((CAUSAL && kv > q) || kv >= N) s[r] = -__builtin_inff();
         }
-        s[r] = x;
-        mx = fmaxf(mx, x);
+        mx = fmaxf(mx, s[r]);
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m, mx);
-      const float alpha = fast_exp2(m - m_new);
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
+      // Lazy rescaling: the running max m moves only when a row's new max
+      // exceeds it by more than 8 (log2 units), so P = exp2(s c - m) stays
+      // below 2^8 and the accumulators are rescaled only when some row of
+      // the wave moved (rarely, once the max has settled).
+      const bool upd = mx > m + 8.f;
+      if (__builtin_amdgcn_ballot_w64(upd)) {
+        const float m_new = upd ? mx : m;
+        const float alpha = fast_exp2(m - m_new);
+        l *= alpha;
+        m = m_new;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;
+      }
       float sum = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(s[r] - m_new);
+        const float p = fast_exp2(__builtin_fmaf(s[r], scale_log2, -m));
         s[r] = p;
         sum += p;
       }
       sum += __shfl_xor(sum, 32);
-      l = l * alpha + sum;
-      m = m_new;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;
+      l += sum;
 #pragma unroll
       for (int ss = 0; ss < RS; ++ss) {
         const frag bp = M::pack(s, ss);

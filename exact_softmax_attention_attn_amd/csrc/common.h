@@ -64,6 +64,23 @@ __device__ __forceinline__ void mma_acc_agpr(f32x16& acc, const bf16x8& a, const
 // addresses built from it stay scalar).
 __device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// Block order.  The grid is (blocks per head, H, B); workgroups are
+// dispatched in linear order and handed to the XCDs round-robin.  Numbering
+// the linear index "rank-major" (all (b, h) of rank 0 first, then rank 1, ...)
+// and giving rank 0 the longest block makes the dispatch longest-first across
+// all heads, so no long block starts late, and it sends every block of a
+// given (b, h) to the same XCD (when B*H is a multiple of the XCD count), so
+// the tiles the blocks of a head share stay in that XCD's L2.
+struct BlockOrder {
+  int rank, head, b;
+};
+__device__ __forceinline__ BlockOrder block_order() {
+  const int nbh = gridDim.y * gridDim.z;
+  const int lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  const int bh = lin % nbh;
+  return {lin / nbh, bh % (int)gridDim.y, bh / (int)gridDim.y};
+}
+
 // Before the VALU reads AGPR accumulators written by mma_acc_agpr: the last
 // 32x32 matrix instruction must have written its results back (it takes 8
 // passes of 4 cycles plus write-back latency).
