@@ -351,70 +351,6 @@ __device__ __forceinline__ void fill_row64_untracked(float* lds, const float* g,
   lds_dma_b32(g, (unsigned)lane * 4u, lds_address(lds));
 }
 
-// The plan for a tile whose rows may run past the end of the matrix: rows
-// beyond last_row (tile-relative) fetch row last_row instead, so every copy
-// stays in bounds; the kernel masks the duplicated rows out of the result.
-template <int ROWS, int D, int NWAVES = 4>
-__device__ __forceinline__ void async_fill_plan_clamped(unsigned* off, long rs, int wave, int lane,
-                                                        int last_row) {
-  using S = AsyncFillShape<ROWS, D, NWAVES>;
-#pragma unroll
-  for (int i = 0; i < S::PER; ++i) {
-    const int r = (wave * S::PER + i) * S::RPI + lane / S::CPR;
-    const int chunk = (lane % S::CPR) ^ Tile<bf16, ROWS, D>::swz(r);
-    off[i] = (unsigned)(((long)min(r, last_row) * rs + chunk * 8) * (long)sizeof(bf16));
-  }
-}
-
-// A whole tile copy by the plan, as one assembly block with a run-time
-// switch: with on == 0 the copy instructions still issue (every fill then
-// counts the same against vmcnt) but with no lane active, so nothing is read
-// or written.  Being one block, it needs no branch around it, and the
-// compiler keeps the instruction order of the code around it intact.
-template <int ROWS, int D, int NWAVES = 4>
-__device__ __forceinline__ void async_fill_switched(const Tile<bf16, ROWS, D>& t,
-                                                    const bf16* tile_base, const unsigned* off,
-                                                    int wave, int on) {
-  using S = AsyncFillShape<ROWS, D, NWAVES>;
-  static_assert(S::PER == 2 || S::PER == 4, "two or four copy instructions per wave");
-  // the operands below must sit in scalar registers: make their uniformity
-  // explicit to the compiler
-  const unsigned lds = (unsigned)wave_uniform((int)lds_address(t.p + wave * S::PER * 512));
-  on = wave_uniform(on);
-  const unsigned long long bp = reinterpret_cast<unsigned long long>(tile_base);
-  const unsigned long long bu =
-      ((unsigned long long)(unsigned)wave_uniform((int)(bp >> 32)) << 32) |
-      (unsigned)wave_uniform((int)(unsigned)bp);
-  tile_base = reinterpret_cast<const bf16*>(bu);
-  unsigned long long saved_exec;
-  unsigned saved_m0;
-  if constexpr (S::PER == 4) {
-    asm volatile(
-        "s_mov_b64 %[sx], exec\n\ts_mov_b32 %[sm], m0\n\t"
-        "s_cmp_eq_u32 %[on], 0\n\ts_cselect_b64 exec, 0, exec\n\t"
-        "s_mov_b32 m0, %[lds]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[o0], %[base]\n\t"
-        "s_add_u32 m0, %[lds], 1024\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[o1], %[base]\n\t"
-        "s_add_u32 m0, %[lds], 2048\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[o2], %[base]\n\t"
-        "s_add_u32 m0, %[lds], 3072\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[o3], %[base]\n\t"
-        "s_nop 0\n\ts_mov_b32 m0, %[sm]\n\ts_mov_b64 exec, %[sx]"
-        : [sx] "=&s"(saved_exec), [sm] "=&s"(saved_m0)
-        : [on] "s"(on), [lds] "s"(lds), [base] "s"(tile_base), [o0] "v"(off[0]),
-          [o1] "v"(off[1]), [o2] "v"(off[2]), [o3] "v"(off[3])
-        : "memory", "scc");
-  } else {
-    asm volatile(
-        "s_mov_b64 %[sx], exec\n\ts_mov_b32 %[sm], m0\n\t"
-        "s_cmp_eq_u32 %[on], 0\n\ts_cselect_b64 exec, 0, exec\n\t"
-        "s_mov_b32 m0, %[lds]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[o0], %[base]\n\t"
-        "s_add_u32 m0, %[lds], 1024\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[o1], %[base]\n\t"
-        "s_nop 0\n\ts_mov_b32 m0, %[sm]\n\ts_mov_b64 exec, %[sx]"
-        : [sx] "=&s"(saved_exec), [sm] "=&s"(saved_m0)
-        : [on] "s"(on), [lds] "s"(lds), [base] "s"(tile_base), [o0] "v"(off[0]),
-          [o1] "v"(off[1])
-        : "memory", "scc");
-  }
-}
-
 // One-off form for kernels that do not keep a plan.
 template <int ROWS, int D, int NWAVES = 4>
 __device__ __forceinline__ void fill_async(const Tile<bf16, ROWS, D>& t, const bf16* g, long rs,
