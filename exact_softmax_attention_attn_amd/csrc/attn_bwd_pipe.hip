@@ -239,16 +239,27 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     if (k + 2 < ntiles) fill_whole(ahead, tile_of(k + 2));
     tile_body(tile_of(k), cur, CAUSAL && k + 2 >= ntiles);
   };
+  // Steps at least two ahead of the last are unmasked and have two tiles
+  // after them: the main loop takes three of them at a time without a
+  // branch, which keeps each tile body one straight block.
+  auto step_inner = [&](int k, const Buf& cur, Buf& ahead) ATTN_INLINE {
+    wait_async_fills_but<2 * FS::PER>();
+    lds_barrier();
+    fill_whole(ahead, tile_of(k + 2));
+    tile_body(tile_of(k), cur, false);
+  };
   fill(buf0, tile_of(0));
   if (ntiles > 1) fill_whole(buf1, tile_of(1));
   int k = 0;
-  for (; k + 3 <= ntiles; k += 3) {
-    step(k, buf0, buf2);
-    step(k + 1, buf1, buf0);
-    step(k + 2, buf2, buf1);
+  for (; k + 5 <= ntiles; k += 3) {
+    step_inner(k, buf0, buf2);
+    step_inner(k + 1, buf1, buf0);
+    step_inner(k + 2, buf2, buf1);
   }
   if (k < ntiles) step(k, buf0, buf2);
   if (k + 1 < ntiles) step(k + 1, buf1, buf0);
+  if (k + 2 < ntiles) step(k + 2, buf2, buf1);
+  if (k + 3 < ntiles) step(k + 3, buf0, buf2);
 
   mma_acc_drain();
 #pragma unroll
@@ -475,9 +486,26 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
     if (kt + 2 < ntiles) fill(ahead, kt + 2);
     tile_body(kt, cur, CAUSAL && kt >= diag0);
   };
+  // Steps below the diagonal whose tile two ahead is whole need none of the
+  // checks above: the first loop takes three of them at a time without a
+  // branch, which keeps each tile body one straight block.
+  auto step_inner = [&](int kt, const Buf& cur, Buf& ahead) ATTN_INLINE {
+    wait_async_fills_but<2 * FS::PER>();
+    lds_barrier();
+    const int k0 = (kt + 2) * BKV;
+    async_fill_untracked<BKV, D, NW>(KT{ahead.k}, K + base + k0 * rs, copy_off, wave);
+    async_fill_untracked<BKV, D, NW>(KT{ahead.v}, V + base + k0 * rs, copy_off, wave);
+    tile_body(kt, cur, false);
+  };
   fill(buf0, 0);
   if (ntiles > 1) fill(buf1, 1);
   int kt = 0;
+  const int inner_end = min(diag0, min(ntiles - 2, N / BKV - 2));   // steps kt < inner_end
+  for (; kt + 3 <= inner_end; kt += 3) {
+    step_inner(kt, buf0, buf2);
+    step_inner(kt + 1, buf1, buf0);
+    step_inner(kt + 2, buf2, buf1);
+  }
   for (; kt + 3 <= ntiles; kt += 3) {
     step(kt, buf0, buf2);
     step(kt + 1, buf1, buf0);

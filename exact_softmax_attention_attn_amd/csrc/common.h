@@ -128,11 +128,13 @@ template <> struct Mma<float> {
 // A ROWS x D tile of a [pos, row_stride] global matrix staged in LDS.
 //
 // bf16: row-major, 16-byte chunks permuted within each row: logical chunk c
-// of row r sits at chunk c ^ swz(r).
-//   - along_cols (ds_read_b128, 32 lanes on 32 rows, one chunk): any 16
-//     consecutive rows hit 16 distinct chunk slots, i.e. all 64 banks once.
-//   - along_rows (ds_read_b64_tr_b16): a 16-lane group reads 4 consecutive
-//     rows x 2 neighbouring chunks; the 8 slots are distinct.
+// of row r sits at chunk c ^ swz(r).  A read is served 256 bytes (all 64
+// banks) at a time; the permutation keeps every such group on distinct slots:
+//   - along_cols (ds_read_b128, one chunk per lane): any 16 consecutive rows
+//     of one chunk, and any 8 aligned rows of two neighbouring chunks.
+//   - along_rows (ds_read_b64_tr_b16, 8 bytes per lane): 32 consecutive lanes
+//     read 4 aligned rows x 4 neighbouring chunks, lanes {0-15, 32-47} read 8
+//     aligned rows x 2 chunks; both land on 16 distinct slots.
 // f32: row-major with 4 floats of padding per row (a 1-float fragment reads
 //   any layout in one access).
 //
@@ -151,15 +153,16 @@ template <int ROWS, int D> struct Tile<bf16, ROWS, D> {
   static_assert(CPR >= 4 && (CPR & (CPR - 1)) == 0, "head-dim bucket must be 32, 64 or 128");
   bf16* p;
 
-  // Bank slot of (row, physical chunk) = (row % (16 / CPR)) * CPR + chunk; the
-  // permutation keeps 16 consecutive rows on 16 distinct slots for one logical
-  // chunk, and 4 consecutive rows x 2 neighbouring chunks on 8 distinct slots.
-  __device__ __forceinline__ static int swz(int r) {
-    if constexpr (CPR == 16) return ((r & 3) << 1) | ((r >> 2) & 1) | (r & 8);
-    else if constexpr (CPR == 8) return (r & 2) | ((r >> 2) & 1) | ((r >> 1) & 4);
-    else return (r >> 2) & 3;
+  // Bank slot of (row, physical chunk) = (row % (16 / CPR)) * CPR + chunk.
+  // With row bits r3 r2 r1 r0: CPR 16 permutes by (r1 r0 r2 r3), CPR 8 by
+  // (r1 r2 r3), CPR 4 by (r2 r3); rows sharing a slot line (same r % (16/CPR))
+  // then differ in the chunk bits that each read group above spans.
+  __host__ __device__ __forceinline__ static int swz(int r) {
+    if constexpr (CPR == 16) return ((r & 2) << 2) | ((r & 1) << 2) | ((r >> 1) & 2) | ((r >> 3) & 1);
+    else if constexpr (CPR == 8) return ((r & 2) << 1) | ((r >> 1) & 2) | ((r >> 3) & 1);
+    else return ((r >> 1) & 2) | ((r >> 3) & 1);
   }
-  __device__ __forceinline__ int off(int r, int chunk) const {
+  __host__ __device__ __forceinline__ static int off(int r, int chunk) {
     return r * D + ((chunk ^ swz(r)) << 3);
   }
   __device__ __forceinline__ bf16x8 along_cols(int r, int ks, int h) const {
@@ -197,7 +200,7 @@ template <int D> struct LanePlan {
   static constexpr int CPR = D / 8;
   int col[D / 16];
   int tr[D / 32][2];
-  __device__ __forceinline__ explicit LanePlan(int lane) {
+  __host__ __device__ __forceinline__ explicit LanePlan(int lane) {
     using TT = Tile<bf16, 32, D>;
     const int h = lane >> 5, l32 = lane & 31, j = lane & 15;
 #pragma unroll
@@ -276,7 +279,8 @@ template <int ROWS, int D, int NWAVES = 4> struct AsyncFillShape {
 };
 
 template <int ROWS, int D, int NWAVES = 4>
-__device__ __forceinline__ void async_fill_plan(unsigned* off, long rs, int wave, int lane) {
+__host__ __device__ __forceinline__ void async_fill_plan(unsigned* off, long rs, int wave,
+                                                         int lane) {
   using S = AsyncFillShape<ROWS, D, NWAVES>;
 #pragma unroll
   for (int i = 0; i < S::PER; ++i) {

@@ -32,35 +32,90 @@ def _agprs(tok):
     return {int(m.group(1))} if m else set()
 
 
+def _blocks(lines):
+    """Split a kernel body into basic blocks: (label, [(line index, text, in inline asm)])."""
+    blocks, cur, inasm = [], ["<entry>", []], False
+    for i, line in enumerate(lines):
+        if ";;#ASMSTART" in line:
+            inasm = True
+            continue
+        if ";;#ASMEND" in line:
+            inasm = False
+            continue
+        t = line.split(";")[0].strip()
+        if t.endswith(":") and not t.startswith("."):
+            continue
+        if re.match(r"^\.LBB\w+:$", t):
+            blocks.append(cur)
+            cur = [t[:-1], []]
+            continue
+        if not t or t.startswith("."):
+            continue
+        cur[1].append((i, t, inasm))
+        if not inasm and re.match(r"s_(c?branch|endpgm|setpc)", t):
+            blocks.append(cur)               # a branch ends the block
+            cur = [None, []]
+    blocks.append(cur)
+    return [b for b in blocks if b[0] is not None or b[1]]
+
+
+def _successors(blocks, k):
+    label, ins = blocks[k]
+    last = ins[-1][1] if ins else ""
+    out = []
+    m = re.match(r"s_c?branch\S*\s+(\.LBB\w+)", last)
+    if m:
+        out.append(m.group(1))
+    unconditional = re.match(r"s_(branch|endpgm|setpc)", last)
+    if not unconditional and k + 1 < len(blocks):
+        out.append(k + 1)
+    return out
+
+
+def _transfer(ins, flight, bad=None):
+    flight = set(flight)
+    for i, t, inasm in ins:
+        if inasm:
+            if t.startswith("v_mfma"):
+                flight |= _agprs(t.split()[1].rstrip(","))
+            elif t.startswith("s_nop 15"):
+                flight = set()
+            continue
+        used = set()
+        for tok in t.split()[1:]:
+            used |= _agprs(tok.rstrip(","))
+        if used & flight and bad is not None:
+            bad.append((i, t))
+    return flight
+
+
 def hazards(asm: str):
-    """Per kernel: (line, instruction) pairs touching in-flight inline-product registers."""
+    """Per kernel: (line, instruction) pairs touching in-flight inline-product registers.
+
+    The in-flight set of each basic block's entry is the union over its
+    predecessors (branch targets and fall-through), iterated to a fixed point.
+    """
     out = {}
     for name in re.findall(r"^(_Z\S+):", asm, re.M):
         st = asm.index(name + ":")
         en = asm.index(".Lfunc_end", st)
-        inasm, flight, bad = False, set(), []
-        for i, line in enumerate(asm[st:en].splitlines()):
-            if ";;#ASMSTART" in line:
-                inasm = True
-                continue
-            if ";;#ASMEND" in line:
-                inasm = False
-                continue
-            t = line.split(";")[0].strip()
-            if not t or t.startswith(".") or t.endswith(":"):
-                continue
-            if inasm:
-                if t.startswith("v_mfma"):
-                    flight |= _agprs(t.split()[1].rstrip(","))
-                elif t.startswith("s_nop 15"):
-                    flight = set()
-                continue
-            used = set()
-            for tok in t.split()[1:]:
-                used |= _agprs(tok.rstrip(","))
-            if used & flight:
-                bad.append((i, t))
-        out[name] = bad
+        blocks = _blocks(asm[st:en].splitlines())
+        index = {b[0]: k for k, b in enumerate(blocks) if b[0] is not None}
+        entry = [set() for _ in blocks]
+        work = list(range(len(blocks)))
+        while work:
+            k = work.pop(0)
+            fl = _transfer(blocks[k][1], entry[k])
+            for s in _successors(blocks, k):
+                j = index[s] if isinstance(s, str) else s
+                if not fl <= entry[j]:
+                    entry[j] |= fl
+                    if j not in work:
+                        work.append(j)
+        bad = []
+        for k, b in enumerate(blocks):
+            _transfer(b[1], entry[k], bad)
+        out[name] = sorted(bad)
     return out
 
 
@@ -71,6 +126,22 @@ def test_checker_flags_a_copy_after_an_inline_product():
     assert hazards(asm)["_Zk"] == [(5, "v_accvgpr_mov_b32 a16, a3")]
     drained = asm.replace("v_accvgpr_mov", ";;#ASMSTART\ns_nop 15\n;;#ASMEND\nv_accvgpr_mov")
     assert hazards(drained)["_Zk"] == []
+
+
+def test_checker_follows_branches_not_text_order():
+    product = [";;#ASMSTART", "s_nop 2", "v_mfma_f32_32x32x16_bf16 a[0:15], v[0:3], v[4:7], a[0:15]",
+               ";;#ASMEND"]
+    drain = [";;#ASMSTART", "s_nop 15", ";;#ASMEND"]
+    # a product at the end of a loop laid out last, branching back: the block
+    # after it in the text is not reached from it
+    tail = "\n".join(["_Zt:", "s_branch .LBB0_2", ".LBB0_1:", *drain, "v_accvgpr_read_b32 v0, a3",
+                      "s_endpgm", ".LBB0_2:", *product, "s_cbranch_scc0 .LBB0_2", "s_branch .LBB0_1",
+                      ".LBB0_3:", "v_accvgpr_read_b32 v1, a4", "s_endpgm", ".Lfunc_end0:"])
+    assert hazards(tail)["_Zt"] == []
+    # a product before a forward branch reaches the target block undrained
+    fwd = "\n".join(["_Zf:", *product, "s_cbranch_scc0 .LBB0_1", *drain, "s_endpgm", ".LBB0_1:",
+                     "v_accvgpr_read_b32 v1, a4", "s_endpgm", ".Lfunc_end0:"])
+    assert [t for _, t in hazards(fwd)["_Zf"]] == ["v_accvgpr_read_b32 v1, a4"]
 
 
 @pytest.mark.skipif(shutil.which(build_lib.HIPCC) is None and not os.path.exists(build_lib.HIPCC),
