@@ -65,7 +65,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     float l[BQ];      // -L * log2(e)
     float dd[BQ];     // -D
   };
-  __shared__ Buf buf0, buf1, buf2;
+  __shared__ Buf buf0, buf1, buf2, buf3;
 
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
   const int wave = wave_uniform(tid >> 6);
@@ -131,93 +131,160 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     }
   };
 
-  auto tile_body = [&](int t, const Buf& B, bool masked) ATTN_INLINE {
-    // operand n of the tile: sub-tile n / OPS; within it Q cols, dO cols,
-    // dO rows (dV), Q rows (dK)
+  // One step = one query tile t, sub-tiles a (rows 0..31) and b (32..63),
+  // plus the dV / dK products of the previous tile's sub-tile b ("p"), whose
+  // P and dS arrive packed in bpp / bdsp.  Chains of L = D / 16 products:
+  //   S_a | dV_p | dP_a | dK_p | S_b | dV_a | dP_b | dK_a
+  // Each VALU stage reads a chain that finished one chain earlier: the exps
+  // of S_a run beside dV_p and dP_a, dS_a beside dK_p, the exps of S_b beside
+  // dV_a and dP_b, dS_b beside dK_a.  P_b and dS_b leave packed for the next
+  // step.  Operand reads run AH fragments ahead through the step.
+  constexpr int L = KS;                       // = 2 * MT
+  static_assert(L == 2 * MT, "chain length");
+  auto row_scalars = [&](const float* src, int r0) ATTN_INLINE {
+    f32x16 v;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 x = lds_f32x4(&src[r0 + 8 * g + 4 * h]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[4 * g + i] = x[i];
+    }
+    return v;
+  };
+  auto mask_rows = [&](f32x16& p, int qa) ATTN_INLINE {
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (kv > qa + acc_row(r, h)) p[r] = 0.f;
+  };
+  auto step_body = [&](auto has_prev, int t, const Buf& B, const Buf& Pv, bool masked,
+                       frag (&bpp)[2], frag (&bdsp)[2]) ATTN_INLINE {
+    constexpr bool HP = decltype(has_prev)::value;
+    constexpr int C_SA = 0, C_DVP = 1, C_DPA = HP ? 2 : 1, C_DKP = 3, C_SB = HP ? 4 : 2,
+                  C_DVA = HP ? 5 : 3, C_DPB = HP ? 6 : 4, C_DKA = HP ? 7 : 5;
+    constexpr int NOPS = (HP ? 8 : 6) * L;
     auto opnd = [&](int n) ATTN_INLINE -> frag {
-      const int r0 = (n / OPS) * 32, m = n % OPS;
-      if (m < KS) return plan.cols(B.q, r0, m);
-      if (m < 2 * KS) return plan.cols(B.o, r0, m - KS);
-      if (m < 2 * KS + 2 * MT) {
-        const int i = m - 2 * KS;
-        return plan.rows(B.o, r0, i / MT, i % MT);
-      }
-      const int i = m - 2 * KS - 2 * MT;
-      return plan.rows(B.q, r0, i / MT, i % MT);
+      const int c = n / L, i = n % L;
+      if (c == C_SA) return plan.cols(B.q, 0, i);
+      if (c == C_DPA) return plan.cols(B.o, 0, i);
+      if (c == C_SB) return plan.cols(B.q, 32, i);
+      if (c == C_DPB) return plan.cols(B.o, 32, i);
+      if (c == C_DVA) return plan.rows(B.o, 0, i / MT, i % MT);
+      if (c == C_DKA) return plan.rows(B.q, 0, i / MT, i % MT);
+      if (HP && c == C_DVP) return plan.rows(Pv.o, 32, i / MT, i % MT);
+      return plan.rows(Pv.q, 32, i / MT, i % MT);              // C_DKP
     };
     frag ring[AH];
 #pragma unroll
     for (int n = 0; n < AH; ++n) ring[n] = opnd(n);
     fence();
+    // take operand n, issue its product, then refill the slot: the copy to
+    // LDS of the next operand goes out after the product, not before it
+    auto refill = [&](int n) ATTN_INLINE {
+      if (n + AH < NOPS) ring[n % AH] = opnd(n + AH);
+    };
+    const int qa = (qt0 + t) * BQ;               // absolute first query row of the tile
+    constexpr int E = 8 / L;                     // exps per product (half a sub-tile per chain)
+    constexpr int M2 = 16 / L;                   // dS multiplies per product
+    // S_a
+    f32x16 sa = row_scalars(B.l, 0);
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const int r0 = st * 32;
-      const int qa = (qt0 + t) * BQ + r0;        // absolute first query row of the sub-tile
-      const int n0 = st * OPS;
-      // C inputs: -L2 and -D of the sub-tile's rows, in accumulator order
-      f32x16 sc, pc;
+    for (int i = 0; i < L; ++i) { sa = M::mma(ring[(C_SA * L + i) % AH], kf[i], sa); refill(C_SA * L + i); fence(); }
+    // dV_p | exps of S_a, first half
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 lv = *reinterpret_cast<const f32x4*>(&B.l[r0 + 8 * g + 4 * h]);
-        const f32x4 dv = *reinterpret_cast<const f32x4*>(&B.dd[r0 + 8 * g + 4 * h]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) { sc[4 * g + i] = lv[i]; pc[4 * g + i] = dv[i]; }
+    for (int i = 0; i < L; ++i) {
+      if constexpr (HP) {
+        mma_acc_agpr(dv_acc[i % MT], ring[(C_DVP * L + i) % AH], bpp[i / MT]);
+        refill(C_DVP * L + i);
       }
-      // S' = Q (c K)^T - L2
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int n = n0 + ks;
-        const frag a = ring[n % AH];
-        if (n + AH < 2 * OPS) ring[n % AH] = opnd(n + AH);
-        sc = M::mma(a, kf[ks], sc);
-        fence();
-      }
-      // dP' = dO V^T - D  |  P = exp2(S') on the VALU
-      constexpr int PER = 16 / KS;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int n = n0 + KS + ks;
-        const frag a = ring[n % AH];
-        if (n + AH < 2 * OPS) ring[n % AH] = opnd(n + AH);
-        pc = M::mma(a, vf[ks], pc);
-#pragma unroll
-        for (int e = 0; e < PER; ++e) sc[ks * PER + e] = fast_exp2(sc[ks * PER + e]);
-        fence();
-      }
-      if (CAUSAL && masked) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (kv > qa + acc_row(r, h)) sc[r] = 0.f;
-      }
-      frag bp[2];
-      bp[0] = M::pack(sc, 0);
-      bp[1] = M::pack(sc, 1);
+      for (int e = 0; e < E; ++e) sa[i * E + e] = fast_exp2(sa[i * E + e]);
       fence();
-      // dV^T += dO^T P  |  dS = P o dP' on the VALU
-      constexpr int PER2 = 16 / (2 * MT);
-      frag bds[2];
+    }
+    // dP_a | exps of S_a, second half
+    f32x16 pa = row_scalars(B.dd, 0);
 #pragma unroll
-      for (int i = 0; i < 2 * MT; ++i) {
-        const int n = n0 + 2 * KS + i;
-        const frag a = ring[n % AH];
-        if (n + AH < 2 * OPS) ring[n % AH] = opnd(n + AH);
-        mma_acc_agpr(dv_acc[i % MT], a, bp[i / MT]);
+    for (int i = 0; i < L; ++i) {
+      pa = M::mma(ring[(C_DPA * L + i) % AH], vf[i], pa);
+      refill(C_DPA * L + i);
 #pragma unroll
-        for (int e = 0; e < PER2; ++e) pc[i * PER2 + e] = sc[i * PER2 + e] * pc[i * PER2 + e];
-        fence();
-      }
-      bds[0] = M::pack(pc, 0);
-      bds[1] = M::pack(pc, 1);
+      for (int e = 0; e < E; ++e) sa[8 + i * E + e] = fast_exp2(sa[8 + i * E + e]);
       fence();
-      // dK^T += Q^T dS
+    }
+    if (CAUSAL && masked) mask_rows(sa, qa);
+    frag bpa[2] = {M::pack(sa, 0), M::pack(sa, 1)};
+    pin_operand(bpa[0]);
+    pin_operand(bpa[1]);
+    fence();
+    // dK_p | dS_a = P_a o dP'_a
 #pragma unroll
-      for (int i = 0; i < 2 * MT; ++i) {
-        const int n = n0 + 2 * KS + 2 * MT + i;
-        const frag a = ring[n % AH];
-        if (n + AH < 2 * OPS) ring[n % AH] = opnd(n + AH);
-        mma_acc_agpr(dk_acc[i % MT], a, bds[i / MT]);
-        fence();
+    for (int i = 0; i < L; ++i) {
+      if constexpr (HP) {
+        mma_acc_agpr(dk_acc[i % MT], ring[(C_DKP * L + i) % AH], bdsp[i / MT]);
+        refill(C_DKP * L + i);
       }
+#pragma unroll
+      for (int e = 0; e < M2; ++e) pa[i * M2 + e] = sa[i * M2 + e] * pa[i * M2 + e];
+      fence();
+    }
+    frag bdsa[2] = {M::pack(pa, 0), M::pack(pa, 1)};
+    pin_operand(bdsa[0]);
+    pin_operand(bdsa[1]);
+    fence();
+    // S_b
+    f32x16 sb = row_scalars(B.l, 32);
+#pragma unroll
+    for (int i = 0; i < L; ++i) { sb = M::mma(ring[(C_SB * L + i) % AH], kf[i], sb); refill(C_SB * L + i); fence(); }
+    // dV_a | exps of S_b, first half
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      mma_acc_agpr(dv_acc[i % MT], ring[(C_DVA * L + i) % AH], bpa[i / MT]);
+      refill(C_DVA * L + i);
+#pragma unroll
+      for (int e = 0; e < E; ++e) sb[i * E + e] = fast_exp2(sb[i * E + e]);
+      fence();
+    }
+    // dP_b | exps of S_b, second half
+    f32x16 pb = row_scalars(B.dd, 32);
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      pb = M::mma(ring[(C_DPB * L + i) % AH], vf[i], pb);
+      refill(C_DPB * L + i);
+#pragma unroll
+      for (int e = 0; e < E; ++e) sb[8 + i * E + e] = fast_exp2(sb[8 + i * E + e]);
+      fence();
+    }
+    if (CAUSAL && masked) mask_rows(sb, qa + 32);
+    bpp[0] = M::pack(sb, 0);
+    bpp[1] = M::pack(sb, 1);
+    pin_operand(bpp[0]);
+    pin_operand(bpp[1]);
+    fence();
+    // dK_a | dS_b = P_b o dP'_b
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      mma_acc_agpr(dk_acc[i % MT], ring[(C_DKA * L + i) % AH], bdsa[i / MT]);
+      refill(C_DKA * L + i);
+#pragma unroll
+      for (int e = 0; e < M2; ++e) pb[i * M2 + e] = sb[i * M2 + e] * pb[i * M2 + e];
+      fence();
+    }
+    bdsp[0] = M::pack(pb, 0);
+    bdsp[1] = M::pack(pb, 1);
+    pin_operand(bdsp[0]);
+    pin_operand(bdsp[1]);
+    fence();
+  };
+  // dV / dK of the last step's sub-tile b, once the walk is over
+  auto flush = [&](const Buf& Pv, const frag (&bpp)[2], const frag (&bdsp)[2]) ATTN_INLINE {
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      mma_acc_agpr(dv_acc[i % MT], plan.rows(Pv.o, 32, i / MT, i % MT), bpp[i / MT]);
+      fence();
+    }
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      mma_acc_agpr(dk_acc[i % MT], plan.rows(Pv.q, 32, i / MT, i % MT), bdsp[i / MT]);
+      fence();
     }
   };
 
@@ -226,40 +293,50 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
   // in L2 instead of each block streaming its own stretch.  Step k visits
   // tile ntiles - 1 - k; causal: the last two steps (the diagonal tiles,
   // BKV = 2 BQ) apply the element mask.  Tiles are copied two steps ahead
-  // into a ring of three separately named buffers picked statically (the loop
-  // is unrolled by three), so a copy has two steps to land: step k waits only
-  // for tile k's copy, leaving tile k + 1's in flight.  A runtime choice
-  // between buffers would make the compiler shuffle the accumulators between
-  // registers while products are in flight.
+  // into a ring of four separately named buffers picked statically (the loop
+  // is unrolled by four): a step reads its own tile and the previous one, and
+  // a copy has two steps to land, so step k waits only for tile k's copy,
+  // leaving tile k + 1's in flight.  A runtime choice between buffers would
+  // make the compiler shuffle the accumulators between registers while
+  // products are in flight.
   auto tile_of = [&](int k) ATTN_INLINE { return ntiles - 1 - k; };
-  auto step = [&](int k, const Buf& cur, Buf& ahead) ATTN_INLINE {
+  frag bpp[2], bdsp[2];
+  auto step = [&](auto has_prev, int k, const Buf& cur, const Buf& prv, Buf& ahead) ATTN_INLINE {
     if (k + 1 < ntiles) wait_async_fills_but<2 * FS::PER>();   // tile k + 1's copy may fly
     else wait_async_fills();
     lds_barrier();
     if (k + 2 < ntiles) fill_whole(ahead, tile_of(k + 2));
-    tile_body(tile_of(k), cur, CAUSAL && k + 2 >= ntiles);
+    step_body(has_prev, tile_of(k), cur, prv, CAUSAL && k + 2 >= ntiles, bpp, bdsp);
   };
   // Steps at least two ahead of the last are unmasked and have two tiles
-  // after them: the main loop takes three of them at a time without a
-  // branch, which keeps each tile body one straight block.
-  auto step_inner = [&](int k, const Buf& cur, Buf& ahead) ATTN_INLINE {
+  // after them: the main loop takes four of them at a time without a
+  // branch, which keeps each step one straight block.
+  auto step_inner = [&](int k, const Buf& cur, const Buf& prv, Buf& ahead) ATTN_INLINE {
     wait_async_fills_but<2 * FS::PER>();
     lds_barrier();
     fill_whole(ahead, tile_of(k + 2));
-    tile_body(tile_of(k), cur, false);
+    step_body(bool_c<true>{}, tile_of(k), cur, prv, false, bpp, bdsp);
   };
   fill(buf0, tile_of(0));
   if (ntiles > 1) fill_whole(buf1, tile_of(1));
-  int k = 0;
-  for (; k + 5 <= ntiles; k += 3) {
-    step_inner(k, buf0, buf2);
-    step_inner(k + 1, buf1, buf0);
-    step_inner(k + 2, buf2, buf1);
+  step(bool_c<false>{}, 0, buf0, buf3, buf2);
+  int k = 1;
+  for (; k + 6 <= ntiles; k += 4) {
+    step_inner(k, buf1, buf0, buf3);
+    step_inner(k + 1, buf2, buf1, buf0);
+    step_inner(k + 2, buf3, buf2, buf1);
+    step_inner(k + 3, buf0, buf3, buf2);
   }
-  if (k < ntiles) step(k, buf0, buf2);
-  if (k + 1 < ntiles) step(k + 1, buf1, buf0);
-  if (k + 2 < ntiles) step(k + 2, buf2, buf1);
-  if (k + 3 < ntiles) step(k + 3, buf0, buf2);
+  if (k < ntiles) step(bool_c<true>{}, k, buf1, buf0, buf3);
+  if (k + 1 < ntiles) step(bool_c<true>{}, k + 1, buf2, buf1, buf0);
+  if (k + 2 < ntiles) step(bool_c<true>{}, k + 2, buf3, buf2, buf1);
+  if (k + 3 < ntiles) step(bool_c<true>{}, k + 3, buf0, buf3, buf2);
+  if (k + 4 < ntiles) step(bool_c<true>{}, k + 4, buf1, buf0, buf3);
+  {
+    const int last = (ntiles - 1) & 3;         // buffer of the last step
+    const Buf& lb = last == 0 ? buf0 : last == 1 ? buf1 : last == 2 ? buf2 : buf3;
+    flush(lb, bpp, bdsp);
+  }
 
   mma_acc_drain();
 #pragma unroll
@@ -444,6 +521,9 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
       for (int r = 0; r < 16; ++r) pc[0][r] = sc[0][r] * pc[0][r];
       bds[0][0] = M::pack(pc[0], 0);
       bds[0][1] = M::pack(pc[0], 1);
+      pin_operand(bds[0][0]);
+      pin_operand(bds[0][1]);
+      mma_operand_guard();
       fence();
       frag t[2 * MT];
       constexpr int PER3 = 16 / (2 * MT);
@@ -451,8 +531,8 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
       for (int i = 0; i < 2 * MT; ++i) {
         const int n = n0 + 2 * KS + i;
         t[i] = ring[n % AH];
-        if (n + AH < 2 * OPS) ring[n % AH] = opnd(n + AH);
         mma_acc_agpr(acc[0][i % MT], t[i], bds[0][i / MT]);
+        if (n + AH < 2 * OPS) ring[n % AH] = opnd(n + AH);
         if constexpr (NH == 2) {
 #pragma unroll
           for (int e = 0; e < PER3; ++e) {
@@ -465,6 +545,9 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
       if constexpr (NH == 2) {
         bds[1][0] = M::pack(pc[1], 0);
         bds[1][1] = M::pack(pc[1], 1);
+        pin_operand(bds[1][0]);
+        pin_operand(bds[1][1]);
+        mma_operand_guard();
         fence();
 #pragma unroll
         for (int i = 0; i < 2 * MT; ++i) mma_acc_agpr(acc[1][i % MT], t[i], bds[1][i / MT]);

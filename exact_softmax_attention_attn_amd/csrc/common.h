@@ -53,11 +53,21 @@ __device__ __forceinline__ void pin_agpr(V& x) { asm volatile("" : "+a"(x)); }
 // v_mfma_f32_32x32x16_bf16 in its AGPR form.  Kernels compiled with every
 // builtin MFMA in VGPR form (their results feed the VALU) use this for the
 // accumulators that only ever meet the matrix core.  The compiler cannot see
-// into the asm, so it is made hazard-safe by itself: the leading s_nop covers
-// the wait states a matrix instruction needs after a VALU write of its A/B
-// operands; back-to-back accumulation into the same registers needs none.
+// into the asm, so it cannot add the two wait states a matrix instruction
+// needs after a VALU write of its A/B operands: callers either write those
+// operands at least two instructions earlier or put mma_operand_guard()
+// between the write and the product (the library's assembly test checks
+// this on the compiled kernels).  Back-to-back accumulation into the same
+// registers needs no wait states.
 __device__ __forceinline__ void mma_acc_agpr(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// Two wait states: between a VALU write of an operand and mma_acc_agpr.
+__device__ __forceinline__ void mma_operand_guard() { asm volatile("s_nop 1"); }
+// Fix where an mma_acc_agpr operand is produced: the optimiser may otherwise
+// sink a pure computation (a pack) down to just before its first product.
+template <typename V> __device__ __forceinline__ void pin_operand(V& x) {
+  asm volatile("" : "+v"(x));
 }
 
 // A value every lane of the wave agrees on, moved to a scalar register (so

@@ -10,6 +10,11 @@ reading accumulators; this test compiles the source to gfx950 assembly with
 the library's own flags and asserts that no instruction outside inline
 assembly touches an accumulator register between an inline product and the
 next drain.
+
+For the same reason the compiler cannot give an inline product the two wait
+states it needs after a VALU instruction writes one of its A/B operand
+registers; the second check asserts that on every path into an inline
+product at least two wait states separate it from such a write.
 """
 
 import os
@@ -119,6 +124,91 @@ def hazards(asm: str):
     return out
 
 
+def _vgprs(tok):
+    m = re.match(r"v\[(\d+):(\d+)\]", tok)
+    if m:
+        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+    m = re.match(r"v(\d+)$", tok)
+    return {int(m.group(1))} if m else set()
+
+
+def _wait_states(t):
+    m = re.match(r"s_nop\s+(\d+)", t)
+    return int(m.group(1)) + 1 if m else 1
+
+
+def _valu_writes(t):
+    op = t.split()[0]
+    if not op.startswith("v_") or op.startswith(("v_mfma", "v_accvgpr_write", "v_cmp", "v_readfirstlane",
+                                                 "v_readlane")):
+        return set()
+    parts = t.split()
+    return _vgprs(parts[1].rstrip(",")) if len(parts) > 1 else set()
+
+
+NEEDED_WAIT_STATES = 2
+
+
+def operand_hazards(asm: str):
+    """Per kernel: inline products reading a VGPR that a VALU instruction wrote
+    fewer than two wait states earlier, on some path."""
+    out = {}
+    for name in re.findall(r"^(_Z\S+):", asm, re.M):
+        st = asm.index(name + ":")
+        en = asm.index(".Lfunc_end", st)
+        blocks = _blocks(asm[st:en].splitlines())
+        index = {b[0]: k for k, b in enumerate(blocks) if b[0] is not None}
+        preds = [[] for _ in blocks]
+        for k in range(len(blocks)):
+            for s_ in _successors(blocks, k):
+                preds[index[s_] if isinstance(s_, str) else s_].append(k)
+
+        def back(k, j, regs, ws, seen):
+            # walk back from instruction j (exclusive) of block k
+            ins = blocks[k][1]
+            for i in range(j - 1, -1, -1):
+                if ws >= NEEDED_WAIT_STATES:
+                    return []
+                t = ins[i][1]
+                if _valu_writes(t) & regs:
+                    return [ins[i]]
+                ws += _wait_states(t)
+            if ws >= NEEDED_WAIT_STATES:
+                return []
+            bad = []
+            for p_ in preds[k]:
+                if (p_, ws) not in seen:
+                    seen.add((p_, ws))
+                    bad += back(p_, len(blocks[p_][1]), regs, ws, seen)
+            return bad
+
+        bad = []
+        for k, b in enumerate(blocks):
+            for j, (i, t, inasm) in enumerate(b[1]):
+                if inasm and t.startswith("v_mfma"):
+                    toks = [x.rstrip(",") for x in t.split()]
+                    regs = _vgprs(toks[2]) | _vgprs(toks[3])
+                    for w in back(k, j, regs, 0, set()):
+                        bad.append((i, t, w[1]))
+        out[name] = bad
+    return out
+
+
+def test_operand_checker_counts_wait_states_along_paths():
+    prod = [";;#ASMSTART", "v_mfma_f32_32x32x16_bf16 a[0:15], v[4:7], v[8:11], a[0:15]", ";;#ASMEND"]
+    close = "\n".join(["_Za:", "v_cvt_pk_bf16_f32 v9, v1, v2", "s_nop 0", *prod, "s_endpgm",
+                       ".Lfunc_end0:"])
+    assert len(operand_hazards(close)["_Za"]) == 1
+    guarded = close.replace("s_nop 0", "s_nop 1")
+    assert operand_hazards(guarded)["_Za"] == []
+    other = close.replace("v9,", "v12,")
+    assert operand_hazards(other)["_Za"] == []
+    # the write sits in a predecessor block that branches straight to the product
+    pred = "\n".join(["_Zb:", "s_cbranch_scc0 .LBB0_2", "v_cvt_pk_bf16_f32 v5, v1, v2",
+                      ".LBB0_2:", *prod, "s_endpgm", ".Lfunc_end0:"])
+    assert [w for _, _, w in operand_hazards(pred)["_Zb"]] == ["v_cvt_pk_bf16_f32 v5, v1, v2"]
+
+
 def test_checker_flags_a_copy_after_an_inline_product():
     asm = "\n".join([
         "_Zk:", ";;#ASMSTART", "s_nop 2", "v_mfma_f32_32x32x16_bf16 a[0:15], v[0:3], v[4:7], a[0:15]",
@@ -159,3 +249,5 @@ def test_pipelined_kernels_never_touch_in_flight_accumulators(tmp_path):
     assert any("dkdv" in k for k in found) and any("dq" in k for k in found)
     bad = {k: v[:3] for k, v in found.items() if v}
     assert not bad, bad
+    close = {k: v[:3] for k, v in operand_hazards(out.read_text()).items() if v}
+    assert not close, close
