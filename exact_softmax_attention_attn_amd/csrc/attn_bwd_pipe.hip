@@ -156,12 +156,32 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     for (int r = 0; r < 16; ++r)
       if (kv > qa + acc_row(r, h)) p[r] = 0.f;
   };
+  // Copy slot j of a tile two steps ahead (issued during this step, into the
+  // buffer freed by this step's barrier): j < PER Q, then dO, then the row
+  // scalars (waves 0 and 1).  Spreading the slots over the step's chains
+  // keeps the four waves from queueing their copies all at once.
+  constexpr int NSLOT = 2 * FS::PER + 1;
+  auto copy_slot = [&](Buf& A, int q0, int j) ATTN_INLINE {
+    if (j < FS::PER) {
+      async_fill_one_untracked<BQ, D>(QT{A.q}, Q + base + q0 * rs, copy_off, wave, j);
+    } else if (j < 2 * FS::PER) {
+      async_fill_one_untracked<BQ, D>(QT{A.o}, dO + base + q0 * rs, copy_off, wave, j - FS::PER);
+    } else {
+      if (wave == 0) fill_row64_untracked(A.l, Lh + q0, lane);
+      if (wave == 1) fill_row64_untracked(A.dd, Dh + q0, lane);
+    }
+  };
   auto step_body = [&](auto has_prev, int t, const Buf& B, const Buf& Pv, bool masked,
-                       frag (&bpp)[2], frag (&bdsp)[2]) ATTN_INLINE {
+                       frag (&bpp)[2], frag (&bdsp)[2], auto&& copy) ATTN_INLINE {
     constexpr bool HP = decltype(has_prev)::value;
     constexpr int C_SA = 0, C_DVP = 1, C_DPA = HP ? 2 : 1, C_DKP = 3, C_SB = HP ? 4 : 2,
                   C_DVA = HP ? 5 : 3, C_DPB = HP ? 6 : 4, C_DKA = HP ? 7 : 5;
-    constexpr int NOPS = (HP ? 8 : 6) * L;
+    constexpr int NCH = HP ? 8 : 6;
+    constexpr int NOPS = NCH * L;
+    // copy slot i * NCH + c goes out after product i of chain c
+    auto slot = [&](int c, int i) ATTN_INLINE {
+      if (i * NCH + c < NSLOT) copy(i * NCH + c);
+    };
     auto opnd = [&](int n) ATTN_INLINE -> frag {
       const int c = n / L, i = n % L;
       if (c == C_SA) return plan.cols(B.q, 0, i);
@@ -188,13 +208,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     // S_a
     f32x16 sa = row_scalars(B.l, 0);
 #pragma unroll
-    for (int i = 0; i < L; ++i) { sa = M::mma(ring[(C_SA * L + i) % AH], kf[i], sa); refill(C_SA * L + i); fence(); }
+    for (int i = 0; i < L; ++i) {
+      sa = M::mma(ring[(C_SA * L + i) % AH], kf[i], sa);
+      refill(C_SA * L + i);
+      slot(C_SA, i);
+      fence();
+    }
     // dV_p | exps of S_a, first half
 #pragma unroll
     for (int i = 0; i < L; ++i) {
       if constexpr (HP) {
         mma_acc_agpr(dv_acc[i % MT], ring[(C_DVP * L + i) % AH], bpp[i / MT]);
         refill(C_DVP * L + i);
+        slot(C_DVP, i);
       }
 #pragma unroll
       for (int e = 0; e < E; ++e) sa[i * E + e] = fast_exp2(sa[i * E + e]);
@@ -206,6 +232,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     for (int i = 0; i < L; ++i) {
       pa = M::mma(ring[(C_DPA * L + i) % AH], vf[i], pa);
       refill(C_DPA * L + i);
+      slot(C_DPA, i);
 #pragma unroll
       for (int e = 0; e < E; ++e) sa[8 + i * E + e] = fast_exp2(sa[8 + i * E + e]);
       fence();
@@ -221,6 +248,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
       if constexpr (HP) {
         mma_acc_agpr(dk_acc[i % MT], ring[(C_DKP * L + i) % AH], bdsp[i / MT]);
         refill(C_DKP * L + i);
+        slot(C_DKP, i);
       }
 #pragma unroll
       for (int e = 0; e < M2; ++e) pa[i * M2 + e] = sa[i * M2 + e] * pa[i * M2 + e];
@@ -233,12 +261,18 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     // S_b
     f32x16 sb = row_scalars(B.l, 32);
 #pragma unroll
-    for (int i = 0; i < L; ++i) { sb = M::mma(ring[(C_SB * L + i) % AH], kf[i], sb); refill(C_SB * L + i); fence(); }
+    for (int i = 0; i < L; ++i) {
+      sb = M::mma(ring[(C_SB * L + i) % AH], kf[i], sb);
+      refill(C_SB * L + i);
+      slot(C_SB, i);
+      fence();
+    }
     // dV_a | exps of S_b, first half
 #pragma unroll
     for (int i = 0; i < L; ++i) {
       mma_acc_agpr(dv_acc[i % MT], ring[(C_DVA * L + i) % AH], bpa[i / MT]);
       refill(C_DVA * L + i);
+      slot(C_DVA, i);
 #pragma unroll
       for (int e = 0; e < E; ++e) sb[i * E + e] = fast_exp2(sb[i * E + e]);
       fence();
@@ -249,6 +283,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     for (int i = 0; i < L; ++i) {
       pb = M::mma(ring[(C_DPB * L + i) % AH], vf[i], pb);
       refill(C_DPB * L + i);
+      slot(C_DPB, i);
 #pragma unroll
       for (int e = 0; e < E; ++e) sb[8 + i * E + e] = fast_exp2(sb[8 + i * E + e]);
       fence();
@@ -264,6 +299,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     for (int i = 0; i < L; ++i) {
       mma_acc_agpr(dk_acc[i % MT], ring[(C_DKA * L + i) % AH], bdsa[i / MT]);
       refill(C_DKA * L + i);
+      slot(C_DKA, i);
 #pragma unroll
       for (int e = 0; e < M2; ++e) pb[i * M2 + e] = sb[i * M2 + e] * pb[i * M2 + e];
       fence();
@@ -305,8 +341,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     if (k + 1 < ntiles) wait_async_fills_but<2 * FS::PER>();   // tile k + 1's copy may fly
     else wait_async_fills();
     lds_barrier();
-    if (k + 2 < ntiles) fill_whole(ahead, tile_of(k + 2));
-    step_body(has_prev, tile_of(k), cur, prv, CAUSAL && k + 2 >= ntiles, bpp, bdsp);
+    const bool ahead_on = k + 2 < ntiles;
+    const int qn = (qt0 + tile_of(k + 2)) * BQ;
+    step_body(has_prev, tile_of(k), cur, prv, CAUSAL && k + 2 >= ntiles, bpp, bdsp,
+              [&](int j) ATTN_INLINE { if (ahead_on) copy_slot(ahead, qn, j); });
   };
   // Steps at least two ahead of the last are unmasked and have two tiles
   // after them: the main loop takes four of them at a time without a
@@ -314,8 +352,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
   auto step_inner = [&](int k, const Buf& cur, const Buf& prv, Buf& ahead) ATTN_INLINE {
     wait_async_fills_but<2 * FS::PER>();
     lds_barrier();
-    fill_whole(ahead, tile_of(k + 2));
-    step_body(bool_c<true>{}, tile_of(k), cur, prv, false, bpp, bdsp);
+    const int qn = (qt0 + tile_of(k + 2)) * BQ;
+    step_body(bool_c<true>{}, tile_of(k), cur, prv, false, bpp, bdsp,
+              [&](int j) ATTN_INLINE { copy_slot(ahead, qn, j); });
   };
   fill(buf0, tile_of(0));
   if (ntiles > 1) fill_whole(buf1, tile_of(1));
