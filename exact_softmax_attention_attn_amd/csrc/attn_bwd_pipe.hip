@@ -495,7 +495,20 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
   // sub-tile is K (head dim), V (head dim), K^T (positions); reads run AH
   // operands ahead through the whole tile.
   constexpr int OPS = 2 * KS + 2 * MT;          // operands per sub-tile
-  auto tile_body = [&](int kt, const Buf& B, bool masked) ATTN_INLINE {
+  // Copy slot j (K for j < PER, then V) of the tile two steps ahead goes out
+  // inside the step, spread over the S and dP chains of both sub-tiles, into
+  // the buffer this step's barrier freed.
+  constexpr int NSLOT = 2 * FS::PER, SPC = NSLOT / 4;    // slots per chain
+  static_assert(NSLOT % 4 == 0 && KS % SPC == 0, "copy slots per chain");
+  auto copy_slot = [&](Buf& A, int k0, int j) ATTN_INLINE {
+    if (j < FS::PER) async_fill_one_untracked<BKV, D, NW>(KT{A.k}, K + base + k0 * rs, copy_off, wave, j);
+    else async_fill_one_untracked<BKV, D, NW>(KT{A.v}, V + base + k0 * rs, copy_off, wave, j - FS::PER);
+  };
+  auto tile_body = [&](int kt, const Buf& B, bool masked, auto&& copy) ATTN_INLINE {
+    // slot of (sub-tile st, chain ch in {S, dP}, step kk), or -1
+    auto slot = [&](int st, int ch, int kk) ATTN_INLINE {
+      if (kk % (KS / SPC) == 0) copy(st * 2 * SPC + ch * SPC + kk / (KS / SPC));
+    };
     auto opnd = [&](int n) ATTN_INLINE -> frag {
       const int r0 = (n / OPS) * 32, m = n % OPS;
       if (m < KS) return plan.cols(B.k, r0, m);
@@ -522,6 +535,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
         if (n + AH < 2 * OPS) ring[n % AH] = opnd(n + AH);
 #pragma unroll
         for (int c = 0; c < NH; ++c) sc[c] = M::mma(a, qf[c][kk], sc[c]);
+        slot(st, 0, kk);
         fence();
       }
       // dP'^T = ones bd^T + V dO^T | P = exp2(S') on the VALU
@@ -534,6 +548,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
         if (n + AH < 2 * OPS) ring[n % AH] = opnd(n + AH);
 #pragma unroll
         for (int c = 0; c < NH; ++c) pc[c] = M::mma(a, of[c][kk], pc[c]);
+        slot(st, 1, kk);
 #pragma unroll
         for (int c = 0; c < NH; ++c)
 #pragma unroll
@@ -605,8 +620,11 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
     if (kt + 1 < ntiles && (kt + 2) * BKV <= N) wait_async_fills_but<2 * FS::PER>();
     else wait_async_fills();
     lds_barrier();
-    if (kt + 2 < ntiles) fill(ahead, kt + 2);
-    tile_body(kt, cur, CAUSAL && kt >= diag0);
+    const int k2 = (kt + 2) * BKV;
+    const bool spread = kt + 2 < ntiles && k2 + BKV <= N;
+    if (kt + 2 < ntiles && !spread) fill(ahead, kt + 2);     // ragged: register path now
+    tile_body(kt, cur, CAUSAL && kt >= diag0,
+              [&](int j) ATTN_INLINE { if (spread) copy_slot(ahead, k2, j); });
   };
   // Steps below the diagonal whose tile two ahead is whole need none of the
   // checks above: the first loop takes three of them at a time without a
@@ -614,10 +632,8 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
   auto step_inner = [&](int kt, const Buf& cur, Buf& ahead) ATTN_INLINE {
     wait_async_fills_but<2 * FS::PER>();
     lds_barrier();
-    const int k0 = (kt + 2) * BKV;
-    async_fill_untracked<BKV, D, NW>(KT{ahead.k}, K + base + k0 * rs, copy_off, wave);
-    async_fill_untracked<BKV, D, NW>(KT{ahead.v}, V + base + k0 * rs, copy_off, wave);
-    tile_body(kt, cur, false);
+    const int k2 = (kt + 2) * BKV;
+    tile_body(kt, cur, false, [&](int j) ATTN_INLINE { copy_slot(ahead, k2, j); });
   };
   fill(buf0, 0);
   if (ntiles > 1) fill(buf1, 1);
