@@ -134,11 +134,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
   // One step = one query tile t, sub-tiles a (rows 0..31) and b (32..63),
   // plus the dV / dK products of the previous tile's sub-tile b ("p"), whose
   // P and dS arrive packed in bpp / bdsp.  Chains of L = D / 16 products:
-  //   S_a | dV_p | dP_a | dK_p | S_b | dV_a | dP_b | dK_a
-  // Each VALU stage reads a chain that finished one chain earlier: the exps
-  // of S_a run beside dV_p and dP_a, dS_a beside dK_p, the exps of S_b beside
-  // dV_a and dP_b, dS_b beside dK_a.  P_b and dS_b leave packed for the next
-  // step.  Operand reads run AH fragments ahead through the step.
+  //   dV_p | S_a | dK_p | dP_a | S_b | dV_a | dP_b | dK_a
+  // Each VALU stage reads a chain that finished at least one chain earlier:
+  // the exps of S_a run beside dK_p and dP_a, dS_a beside S_b, the exps of
+  // S_b beside dV_a and dP_b, dS_b beside dK_a; P_b and dS_b leave packed for
+  // the next step.  The row scalars that enter S and dP as C inputs are read
+  // from LDS one chain ahead, and operand reads run AH fragments ahead
+  // through the step, so no chain starts on a fresh LDS read.
   constexpr int L = KS;                       // = 2 * MT
   static_assert(L == 2 * MT, "chain length");
   auto row_scalars = [&](const float* src, int r0) ATTN_INLINE {
@@ -174,7 +176,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
   auto step_body = [&](auto has_prev, int t, const Buf& B, const Buf& Pv, bool masked,
                        frag (&bpp)[2], frag (&bdsp)[2], auto&& copy) ATTN_INLINE {
     constexpr bool HP = decltype(has_prev)::value;
-    constexpr int C_SA = 0, C_DVP = 1, C_DPA = HP ? 2 : 1, C_DKP = 3, C_SB = HP ? 4 : 2,
+    constexpr int C_DVP = 0, C_SA = HP ? 1 : 0, C_DKP = 2, C_DPA = HP ? 3 : 1, C_SB = HP ? 4 : 2,
                   C_DVA = HP ? 5 : 3, C_DPB = HP ? 6 : 4, C_DKA = HP ? 7 : 5;
     constexpr int NCH = HP ? 8 : 6;
     constexpr int NOPS = NCH * L;
@@ -196,38 +198,52 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     frag ring[AH];
 #pragma unroll
     for (int n = 0; n < AH; ++n) ring[n] = opnd(n);
-    fence();
-    // take operand n, issue its product, then refill the slot: the copy to
-    // LDS of the next operand goes out after the product, not before it
+    // take operand n, issue its product, then refill the slot: the read of
+    // the next operand goes out after the product, not before it
     auto refill = [&](int n) ATTN_INLINE {
       if (n + AH < NOPS) ring[n % AH] = opnd(n + AH);
     };
     const int qa = (qt0 + t) * BQ;               // absolute first query row of the tile
     constexpr int E = 8 / L;                     // exps per product (half a sub-tile per chain)
     constexpr int M2 = 16 / L;                   // dS multiplies per product
-    // S_a
-    f32x16 sa = row_scalars(B.l, 0);
+    auto s_chain = [&](int c, f32x16& acc) ATTN_INLINE {
 #pragma unroll
-    for (int i = 0; i < L; ++i) {
-      sa = M::mma(ring[(C_SA * L + i) % AH], kf[i], sa);
-      refill(C_SA * L + i);
-      slot(C_SA, i);
-      fence();
-    }
-    // dV_p | exps of S_a, first half
+      for (int i = 0; i < L; ++i) {
+        acc = M::mma(ring[(c * L + i) % AH], kf[i], acc);
+        refill(c * L + i);
+        slot(c, i);
+        fence();
+      }
+    };
+    f32x16 sa = row_scalars(B.l, 0);             // S_a's C input, read during dV_p
+    fence();
+    // dV_p
+    if constexpr (HP) {
 #pragma unroll
-    for (int i = 0; i < L; ++i) {
-      if constexpr (HP) {
+      for (int i = 0; i < L; ++i) {
         mma_acc_agpr(dv_acc[i % MT], ring[(C_DVP * L + i) % AH], bpp[i / MT]);
         refill(C_DVP * L + i);
         slot(C_DVP, i);
+        fence();
+      }
+    }
+    // S_a
+    s_chain(C_SA, sa);
+    // dK_p | exps of S_a, first half
+    f32x16 pa = row_scalars(B.dd, 0);            // dP_a's C input
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      if constexpr (HP) {
+        mma_acc_agpr(dk_acc[i % MT], ring[(C_DKP * L + i) % AH], bdsp[i / MT]);
+        refill(C_DKP * L + i);
+        slot(C_DKP, i);
       }
 #pragma unroll
       for (int e = 0; e < E; ++e) sa[i * E + e] = fast_exp2(sa[i * E + e]);
       fence();
     }
     // dP_a | exps of S_a, second half
-    f32x16 pa = row_scalars(B.dd, 0);
+    f32x16 sb = row_scalars(B.l, 32);            // S_b's C input
 #pragma unroll
     for (int i = 0; i < L; ++i) {
       pa = M::mma(ring[(C_DPA * L + i) % AH], vf[i], pa);
@@ -242,14 +258,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     pin_operand(bpa[0]);
     pin_operand(bpa[1]);
     fence();
-    // dK_p | dS_a = P_a o dP'_a
+    // S_b | dS_a = P_a o dP'_a
 #pragma unroll
     for (int i = 0; i < L; ++i) {
-      if constexpr (HP) {
-        mma_acc_agpr(dk_acc[i % MT], ring[(C_DKP * L + i) % AH], bdsp[i / MT]);
-        refill(C_DKP * L + i);
-        slot(C_DKP, i);
-      }
+      sb = M::mma(ring[(C_SB * L + i) % AH], kf[i], sb);
+      refill(C_SB * L + i);
+      slot(C_SB, i);
 #pragma unroll
       for (int e = 0; e < M2; ++e) pa[i * M2 + e] = sa[i * M2 + e] * pa[i * M2 + e];
       fence();
@@ -257,16 +271,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     frag bdsa[2] = {M::pack(pa, 0), M::pack(pa, 1)};
     pin_operand(bdsa[0]);
     pin_operand(bdsa[1]);
+    f32x16 pb = row_scalars(B.dd, 32);           // dP_b's C input
     fence();
-    // S_b
-    f32x16 sb = row_scalars(B.l, 32);
-#pragma unroll
-    for (int i = 0; i < L; ++i) {
-      sb = M::mma(ring[(C_SB * L + i) % AH], kf[i], sb);
-      refill(C_SB * L + i);
-      slot(C_SB, i);
-      fence();
-    }
     // dV_a | exps of S_b, first half
 #pragma unroll
     for (int i = 0; i < L; ++i) {
@@ -278,7 +284,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
       fence();
     }
     // dP_b | exps of S_b, second half
-    f32x16 pb = row_scalars(B.dd, 32);
 #pragma unroll
     for (int i = 0; i < L; ++i) {
       pb = M::mma(ring[(C_DPB * L + i) % AH], vf[i], pb);
