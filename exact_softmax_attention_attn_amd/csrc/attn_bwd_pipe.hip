@@ -174,10 +174,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     }
   };
   auto step_body = [&](auto has_prev, int t, const Buf& B, const Buf& Pv, bool masked,
-                       frag (&bpp)[2], frag (&bdsp)[2], auto&& copy) ATTN_INLINE {
+                       frag (&bpp)[2], frag (&bdsp)[2], frag (&ring)[AH], auto&& copy) ATTN_INLINE {
     constexpr bool HP = decltype(has_prev)::value;
-    constexpr int C_DVP = 0, C_SA = HP ? 1 : 0, C_DKP = 2, C_DPA = HP ? 3 : 1, C_SB = HP ? 4 : 2,
-                  C_DVA = HP ? 5 : 3, C_DPB = HP ? 6 : 4, C_DKA = HP ? 7 : 5;
+    // chain positions in the step (-1: chain absent in the walk's first step)
+    constexpr int C_DVP = HP ? 0 : -1, C_SA = HP ? 1 : 0, C_DKP = HP ? 2 : -1, C_DPA = HP ? 3 : 1,
+                  C_SB = HP ? 4 : 2, C_DVA = HP ? 5 : 3, C_DPB = HP ? 6 : 4, C_DKA = HP ? 7 : 5;
     constexpr int NCH = HP ? 8 : 6;
     constexpr int NOPS = NCH * L;
     // copy slot i * NCH + c goes out after product i of chain c
@@ -192,17 +193,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
       if (c == C_DPB) return plan.cols(B.o, 32, i);
       if (c == C_DVA) return plan.rows(B.o, 0, i / MT, i % MT);
       if (c == C_DKA) return plan.rows(B.q, 0, i / MT, i % MT);
-      if (HP && c == C_DVP) return plan.rows(Pv.o, 32, i / MT, i % MT);
-      return plan.rows(Pv.q, 32, i / MT, i % MT);              // C_DKP
+      if (c == C_DKP) return plan.rows(Pv.q, 32, i / MT, i % MT);
+      if (c == C_DVP) return plan.rows(Pv.o, 32, i / MT, i % MT);
+      // past the step: the next step's dV_p reads this tile's sub-tile b
+      return plan.rows(B.o, 32, i / MT, i % MT);
     };
-    frag ring[AH];
+    // The ring arrives holding this step's first AH operands (the previous
+    // step read them ahead) except in the walk's first step.
+    if constexpr (!HP) {
 #pragma unroll
-    for (int n = 0; n < AH; ++n) ring[n] = opnd(n);
+      for (int n = 0; n < AH; ++n) ring[n] = opnd(n);
+    }
     // take operand n, issue its product, then refill the slot: the read of
-    // the next operand goes out after the product, not before it
-    auto refill = [&](int n) ATTN_INLINE {
-      if (n + AH < NOPS) ring[n % AH] = opnd(n + AH);
-    };
+    // the next operand goes out after the product, not before it; the last
+    // refills fetch the next step's first operands
+    auto refill = [&](int n) ATTN_INLINE { ring[n % AH] = opnd(n + AH); };
     const int qa = (qt0 + t) * BQ;               // absolute first query row of the tile
     constexpr int E = 8 / L;                     // exps per product (half a sub-tile per chain)
     constexpr int M2 = 16 / L;                   // dS multiplies per product
@@ -341,14 +346,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
   // make the compiler shuffle the accumulators between registers while
   // products are in flight.
   auto tile_of = [&](int k) ATTN_INLINE { return ntiles - 1 - k; };
-  frag bpp[2], bdsp[2];
+  frag bpp[2], bdsp[2], ring[AH];
   auto step = [&](auto has_prev, int k, const Buf& cur, const Buf& prv, Buf& ahead) ATTN_INLINE {
     if (k + 1 < ntiles) wait_async_fills_but<2 * FS::PER>();   // tile k + 1's copy may fly
     else wait_async_fills();
     lds_barrier();
     const bool ahead_on = k + 2 < ntiles;
     const int qn = (qt0 + tile_of(k + 2)) * BQ;
-    step_body(has_prev, tile_of(k), cur, prv, CAUSAL && k + 2 >= ntiles, bpp, bdsp,
+    step_body(has_prev, tile_of(k), cur, prv, CAUSAL && k + 2 >= ntiles, bpp, bdsp, ring,
               [&](int j) ATTN_INLINE { if (ahead_on) copy_slot(ahead, qn, j); });
   };
   // Steps at least two ahead of the last are unmasked and have two tiles
@@ -358,7 +363,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     wait_async_fills_but<2 * FS::PER>();
     lds_barrier();
     const int qn = (qt0 + tile_of(k + 2)) * BQ;
-    step_body(bool_c<true>{}, tile_of(k), cur, prv, false, bpp, bdsp,
+    step_body(bool_c<true>{}, tile_of(k), cur, prv, false, bpp, bdsp, ring,
               [&](int j) ATTN_INLINE { copy_slot(ahead, qn, j); });
   };
   fill(buf0, tile_of(0));
