@@ -116,6 +116,8 @@ EDGE = [
     (1, 2, 300, 100, "f32", True),
     (2, 2, 77, 32, "f32", False),
     (1, 2, 190, 128, "bf16", False),
+    (1, 2, 1000, 128, "bf16", False),  # long non-causal walks through the pipelined main loops
+    (1, 2, 700, 64, "bf16", False),
     (1, 1, 257, 64, "f32", False),
     (1, 1, 1, 16, "bf16", False),
 ]
