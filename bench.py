@@ -13,6 +13,13 @@ dV, dK) over its mean duration from HIP events recorded around it on the
 launch stream, against the bf16 dense MFMA peak.  `cpu_baseline` times the
 fp64 oracle on whole (batch, head) slices of the same workload on the host
 cores (a bounded sample of about CPU_BASELINE_SECONDS).
+
+Secondary denominators, measured after the timed region on the same GPU:
+`denominators.copy_gbs` (a 1 GiB cast copy, bytes read + written per second)
+and `denominators.gemm_bf16_tflops` (one plain 8192^3 bf16 matrix product
+through torch, which runs the vendor GEMM library), with the backward's value
+as a fraction of each.  `device_mem_delta_bytes` is the drop in free device
+memory across one synchronised backward step (no N x N buffer: 0 expected).
 """
 
 from __future__ import annotations
@@ -136,6 +143,39 @@ def summarize_pmc(fetch_dirs, write_dirs, calib_mib):
     return rec
 
 
+def measure_denominators(torch, dev):
+    """Measured copy bandwidth and library GEMM rate on this GPU (medians of 5)."""
+    import numpy as np
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    def timed(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        t = []
+        for _ in range(reps):
+            ev[0].record()
+            fn()
+            ev[1].record()
+            torch.cuda.synchronize()
+            t.append(ev[0].elapsed_time(ev[1]))
+        return float(np.median(t)) * 1e-3
+
+    n = (1 << 30) // 4
+    a = torch.ones(n, dtype=torch.float32, device=dev)
+    b = torch.empty(n, dtype=torch.int32, device=dev)
+    copy_s = timed(lambda: b.copy_(a))           # a cast copy runs as a kernel
+    del a, b
+    m = 8192
+    x = torch.randn(m, m, device=dev).to(torch.bfloat16).contiguous()
+    y = torch.randn(m, m, device=dev).to(torch.bfloat16).contiguous()
+    gemm_s = timed(lambda: torch.matmul(x, y))
+    del x, y
+    torch.cuda.synchronize()
+    return {"copy_gbs": round(2 * (1 << 30) / copy_s / 1e9, 1),
+            "gemm_bf16_tflops": round(2 * m ** 3 / gemm_s / 1e12, 1),
+            "gemm_shape": f"{m}x{m}x{m} bf16, torch.matmul (vendor library)"}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -233,6 +273,15 @@ def main(argv=None):
     torch.cuda.synchronize()
     fwd_ms = fev[0].elapsed_time(fev[1]) / fwd_runs
 
+    # no-N^2 evidence: free device memory across one backward step
+    torch.cuda.synchronize()
+    free0 = torch.cuda.mem_get_info(dev)[0]
+    step()
+    torch.cuda.synchronize()
+    mem_delta = free0 - torch.cuda.mem_get_info(dev)[0]
+
+    denominators = measure_denominators(torch, dev)
+
     if args.copy_calibration_mib:
         # a cast copy runs as a kernel (a same-type copy may go to a DMA engine):
         # it reads and writes exactly n * 4 bytes
@@ -266,6 +315,11 @@ def main(argv=None):
         "hbm_gbs_algorithmic": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
         "fwd_lse": {"ms": round(fwd_ms, 4),
                     "tflops": round(4 * w.d * P / (fwd_ms * 1e-3) / 1e12, 3)},
+        "device_mem_delta_bytes": int(mem_delta),
+        "denominators": dict(denominators,
+                             value_over_gemm=round(value / denominators["gemm_bf16_tflops"], 4),
+                             hbm_over_copy=round(alg_bytes / (ms * 1e-3) / 1e9
+                                                 / denominators["copy_gbs"], 4)),
         "roofline": {"kernel": DOMINANT_KERNEL, "bound": "mfma", "achieved": round(achieved, 3),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic_record()},
