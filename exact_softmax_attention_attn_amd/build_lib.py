@@ -17,11 +17,12 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libattn.so")
-SOURCES = ("attn_api.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_bwd_pipe.hip")
+SOURCES = ("attn_api.hip", "attn_fwd.hip", "attn_fwd_pipe.hip", "attn_bwd.hip", "attn_bwd_pipe.hip")
 # The pipelined kernels keep long-lived operands in AGPRs (pinned in the
 # source) and want every MFMA result and accumulator in VGPRs, where the VALU
 # can read them without copies.
-PER_SOURCE_FLAGS = {"attn_bwd_pipe.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
+PER_SOURCE_FLAGS = {"attn_bwd_pipe.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"],
+                    "attn_fwd_pipe.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 COMMON_FLAGS = [

@@ -387,7 +387,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     flush(lb, bpp, bdsp);
   }
 
-  mma_acc_drain();
+  mma_acc_drain(dv_acc);
+#pragma unroll
+  for (int i = 0; i < MT; ++i) asm volatile("" : "+a"(dk_acc[i]));
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     store_acc_transposed<bf16>(dv_acc[mt], dV + base, rs, kv0, mt * 32, N, d, 1.f, lane);
@@ -662,7 +664,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
   if (kt < ntiles) step(kt, buf0, buf2);
   if (kt + 1 < ntiles) step(kt + 1, buf1, buf0);
 
-  mma_acc_drain();
+  mma_acc_drain(acc);
 #pragma unroll
   for (int c = 0; c < NH; ++c)
 #pragma unroll

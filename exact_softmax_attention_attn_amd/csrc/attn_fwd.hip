@@ -160,6 +160,7 @@ static hipError_t fwd_go(const FwdArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_fwd_lse(const FwdArgs& a, hipStream_t stream) {
+  if (a.dtype == 1 && (a.d == 64 || a.d == 128)) return launch_fwd_lse_bf16_pipe(a, stream);
   const int bucket = head_dim_bucket(a.d);
   if (a.dtype == 1) {
     if (a.causal) {

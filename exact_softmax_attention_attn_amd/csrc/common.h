@@ -97,6 +97,23 @@ __device__ __forceinline__ BlockOrder block_order() {
 __device__ __forceinline__ void mma_acc_drain() {
   asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
 }
+// The drain above, then every accumulator tile re-declared by an empty
+// volatile asm: volatile statements keep their order, so no read of an
+// accumulator can be scheduled above the drain.
+template <int N>
+__device__ __forceinline__ void mma_acc_drain(f32x16 (&acc)[N]) {
+  mma_acc_drain();
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+a"(acc[i]));
+}
+template <int N, int M>
+__device__ __forceinline__ void mma_acc_drain(f32x16 (&acc)[N][M]) {
+  mma_acc_drain();
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+#pragma unroll
+    for (int j = 0; j < M; ++j) asm volatile("" : "+a"(acc[i][j]));
+}
 
 // ---------------------------------------------------------------------------
 // Element type traits: which 32x32 MFMA, how deep one instruction contracts,

@@ -43,5 +43,6 @@ hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_lse(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dkdv_bf16_pipe(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dq_bf16_pipe(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_fwd_lse_bf16_pipe(const FwdArgs& a, hipStream_t stream);
 
 }  // namespace attn

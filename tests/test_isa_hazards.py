@@ -236,8 +236,9 @@ def test_checker_follows_branches_not_text_order():
 
 @pytest.mark.skipif(shutil.which(build_lib.HIPCC) is None and not os.path.exists(build_lib.HIPCC),
                     reason="hipcc not available")
-def test_pipelined_kernels_never_touch_in_flight_accumulators(tmp_path):
-    src = "attn_bwd_pipe.hip"
+@pytest.mark.parametrize("src,kinds", [("attn_bwd_pipe.hip", ("dkdv", "dq")),
+                                       ("attn_fwd_pipe.hip", ("fwd",))])
+def test_pipelined_kernels_never_touch_in_flight_accumulators(tmp_path, src, kinds):
     out = tmp_path / "pipe.s"
     flags = [f for f in build_lib.COMMON_FLAGS if f != "-fPIC"]
     cmd = [build_lib.HIPCC, *flags, *build_lib.PER_SOURCE_FLAGS.get(src, []), "--cuda-device-only",
@@ -246,7 +247,7 @@ def test_pipelined_kernels_never_touch_in_flight_accumulators(tmp_path):
     assert r.returncode == 0, r.stdout[-2000:]
     found = hazards(out.read_text())
     assert found, "no kernels found in the assembly"
-    assert any("dkdv" in k for k in found) and any("dq" in k for k in found)
+    assert all(any(kind in k for k in found) for kind in kinds)
     bad = {k: v[:3] for k, v in found.items() if v}
     assert not bad, bad
     close = {k: v[:3] for k, v in operand_hazards(out.read_text()).items() if v}
