@@ -16,9 +16,9 @@ cores (a bounded sample of about CPU_BASELINE_SECONDS).
 
 Secondary denominators, measured after the timed region on the same GPU:
 `denominators.copy_gbs` (a 1 GiB cast copy, bytes read + written per second)
-and `denominators.gemm_bf16_tflops` (one plain 8192^3 bf16 matrix product
-through torch, which runs the vendor GEMM library), with the backward's value
-as a fraction of each.  `device_mem_delta_bytes` is the drop in free device
+and `denominators.gemm_bf16_tflops` (plain 8192^3 bf16 matrix products through
+torch, which runs the vendor GEMM library), both sustained over back-to-back
+calls, with the backward's value as a fraction of each.  `device_mem_delta_bytes` is the drop in free device
 memory across one synchronised backward step (no N x N buffer: 0 expected).
 """
 
@@ -144,20 +144,23 @@ def summarize_pmc(fetch_dirs, write_dirs, calib_mib):
 
 
 def measure_denominators(torch, dev):
-    """Measured copy bandwidth and library GEMM rate on this GPU (medians of 5)."""
+    """Measured copy bandwidth and library GEMM rate on this GPU, sustained: the
+    median over 3 rounds of the mean time per call of 20 back-to-back calls."""
     import numpy as np
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
 
-    def timed(fn, reps=5):
-        fn()
+    def timed(fn, calls=20, rounds=3):
+        for _ in range(3):
+            fn()
         torch.cuda.synchronize()
         t = []
-        for _ in range(reps):
+        for _ in range(rounds):
             ev[0].record()
-            fn()
+            for _ in range(calls):
+                fn()
             ev[1].record()
             torch.cuda.synchronize()
-            t.append(ev[0].elapsed_time(ev[1]))
+            t.append(ev[0].elapsed_time(ev[1]) / calls)
         return float(np.median(t)) * 1e-3
 
     n = (1 << 30) // 4
@@ -173,7 +176,7 @@ def measure_denominators(torch, dev):
     torch.cuda.synchronize()
     return {"copy_gbs": round(2 * (1 << 30) / copy_s / 1e9, 1),
             "gemm_bf16_tflops": round(2 * m ** 3 / gemm_s / 1e12, 1),
-            "gemm_shape": f"{m}x{m}x{m} bf16, torch.matmul (vendor library)"}
+            "gemm_shape": f"{m}x{m}x{m} bf16, torch.matmul (vendor library), 20 calls back to back"}
 
 
 def main(argv=None):

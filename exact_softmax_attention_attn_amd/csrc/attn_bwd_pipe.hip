@@ -399,7 +399,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
 
 // ---------------------------------------------------------------------------
 // dQ (bf16).  Workgroup = NW waves = 256 query rows of one (b, h); wave w owns
-// query rows qw + [0, WQ) as WQ / 32 halves of 32 rows.  Q (pre-multiplied by
+// query rows qw + [0, WQ) as two halves of 32 rows.  Q (pre-multiplied by
 // scale log2e) and dO of the wave's rows and its dQ^T accumulators live in
 // AGPRs for the whole kernel.  With two halves each LDS operand fragment
 // feeds two matrix instructions.  Per key sub-tile of 32 rows:
@@ -410,9 +410,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
 // a constant "ones" fragment and a fragment carrying the row scalar split
 // into two bf16 parts (hi + lo, exact to about 2^-16 relative), which adds the
 // scalar to every element.  That costs one matrix instruction per chain and
-// saves an add per element on the VALU.  Operand reads run AH fragments ahead
-// through a whole 64-row key tile.  Key tiles are copied two steps ahead into
-// a ring of three separately named LDS buffers.  No atomics.
+// saves an add per element on the VALU.  The two halves' chains run one
+// after the other, so each VALU stage sits beside a chain it does not feed.
+// Key tiles are copied two steps ahead into a ring of three separately named
+// LDS buffers.  No atomics.
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL, int WQ, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
@@ -422,10 +423,8 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
   using M = Mma<bf16>;
   using frag = bf16x8;
   constexpr int NH = WQ / 32;                  // 32-row halves per wave
-  constexpr int BQ = NW * WQ, BKV = 64, KS = D / 16, MT = D / 32, AH = 4;
+  constexpr int BQ = NW * WQ, BKV = 64, KS = D / 16, MT = D / 32;
   constexpr int NT = NW * 64;
-  constexpr int PER = 16 / KS;                 // elements per half handled per dP step
-  static_assert(NH == 1 || NH == 2, "32 or 64 query rows per wave");
   using KT = Tile<bf16, BKV, D>;
   struct __align__(16) Buf {
     bf16 k[KT::ELEMS];
@@ -446,7 +445,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
 
   const int qb = ib * BQ;
   const int qw = qb + wave * WQ;               // this wave's first query row
-  const LanePlan<D> plan(lane);
+  LanePlan<D> plan(lane);
   frag qf[NH][KS], of[NH][KS];
   // bias operands: ones[k] = 1 for k in {0, 1}; bl/bd[k] = (hi, lo) of the
   // lane's row scalar for k in {0, 1}; zero elsewhere (K slots 8h .. 8h + 7)
@@ -503,135 +502,144 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
     }
   };
 
-  // One key tile (two sub-tiles of 32 rows).  The operand stream of a
-  // sub-tile is K (head dim), V (head dim), K^T (positions); reads run AH
-  // operands ahead through the whole tile.
-  constexpr int OPS = 2 * KS + 2 * MT;          // operands per sub-tile
-  // Copy slot j (K for j < PER, then V) of the tile two steps ahead goes out
-  // inside the step, spread over the S and dP chains of both sub-tiles, into
-  // the buffer this step's barrier freed.
-  constexpr int NSLOT = 2 * FS::PER, SPC = NSLOT / 4;    // slots per chain
-  static_assert(NSLOT % 4 == 0 && KS % SPC == 0, "copy slots per chain");
+  // Operands of the 32 key rows at r0 of a tile: K along the head dim (S, in
+  // kf), V along the head dim (dP, in vf), K across positions (dQ, in tf).
+  // Per sub-tile the products run in chains (S and dP chains open with the
+  // row-scalar bias product):
+  //   S_0 | S_1 | dP_0 | dP_1 | dQ_0 | dQ_1        (index = query half)
+  // and every VALU stage reads a chain that finished at least one product
+  // earlier: exps of S_0 beside S_1, exps of S_1 beside dP_0, dS_0 beside
+  // dP_1, dS_1 beside dQ_0.  One operand read feeds the two halves' chains
+  // from registers.  V is read during S_1, K^T during dP_1 and dQ_0, and the
+  // next sub-tile's K during dQ_1, which runs after the next step's barrier
+  // for a tile's last sub-tile, so a tile starts on operands already read.
+  // The copies of the tile two steps ahead go out during the S_0 chains.
+  constexpr int NSLOT = 2 * FS::PER, SPS = NSLOT / 2;     // copy slots per tile, per sub-tile
+  static_assert(KS % SPS == 0, "copy slots per sub-tile");
+  static_assert(KS == 2 * MT, "one K fragment read per dQ_1 product");
+  static_assert(NH == 2, "two query halves per wave");
   auto copy_slot = [&](Buf& A, int k0, int j) ATTN_INLINE {
     if (j < FS::PER) async_fill_one_untracked<BKV, D, NW>(KT{A.k}, K + base + k0 * rs, copy_off, wave, j);
     else async_fill_one_untracked<BKV, D, NW>(KT{A.v}, V + base + k0 * rs, copy_off, wave, j - FS::PER);
   };
-  auto tile_body = [&](int kt, const Buf& B, bool masked, auto&& copy) ATTN_INLINE {
-    // slot of (sub-tile st, chain ch in {S, dP}, step kk), or -1
-    auto slot = [&](int st, int ch, int kk) ATTN_INLINE {
-      if (kk % (KS / SPC) == 0) copy(st * 2 * SPC + ch * SPC + kk / (KS / SPC));
-    };
-    auto opnd = [&](int n) ATTN_INLINE -> frag {
-      const int r0 = (n / OPS) * 32, m = n % OPS;
-      if (m < KS) return plan.cols(B.k, r0, m);
-      if (m < 2 * KS) return plan.cols(B.v, r0, m - KS);
-      const int i = m - 2 * KS;                   // (ss, mt) = (i / MT, i % MT)
-      return plan.rows(B.k, r0, i / MT, i % MT);
-    };
-    frag ring[AH];
+  frag kf[KS], vf[KS], tf[2 * MT], bds1[2];
+  // dQ_1 of the pending sub-tile (K^T in tf, dS_1 packed in bds1), reading the
+  // K fragments of the sub-tile at r0 of B beside it
+  auto dq_half1 = [&](const Buf& B, int r0) ATTN_INLINE {
 #pragma unroll
-    for (int n = 0; n < AH; ++n) ring[n] = opnd(n);
+    for (int i = 0; i < 2 * MT; ++i) {
+      mma_acc_agpr(acc[1][i % MT], tf[i], bds1[i / MT]);
+      kf[i] = plan.cols(B.k, r0, i);
+      fence();
+    }
+  };
+  auto mask_half = [&](f32x16& s, int c, int ka) ATTN_INLINE {
+    const int q = qw + 32 * c + l32;
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (ka + acc_row(r, h) > q) s[r] = 0.f;
+  };
+  // sub-tile st of B (key rows ka ..), K fragments already in kf; leaves
+  // dQ_1 pending in tf and bds1
+  auto sub = [&](const Buf& B, int st, int ka, bool masked, auto&& copy) ATTN_INLINE {
+    const int r0 = st * 32;
+    constexpr int E = 16 / KS;                  // elements per product in the exp and dS_0 stages
+    f32x16 sc[2], pc[2];
+    // S'_0^T = ones bl_0^T + K (c Q_0)^T
+    sc[0] = M::mma(ones, bl[0], zero16());
     fence();
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const int ka = kt * BKV + st * 32;          // absolute first key row of the sub-tile
-      const int n0 = st * OPS;
-      f32x16 sc[NH], pc[NH];
-      // S'^T = ones bl^T + K (c Q)^T
-#pragma unroll
-      for (int c = 0; c < NH; ++c) sc[c] = M::mma(ones, bl[c], zero16());
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
-        const int n = n0 + kk;
-        const frag a = ring[n % AH];
-        if (n + AH < 2 * OPS) ring[n % AH] = opnd(n + AH);
-#pragma unroll
-        for (int c = 0; c < NH; ++c) sc[c] = M::mma(a, qf[c][kk], sc[c]);
-        slot(st, 0, kk);
-        fence();
-      }
-      // dP'^T = ones bd^T + V dO^T | P = exp2(S') on the VALU
-#pragma unroll
-      for (int c = 0; c < NH; ++c) pc[c] = M::mma(ones, bd[c], zero16());
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
-        const int n = n0 + KS + kk;
-        const frag a = ring[n % AH];
-        if (n + AH < 2 * OPS) ring[n % AH] = opnd(n + AH);
-#pragma unroll
-        for (int c = 0; c < NH; ++c) pc[c] = M::mma(a, of[c][kk], pc[c]);
-        slot(st, 1, kk);
-#pragma unroll
-        for (int c = 0; c < NH; ++c)
-#pragma unroll
-          for (int e = 0; e < PER; ++e) {
-            const int r = kk * PER + e;
-            sc[c][r] = fast_exp2(sc[c][r]);
-          }
-        fence();
-      }
-      // causal element mask, only on tiles that cross the diagonal
-      if (CAUSAL && masked) {
-#pragma unroll
-        for (int c = 0; c < NH; ++c) {
-          const int q = qw + 32 * c + l32;
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (ka + acc_row(r, h) > q) sc[c][r] = 0.f;
-        }
-      }
+    for (int kk = 0; kk < KS; ++kk) {
+      sc[0] = M::mma(kf[kk], qf[0][kk], sc[0]);
+      if (kk % (KS / SPS) == 0) copy(st * SPS + kk / (KS / SPS));
       fence();
-      // dS = P o dP': half 0 now, half 1 (if any) under half 0's dQ products
-      frag bds[NH][2];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) pc[0][r] = sc[0][r] * pc[0][r];
-      bds[0][0] = M::pack(pc[0], 0);
-      bds[0][1] = M::pack(pc[0], 1);
-      pin_operand(bds[0][0]);
-      pin_operand(bds[0][1]);
-      mma_operand_guard();
-      fence();
-      frag t[2 * MT];
-      constexpr int PER3 = 16 / (2 * MT);
-#pragma unroll
-      for (int i = 0; i < 2 * MT; ++i) {
-        const int n = n0 + 2 * KS + i;
-        t[i] = ring[n % AH];
-        mma_acc_agpr(acc[0][i % MT], t[i], bds[0][i / MT]);
-        if (n + AH < 2 * OPS) ring[n % AH] = opnd(n + AH);
-        if constexpr (NH == 2) {
-#pragma unroll
-          for (int e = 0; e < PER3; ++e) {
-            const int r = i * PER3 + e;
-            pc[NH - 1][r] = sc[NH - 1][r] * pc[NH - 1][r];
-          }
-        }
-        fence();
-      }
-      if constexpr (NH == 2) {
-        bds[1][0] = M::pack(pc[1], 0);
-        bds[1][1] = M::pack(pc[1], 1);
-        pin_operand(bds[1][0]);
-        pin_operand(bds[1][1]);
-        mma_operand_guard();
-        fence();
-#pragma unroll
-        for (int i = 0; i < 2 * MT; ++i) mma_acc_agpr(acc[1][i % MT], t[i], bds[1][i / MT]);
-        fence();
-      }
     }
+    // S'_1 | P_0 = exp2(S'_0); V read
+    sc[1] = M::mma(ones, bl[1], zero16());
+    vf[0] = plan.cols(B.v, r0, 0);
+    fence();
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      sc[1] = M::mma(kf[kk], qf[1][kk], sc[1]);
+      if (kk + 1 < KS) vf[kk + 1] = plan.cols(B.v, r0, kk + 1);
+#pragma unroll
+      for (int e = 0; e < E; ++e) sc[0][kk * E + e] = fast_exp2(sc[0][kk * E + e]);
+      fence();
+    }
+    if (CAUSAL && masked) mask_half(sc[0], 0, ka);
+    // dP'_0 | P_1 = exp2(S'_1)
+    pc[0] = M::mma(ones, bd[0], zero16());
+    fence();
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      pc[0] = M::mma(vf[kk], of[0][kk], pc[0]);
+#pragma unroll
+      for (int e = 0; e < E; ++e) sc[1][kk * E + e] = fast_exp2(sc[1][kk * E + e]);
+      fence();
+    }
+    if (CAUSAL && masked) mask_half(sc[1], 1, ka);
+    // dP'_1 | dS_0 = P_0 o dP'_0, packed; first half of K^T read
+    pc[1] = M::mma(ones, bd[1], zero16());
+    fence();
+    frag bds0[2];
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      pc[1] = M::mma(vf[kk], of[1][kk], pc[1]);
+      if (kk % 2 == 0) tf[kk / 2] = plan.rows(B.k, r0, 0, kk / 2);
+#pragma unroll
+      for (int e = 0; e < E; ++e) pc[0][kk * E + e] = sc[0][kk * E + e] * pc[0][kk * E + e];
+      if (kk == KS / 2 - 1) {
+        bds0[0] = M::pack(pc[0], 0);
+        pin_operand(bds0[0]);
+      }
+      fence();
+    }
+    bds0[1] = M::pack(pc[0], 1);                // first read MT products into dQ_0
+    pin_operand(bds0[1]);
+    fence();
+    // dQ_0^T += K^T dS_0^T | dS_1 = P_1 o dP'_1 over products 1 .. 2 MT - 1;
+    // second half of K^T read MT products ahead of its use
+    constexpr int S3 = 2 * MT - 1;
+#pragma unroll
+    for (int i = 0; i < 2 * MT; ++i) {
+      mma_acc_agpr(acc[0][i % MT], tf[i], bds0[i / MT]);
+      if (i < MT) tf[MT + i] = plan.rows(B.k, r0, 1, i);
+      if (i > 0) {
+        const int lo = 16 * (i - 1) / S3, hi = 16 * i / S3;
+#pragma unroll
+        for (int r = lo; r < hi; ++r) pc[1][r] = sc[1][r] * pc[1][r];
+        if (lo < 8 && hi >= 8) {
+          bds1[0] = M::pack(pc[1], 0);
+          pin_operand(bds1[0]);
+        }
+      }
+      fence();
+    }
+    bds1[1] = M::pack(pc[1], 1);                // first read MT products into dQ_1
+    pin_operand(bds1[1]);
+    fence();
+  };
+  // One key tile: the pending dQ_1 of the previous tile while this tile's
+  // first K fragments are read, then both sub-tiles.  Before the first tile
+  // the pending products add zero (dS = 0), which keeps every step alike.
+  auto tile_body = [&](int kt, const Buf& B, bool masked, auto&& copy) ATTN_INLINE {
+    dq_half1(B, 0);
+    sub(B, 0, kt * BKV, masked, copy);
+    dq_half1(B, 32);
+    sub(B, 1, kt * BKV + 32, masked, copy);
   };
 
   // Key tiles are copied two steps ahead into a ring of three separately
-  // named buffers, picked statically (the loop is unrolled by three): step kt
-  // waits only for tile kt's copy and leaves tile kt + 1's in flight.  Tiles
-  // from diag0 on apply the causal element mask.
-  // tile kt + 1's copy may still fly, unless it went by the register path
-  // (the ragged last tile), which leaves nothing to count against
+  // named buffers, picked statically (the loops are unrolled by three): step
+  // kt waits only for tile kt's copy and leaves tile kt + 1's in flight
+  // (unless that one went by the register path, the ragged last tile, which
+  // leaves nothing to count against).  Tiles from diag0 on apply the causal
+  // element mask.
   auto step = [&](int kt, const Buf& cur, Buf& ahead) ATTN_INLINE {
     if (kt + 1 < ntiles && (kt + 2) * BKV <= N) wait_async_fills_but<2 * FS::PER>();
     else wait_async_fills();
     lds_barrier();
+    plan.rebind();
     const int k2 = (kt + 2) * BKV;
     const bool spread = kt + 2 < ntiles && k2 + BKV <= N;
     if (kt + 2 < ntiles && !spread) fill(ahead, kt + 2);     // ragged: register path now
@@ -644,9 +652,13 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
   auto step_inner = [&](int kt, const Buf& cur, Buf& ahead) ATTN_INLINE {
     wait_async_fills_but<2 * FS::PER>();
     lds_barrier();
+    plan.rebind();
     const int k2 = (kt + 2) * BKV;
     tile_body(kt, cur, false, [&](int j) ATTN_INLINE { copy_slot(ahead, k2, j); });
   };
+#pragma unroll
+  for (int i = 0; i < 2 * MT; ++i) tf[i] = frag{};
+  bds1[0] = bds1[1] = frag{};
   fill(buf0, 0);
   if (ntiles > 1) fill(buf1, 1);
   int kt = 0;
@@ -663,6 +675,12 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
   }
   if (kt < ntiles) step(kt, buf0, buf2);
   if (kt + 1 < ntiles) step(kt + 1, buf1, buf0);
+  // the last sub-tile's dQ_1
+#pragma unroll
+  for (int i = 0; i < 2 * MT; ++i) {
+    mma_acc_agpr(acc[1][i % MT], tf[i], bds1[i / MT]);
+    fence();
+  }
 
   mma_acc_drain(acc);
 #pragma unroll

@@ -242,6 +242,16 @@ template <int D> struct LanePlan {
       }
     }
   }
+  // Marks the offsets as changed here, so that the compiler cannot hoist
+  // (buffer base + offset) sums out of a loop over several statically named
+  // buffers (one register per buffer and offset); inside the loop the buffer
+  // base then folds into the read's immediate offset.
+  __device__ __forceinline__ void rebind() {
+#pragma unroll
+    for (int n = 0; n < D / 16; ++n) asm volatile("" : "+v"(col[n]));
+#pragma unroll
+    for (int mt = 0; mt < D / 32; ++mt) asm volatile("" : "+v"(tr[mt][0]), "+v"(tr[mt][1]));
+  }
   // operand with K slots along row r0 + l32 (r0 a multiple of 16), K step n
   __device__ __forceinline__ bf16x8 cols(const bf16* t, int r0, int n) const {
     return *reinterpret_cast<const bf16x8*>(t + col[n] + r0 * D);
