@@ -4,8 +4,9 @@ This module holds shapes, seeds and value recipes only: none of the attention
 arithmetic lives here, so the oracle and the HIP path can both draw from it
 without sharing any of the method.
 
-The five workloads stand in for the pages' own workloads (no dataset or
-trained weights exist for them):
+The first five workloads stand in for the pages' own workloads (no dataset
+or trained weights exist for them); two more take c5's shape beyond square
+causal attention:
 
 * ``c1_tiny``  -- the toy of ddx issue #217's repro script: 3 sequences, 2
   heads, 8 positions, 4 channels per head, scale 1/2, and Q/K/V filled with
@@ -19,6 +20,8 @@ trained weights exist for them):
   head dim 64, bf16 in / fp32 accumulate, scale 1/8 (1/sqrt(d); unstated).
 * ``c5_long`` -- 16,384 tokens as in issue #243 item 2, 16 heads, head dim 128,
   bf16 in / fp32 accumulate, scale 1/sqrt(128).
+* ``c5_full`` -- c5_long with full (non-causal) attention.
+* ``c5_ragged`` -- c5_long at 16,383 tokens, a length no tile size divides.
 
 Random draws use numpy's PCG64 ``default_rng(seed)`` in fp64, in the order
 Q, K, V, dO, each of shape [B, N, H, d]; Q/K/V are multiplied by ``qkv_std``.
@@ -66,6 +69,12 @@ WORKLOADS = (
              description="batch 4 x 16 heads x 1024 tokens x d 64, bf16"),
     Workload("c5_long", 1, 16, 16384, 128, 1.0 / math.sqrt(128), "bf16", qkv_std=0.5,
              description="1 x 16 heads x 16384 tokens x d 128, bf16"),
+    # c5's shape beyond square causal: full (non-causal) attention, and a
+    # length that no tile size divides (every walk ends on a ragged tile)
+    Workload("c5_full", 1, 16, 16384, 128, 1.0 / math.sqrt(128), "bf16", qkv_std=0.5,
+             causal=False, description="c5_long without the causal mask"),
+    Workload("c5_ragged", 1, 16, 16383, 128, 1.0 / math.sqrt(128), "bf16", qkv_std=0.5,
+             description="c5_long one token shorter: ragged last tile everywhere"),
 )
 
 

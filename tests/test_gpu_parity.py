@@ -164,16 +164,17 @@ def test_no_device_allocation_during_backward(B):
     assert abs(free1 - free0) < (2 << 20)
 
 
-def test_c5_full_size_sampled_against_oracle(B):
-    """N = 16,384, d = 128, bf16: sampled rows and columns of two heads."""
+@pytest.mark.parametrize("name", ["c5_long", "c5_full", "c5_ragged"])
+def test_c5_full_size_sampled_against_oracle(B, name):
+    """N = 16,384 (or 16,383), d = 128, bf16: sampled rows and columns of two heads."""
     import torch
-    w = workloads.get("c5_long")
-    _say("c5 inputs")
+    w = workloads.get(name)
+    _say(f"{name} inputs")
     x = workloads.make_inputs(w, seed=0)
     q, k, v, do = (_dev(x[n], w.dtype) for n in ("q", "k", "v", "do"))
-    _say("c5 forward + backward on the GPU")
-    o, lse = B.attn_fwd_lse(q, k, v, causal=True, scale=w.scale)
-    dq, dk, dv = B.attn_bwd(q, k, v, o, do, lse, causal=True, scale=w.scale)
+    _say(f"{name} forward + backward on the GPU")
+    o, lse = B.attn_fwd_lse(q, k, v, causal=w.causal, scale=w.scale)
+    dq, dk, dv = B.attn_bwd(q, k, v, o, do, lse, causal=w.causal, scale=w.scale)
     torch.cuda.synchronize()
     rng = np.random.default_rng(5)
     N = w.N
@@ -181,8 +182,8 @@ def test_c5_full_size_sampled_against_oracle(B):
     cols = np.unique(np.concatenate([[0, 1, 127, 128, 8191, 8192, N - 1], rng.integers(0, N, 40)]))
     errs = []
     for h in (0, 11):
-        _say(f"c5 oracle sample head {h}")
-        s = orc.attn_bwd_sampled(x["q"], x["k"], x["v"], x["do"], w.scale, True, 0, h, rows, cols,
+        _say(f"{name} oracle sample head {h}")
+        s = orc.attn_bwd_sampled(x["q"], x["k"], x["v"], x["do"], w.scale, w.causal, 0, h, rows, cols,
                                  row_block=1024)
         got_dq = dq[0, rows, h].float().cpu().numpy()
         got_o = o[0, rows, h].float().cpu().numpy()
@@ -201,4 +202,4 @@ def test_c5_full_size_sampled_against_oracle(B):
     sdk = dk.double().sum(dim=1).cpu().numpy()
     adk = dk.double().abs().sum(dim=1).cpu().numpy()
     assert np.all(np.abs(sdk) <= TOL["bf16"] * adk + 1e-6)
-    print("c5 sampled errors", errs, flush=True)
+    print(f"{name} sampled errors", errs, flush=True)
