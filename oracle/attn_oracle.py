@@ -25,7 +25,15 @@ Sources are the pages' titles and sections:
   and one saved number per row, m + log z, is enough to rebuild the scores.
 * ddx PR #162, "perf(ddx-ad): transpose causal attention's contractions
   without their joins", section "What changed": transpose p = w/z per score,
-  then p @ v (the plan jax.grad uses).
+  then p @ v (the plan jax.grad uses).  The same section describes a mask
+  that reads only grouping keys, so every row of a group passes or none does;
+  ``block_keep`` is that mask with groups of MASK_BLOCK query rows by
+  MASK_BLOCK key rows (a block-sparse mask), combined with the causal rule.
+
+A row whose every key is masked has no softmax.  Its output row is 0, its
+row scalar L is -inf and it adds nothing to any gradient (the limit of a row
+whose kept weights all tend to 0; the pages never produce such a row, since
+the causal rule keeps the diagonal).
 
 Everything here is the textbook definition materialised at N x N per
 (batch, head), in float64, so a reader can check each line against the
@@ -45,7 +53,10 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
+    "MASK_BLOCK",
     "causal_keep",
+    "block_keep",
+    "keep_mask",
     "scores",
     "masked_scores",
     "softmax_rows",
@@ -78,16 +89,41 @@ def causal_keep(n_q: int, n_k: int) -> np.ndarray:
     return j <= i
 
 
+MASK_BLOCK = 128   # query rows and key rows per block of a block-sparse mask
+
+
+def block_keep(n_q: int, n_k: int, block_mask, mask_block: int = MASK_BLOCK) -> np.ndarray:
+    """Element keep-mask of a block mask: keep[i, j] iff block_mask[i // mb, j // mb] != 0.
+
+    PR #162, "What changed": a filter on grouping keys passes a whole group of
+    rows or none of it; here a group is a mask_block x mask_block block.
+    """
+    bm = np.asarray(block_mask) != 0
+    bi = np.arange(n_q) // mask_block
+    bj = np.arange(n_k) // mask_block
+    return bm[bi[:, None], bj[None, :]]
+
+
+def keep_mask(n_q: int, n_k: int, causal: bool, block_mask=None,
+              mask_block: int = MASK_BLOCK) -> np.ndarray:
+    """Pairs kept: the causal rule (if causal) and the block mask (if given)."""
+    keep = causal_keep(n_q, n_k) if causal else np.ones((n_q, n_k), dtype=bool)
+    if block_mask is not None:
+        keep = keep & block_keep(n_q, n_k, block_mask, mask_block)
+    return keep
+
+
 def scores(q: np.ndarray, k: np.ndarray, scale: float) -> np.ndarray:
     """S[i, j] = scale * sum_c q[i, c] k[j, c]  (issue #217 repro, CTE ``scores``)."""
     return scale * (q @ k.T)
 
 
-def masked_scores(q: np.ndarray, k: np.ndarray, scale: float, causal: bool) -> np.ndarray:
+def masked_scores(q: np.ndarray, k: np.ndarray, scale: float, causal: bool,
+                  block_mask=None, mask_block: int = MASK_BLOCK) -> np.ndarray:
     """Scores with masked-out pairs set to -inf (absent rows in the SQL spelling)."""
     s = scores(q, k, scale)
-    if causal:
-        s = np.where(causal_keep(s.shape[0], s.shape[1]), s, -np.inf)
+    if causal or block_mask is not None:
+        s = np.where(keep_mask(s.shape[0], s.shape[1], causal, block_mask, mask_block), s, -np.inf)
     return s
 
 
@@ -95,26 +131,37 @@ def softmax_rows(s: np.ndarray):
     """Row max m, shifted weights w = exp(s - m), normaliser z = sum_j w.
 
     Issue #217 repro, CTEs ``weights`` (exp of the score minus the row MAX
-    window) and ``norm`` (SUM of the weights per row).  -inf scores give w = 0.
+    window) and ``norm`` (SUM of the weights per row).  -inf scores give w = 0;
+    a row of -inf scores (no kept key) has m = -inf, w = 0 and z = 0.
     """
     m = s.max(axis=1)
-    w = np.exp(s - m[:, None])
+    m_shift = np.where(np.isfinite(m), m, 0.0)
+    w = np.exp(s - m_shift[:, None])
     z = w.sum(axis=1)
     return m, w, z
 
 
-def head_forward(q, k, v, scale: float, causal: bool):
+def _normalise(m, w, z):
+    """P = w / z and L = m + log z; a row with z = 0 gets P = 0 and L = -inf."""
+    live = z > 0
+    p = np.divide(w, z[:, None], out=np.zeros_like(w), where=live[:, None])
+    with np.errstate(divide="ignore"):
+        lse = np.where(live, m + np.log(np.where(live, z, 1.0)), -np.inf)
+    return p, lse
+
+
+def head_forward(q, k, v, scale: float, causal: bool, block_mask=None,
+                 mask_block: int = MASK_BLOCK):
     """One (batch, head): O = (w / z) V and the saved row scalar L = m + log z.
 
     O follows the CTE ``heads`` of the issue #217 repro; L is the one number per
     row that issue #243 (item 2) names as enough to rebuild the scores.
     Returns O [N, d], L [N], P [N, N].
     """
-    s = masked_scores(q, k, scale, causal)
+    s = masked_scores(q, k, scale, causal, block_mask, mask_block)
     m, w, z = softmax_rows(s)
-    p = w / z[:, None]
+    p, lse = _normalise(m, w, z)
     o = p @ v
-    lse = m + np.log(z)
     return o, lse, p
 
 
@@ -142,12 +189,13 @@ def grad_q_k(ds: np.ndarray, q: np.ndarray, k: np.ndarray, scale: float):
     return dq, dk
 
 
-def head_backward(q, k, v, do, scale: float, causal: bool):
+def head_backward(q, k, v, do, scale: float, causal: bool, block_mask=None,
+                  mask_block: int = MASK_BLOCK):
     """Exact gradient of sum(dO o O) for one (batch, head), every table materialised.
 
     Returns dQ, dK, dV [N, d], D [N], dS row sums [N], P [N, N].
     """
-    _, _, p = head_forward(q, k, v, scale, causal)
+    _, _, p = head_forward(q, k, v, scale, causal, block_mask, mask_block)
     dv = p.T @ do                      # p @ v transposed against the output cotangent
     dp = do @ v.T                      # dP = dO V^T (issue #243, item 2)
     ds, d = softmax_backward(p, dp)
@@ -187,21 +235,35 @@ def _f64(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64)
 
 
-def attn_fwd(Q, K, V, scale: float, causal: bool = True):
-    """O [B, N, H, d] and L [B, H, N] (natural log) for every (batch, head)."""
+def _head_mask(block_mask, b, h):
+    """The [nb, nb] block mask of (b, h): one shared mask, or one per (b, h)."""
+    if block_mask is None:
+        return None
+    bm = np.asarray(block_mask)
+    return bm if bm.ndim == 2 else bm[b, h]
+
+
+def attn_fwd(Q, K, V, scale: float, causal: bool = True, block_mask=None,
+             mask_block: int = MASK_BLOCK):
+    """O [B, N, H, d] and L [B, H, N] (natural log) for every (batch, head).
+
+    block_mask: None, [nb, nb] (shared) or [B, H, nb, nb], nb = ceil(N / mask_block).
+    """
     Q, K, V = _f64(Q), _f64(K), _f64(V)
     B, N, H, _ = Q.shape
     O = np.empty_like(V)
     L = np.empty((B, H, N))
     for b in range(B):
         for h in range(H):
-            o, lse, _ = head_forward(Q[b, :, h], K[b, :, h], V[b, :, h], scale, causal)
+            o, lse, _ = head_forward(Q[b, :, h], K[b, :, h], V[b, :, h], scale, causal,
+                                     _head_mask(block_mask, b, h), mask_block)
             O[b, :, h] = o
             L[b, h] = lse
     return O, L
 
 
-def attn_bwd(Q, K, V, dO, scale: float, causal: bool = True):
+def attn_bwd(Q, K, V, dO, scale: float, causal: bool = True, block_mask=None,
+             mask_block: int = MASK_BLOCK):
     """dQ, dK, dV [B, N, H, d] plus diagnostics D and dS row sums [B, H, N]."""
     Q, K, V, dO = _f64(Q), _f64(K), _f64(V), _f64(dO)
     B, N, H, _ = Q.shape
@@ -213,14 +275,16 @@ def attn_bwd(Q, K, V, dO, scale: float, causal: bool = True):
     for b in range(B):
         for h in range(H):
             dq, dk, dv, d, dsr, _ = head_backward(
-                Q[b, :, h], K[b, :, h], V[b, :, h], dO[b, :, h], scale, causal)
+                Q[b, :, h], K[b, :, h], V[b, :, h], dO[b, :, h], scale, causal,
+                _head_mask(block_mask, b, h), mask_block)
             dQ[b, :, h], dK[b, :, h], dV[b, :, h] = dq, dk, dv
             D[b, h], ds_rows[b, h] = d, dsr
     return {"dQ": dQ, "dK": dK, "dV": dV, "D": D, "dS_rowsum": ds_rows}
 
 
 def attn_bwd_sampled(Q, K, V, dO, scale: float, causal: bool, b: int, h: int,
-                     rows, cols, row_block: int = 512):
+                     rows, cols, row_block: int = 512, block_mask=None,
+                     mask_block: int = MASK_BLOCK):
     """Selected outputs of one (b, h) without any N x N array.
 
     dQ and O are returned for the query rows ``rows``; dK and dV for the key
@@ -236,17 +300,25 @@ def attn_bwd_sampled(Q, K, V, dO, scale: float, causal: bool, b: int, h: int,
     rows = np.asarray(rows, dtype=np.int64)
     cols = np.asarray(cols, dtype=np.int64)
 
-    def row_stats(r0, r1):
-        s = scale * (q[r0:r1] @ k.T)
+    bm = _head_mask(block_mask, b, h)
+
+    def keep_rows(r0, r1):
+        # the kept pairs of query rows r0 .. r1 - 1, every key
+        keep = np.ones((r1 - r0, n), dtype=bool)
         if causal:
-            s = np.where(np.arange(n)[None, :] <= np.arange(r0, r1)[:, None], s, -np.inf)
-        m = s.max(axis=1)
-        w = np.exp(s - m[:, None])
-        z = w.sum(axis=1)
-        p = w / z[:, None]
+            keep &= np.arange(n)[None, :] <= np.arange(r0, r1)[:, None]
+        if bm is not None:
+            keep &= (np.asarray(bm) != 0)[(np.arange(r0, r1) // mask_block)[:, None],
+                                          (np.arange(n) // mask_block)[None, :]]
+        return keep
+
+    def row_stats(r0, r1):
+        s = np.where(keep_rows(r0, r1), scale * (q[r0:r1] @ k.T), -np.inf)
+        m, w, z = softmax_rows(s)
+        p, lse = _normalise(m, w, z)
         dp = do[r0:r1] @ v.T
         d = (p * dp).sum(axis=1)
-        return m + np.log(z), d, p, dp
+        return lse, d, p, dp
 
     # per-row scalars L and D for all rows
     L = np.empty(n)
@@ -268,11 +340,16 @@ def attn_bwd_sampled(Q, K, V, dO, scale: float, causal: bool, b: int, h: int,
 
     dk = np.empty((cols.size, k.shape[1]))
     dv = np.empty((cols.size, v.shape[1]))
+    live = np.isfinite(L)                                # rows with a kept key
     for t, j in enumerate(cols):
         s_col = scale * (q @ k[j])                       # S[:, j]
-        p_col = np.exp(s_col - L)                        # P[:, j] = exp(S - L)
+        keep = live.copy()
         if causal:
-            p_col = np.where(np.arange(n) >= j, p_col, 0.0)
+            keep &= np.arange(n) >= j
+        if bm is not None:
+            keep &= (np.asarray(bm) != 0)[np.arange(n) // mask_block, j // mask_block]
+        # P[:, j] = exp(S - L) on kept pairs
+        p_col = np.exp(np.where(keep, s_col - np.where(live, L, 0.0), -np.inf))
         dp_col = do @ v[j]                               # dP[:, j]
         ds_col = p_col * (dp_col - D)
         dv[t] = p_col @ do
