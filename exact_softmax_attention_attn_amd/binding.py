@@ -19,6 +19,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libattn.so")
 
 ATTN_F32, ATTN_BF16 = 0, 1
+ATTN_MASK_BLOCK = 128
 ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
 
 _P = ctypes.c_void_p
@@ -32,6 +33,9 @@ _SIGNATURES = {
     "attn_bwd_preprocess": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "attn_bwd_dkdv": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
     "attn_bwd_dq": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "attn_fwd_lse_masked": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "attn_bwd_masked": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I,
+                             _I, _I, _I, _I, _I, _F, _I, _P]),
     "attn_status_string": (ctypes.c_char_p, [_I]),
     "attn_last_error": (ctypes.c_char_p, []),
 }
@@ -99,6 +103,20 @@ def _check_rows(t: torch.Tensor, B: int, H: int, N: int, device, lead=()):
     if t.dtype != torch.float32 or tuple(t.shape) != shape or not t.is_contiguous() \
             or t.device != device:
         raise ValueError(f"expected a contiguous float32 {shape} tensor on {device}")
+
+
+def _mask_arg(mask: torch.Tensor, B: int, H: int, N: int, device):
+    """A block mask tensor -> (pointer, mask_heads).  uint8 or bool, contiguous,
+    [nb, nb] (shared by every (b, h)) or [B, H, nb, nb], nb = ceil(N / 128)."""
+    nb = (N + ATTN_MASK_BLOCK - 1) // ATTN_MASK_BLOCK
+    if mask.dtype not in (torch.uint8, torch.bool) or not mask.is_contiguous() \
+            or mask.device != device:
+        raise ValueError(f"mask must be a contiguous uint8 or bool tensor on {device}")
+    if tuple(mask.shape) == (nb, nb):
+        return ctypes.c_void_p(mask.data_ptr()), 1
+    if tuple(mask.shape) == (B, H, nb, nb):
+        return ctypes.c_void_p(mask.data_ptr()), B * H
+    raise ValueError(f"mask must be [{nb}, {nb}] or [{B}, {H}, {nb}, {nb}]")
 
 
 def new_workspace(B: int, H: int, N: int, device) -> torch.Tensor:
@@ -188,3 +206,41 @@ def attn_bwd_dq(q, k, v, do, workspace, dq, causal: bool = True, scale: float | 
         _call("attn_bwd_dq", _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(workspace),
               _ptr(dq), B, H, N, d, int(bool(causal)), scale, _dtype_code(q), _stream(q.device))
     return dq
+
+
+def attn_fwd_lse_masked(q, k, v, mask, causal: bool = True, scale: float | None = None,
+                        o=None, lse=None):
+    """attn_fwd_lse over the pairs a block mask keeps (rows keeping no key: O = 0, L = -inf)."""
+    _check_bnhd(q, k, v)
+    B, N, H, d = q.shape
+    scale = default_scale(d) if scale is None else float(scale)
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_bnhd(q, o)
+    _check_rows(lse, B, H, N, q.device)
+    mp, mh = _mask_arg(mask, B, H, N, q.device)
+    with torch.cuda.device(q.device):
+        _call("attn_fwd_lse_masked", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), mp, mh,
+              B, H, N, d, int(bool(causal)), scale, _dtype_code(q), _stream(q.device))
+    return o, lse
+
+
+def attn_bwd_masked(q, k, v, o, do, lse, mask, causal: bool = True, scale: float | None = None,
+                    dq=None, dk=None, dv=None, workspace=None):
+    """attn_bwd over the pairs a block mask keeps; lse from attn_fwd_lse_masked (same mask)."""
+    _check_bnhd(q, k, v, o, do)
+    B, N, H, d = q.shape
+    _check_rows(lse, B, H, N, q.device)
+    scale = default_scale(d) if scale is None else float(scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    _check_bnhd(q, dq, dk, dv)
+    workspace = new_workspace(B, H, N, q.device) if workspace is None else workspace
+    _check_rows(workspace, B, H, N, q.device, lead=(2,))
+    mp, mh = _mask_arg(mask, B, H, N, q.device)
+    with torch.cuda.device(q.device):
+        _call("attn_bwd_masked", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse),
+              _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), mp, mh, B, H, N, d,
+              int(bool(causal)), scale, _dtype_code(q), _stream(q.device))
+    return dq, dk, dv

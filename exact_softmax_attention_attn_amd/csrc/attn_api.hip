@@ -58,6 +58,15 @@ int check_ptrs(std::initializer_list<const void*> ps) {
   return ATTN_OK;
 }
 
+// Block masks: a mask given, one per (b, h) or one shared; the walks' visit
+// lists hold up to 1024 tiles of 64 rows.
+int check_mask(const unsigned char* mask, int mask_heads, int B, int H, int N) {
+  if (mask == nullptr) return ATTN_ERR_INVALID;
+  if (mask_heads != 1 && (int64_t)mask_heads != (int64_t)B * H) return ATTN_ERR_INVALID;
+  if (N > 65536) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
 #define ATTN_TRY(expr)           \
   do {                           \
     const int st_ = (expr);      \
@@ -90,6 +99,22 @@ int attn_fwd_lse(const void* Q, const void* K, const void* V, void* O, float* L,
   a.Q = Q; a.K = K; a.V = V; a.O = O; a.L = L;
   a.B = B; a.H = H; a.N = N; a.d = d;
   a.causal = causal; a.scale = scale; a.dtype = dtype;
+  return finish(attn::launch_fwd_lse(a, static_cast<hipStream_t>(stream)));
+}
+
+int attn_fwd_lse_masked(const void* Q, const void* K, const void* V, void* O, float* L,
+                        const unsigned char* mask, int mask_heads, int B, int H, int N, int d,
+                        int causal, float scale, int dtype, void* stream) {
+  ATTN_TRY(check_ptrs({Q, K, V, O, L}));
+  ATTN_TRY(check_sizes(B, H, N, d));
+  ATTN_TRY(check_scale_causal(scale, causal));
+  ATTN_TRY(check_dtype_dim(d, dtype));
+  ATTN_TRY(check_mask(mask, mask_heads, B, H, N));
+  attn::FwdArgs a;
+  a.Q = Q; a.K = K; a.V = V; a.O = O; a.L = L;
+  a.B = B; a.H = H; a.N = N; a.d = d;
+  a.causal = causal; a.scale = scale; a.dtype = dtype;
+  a.mask = mask; a.mask_heads = mask_heads;
   return finish(attn::launch_fwd_lse(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -144,6 +169,28 @@ int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const v
   if (e != hipSuccess) return finish(e);
   const attn::BwdArgs a =
       make_bwd(Q, K, V, dO, workspace, dQ, dK, dV, B, H, N, d, causal, scale, dtype);
+  e = attn::launch_bwd_dkdv(a, s);
+  if (e != hipSuccess) return finish(e);
+  return finish(attn::launch_bwd_dq(a, s));
+}
+
+int attn_bwd_masked(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                    const float* L, void* dQ, void* dK, void* dV, void* workspace,
+                    const unsigned char* mask, int mask_heads, int B, int H, int N, int d,
+                    int causal, float scale, int dtype, void* stream) {
+  ATTN_TRY(check_ptrs({Q, K, V, O, dO, L, dQ, dK, dV, workspace}));
+  ATTN_TRY(check_sizes(B, H, N, d));
+  ATTN_TRY(check_scale_causal(scale, causal));
+  ATTN_TRY(check_dtype_dim(d, dtype));
+  ATTN_TRY(check_mask(mask, mask_heads, B, H, N));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = attn::launch_bwd_preprocess(O, dO, L, static_cast<float*>(workspace), B, H, N,
+                                             d, dtype, s);
+  if (e != hipSuccess) return finish(e);
+  attn::BwdArgs a =
+      make_bwd(Q, K, V, dO, workspace, dQ, dK, dV, B, H, N, d, causal, scale, dtype);
+  a.mask = mask;
+  a.mask_heads = mask_heads;
   e = attn::launch_bwd_dkdv(a, s);
   if (e != hipSuccess) return finish(e);
   return finish(attn::launch_bwd_dq(a, s));

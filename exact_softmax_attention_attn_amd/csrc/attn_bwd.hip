@@ -62,7 +62,8 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(const T* __restrict
     const int b = (int)(bn / N);
     const long i = ((long)b * H + h) * N + n;
     Dout[i] = -acc;
-    L2out[i] = -L[i] * kLog2e;
+    // a row with no kept key (L = -inf) stores -inf, so every P of it is 0
+    L2out[i] = L[i] == -__builtin_inff() ? -__builtin_inff() : -L[i] * kLog2e;
   }
 }
 
@@ -81,7 +82,8 @@ template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dws,
-    T* __restrict__ dK, T* __restrict__ dV, int H, int N, int d, float scale_log2, float scale) {
+    T* __restrict__ dK, T* __restrict__ dV, int H, int N, int d, float scale_log2, float scale,
+    const unsigned char* __restrict__ mask, int mask_heads) {
   using M = Mma<T>;
   using frag = typename M::frag;
   constexpr int BKV = 128, BQ = 64, KS = D / M::K, MT = D / 32, RS = 32 / M::K;
@@ -115,6 +117,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 
   const int nqt = (N + BQ - 1) / BQ;
   const int qt0 = CAUSAL ? kvb / BQ : 0;
+  // the walk: query tiles qt0 .. nqt - 1, or (block-sparse mask) the ones whose
+  // mask block (row of the tile, column jb of this key block) is kept
+  __shared__ unsigned short vis[kMaxVisit];
+  __shared__ int nvis;
+  int ntiles = nqt - qt0;
+  if (mask) {
+    const int nb = (N + kMaskBlock - 1) / kMaskBlock;
+    const unsigned char* mk = head_mask(mask, mask_heads, b, head, H, nb);
+    ntiles = build_visits(vis, &nvis, ntiles, [&](int i) ATTN_INLINE -> unsigned {
+      const int t = qt0 + i;
+      return mk[(t * BQ / kMaskBlock) * nb + jb] ? (1u << 14) | (unsigned)t : 0u;
+    });
+  }
+  auto tile_at = [&](int p) ATTN_INLINE -> int {
+    return mask ? (int)(visit_entry(vis, p) & kVisitTile) : qt0 + p;
+  };
 
   auto fill = [&](Buf& B, int qt) ATTN_INLINE {
     const int q0 = qt * BQ;
@@ -194,9 +212,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     }
   };
 
-  auto step = [&](const Buf& cur, Buf& nxt, int qt) ATTN_INLINE {
-    if (qt + 1 < nqt) fill(nxt, qt + 1);
-    const int q0 = qt * BQ;
+  // step p: tile tile_at(p) in cur while tile tile_at(p + 1) is copied to nxt
+  auto step = [&](const Buf& cur, Buf& nxt, int p) ATTN_INLINE {
+    const int q0 = tile_at(p) * BQ;
+    if (p + 1 < ntiles) fill(nxt, tile_at(p + 1));
     if (CAUSAL && q0 < kvb + BKV)
       body(cur, q0, bool_c<true>{});
     else
@@ -205,12 +224,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     __syncthreads();
   };
 
-  fill(bufA, qt0);
-  wait_async_fills();
-  __syncthreads();
-  for (int qt = qt0; qt < nqt; qt += 2) {
-    step(bufA, bufB, qt);
-    if (qt + 1 < nqt) step(bufB, bufA, qt + 1);
+  if (ntiles > 0) {                               // a sparse walk may visit nothing
+    fill(bufA, tile_at(0));
+    wait_async_fills();
+    __syncthreads();
+  }
+  for (int p = 0; p < ntiles; p += 2) {
+    step(bufA, bufB, p);
+    if (p + 1 < ntiles) step(bufB, bufA, p + 1);
   }
 
 #pragma unroll
@@ -232,7 +253,8 @@ template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dws,
-    T* __restrict__ dQ, int H, int N, int d, float scale_log2, float scale) {
+    T* __restrict__ dQ, int H, int N, int d, float scale_log2, float scale,
+    const unsigned char* __restrict__ mask, int mask_heads) {
   using M = Mma<T>;
   using frag = typename M::frag;
   constexpr int BQ = 128, BKV = 64, KS = D / M::K, MT = D / 32, RS = 32 / M::K;
@@ -268,6 +290,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
 
   const int kv_end = CAUSAL ? min(N, qb + BQ) : N;
   const int nkt = (kv_end + BKV - 1) / BKV;
+  // the walk: key tiles 0 .. nkt - 1, or (block-sparse mask) the ones whose
+  // mask block (row ib of this query block, column of the tile) is kept
+  __shared__ unsigned short vis[kMaxVisit];
+  __shared__ int nvis;
+  int ntiles = nkt;
+  if (mask) {
+    const int nb = (N + kMaskBlock - 1) / kMaskBlock;
+    const unsigned char* mk = head_mask(mask, mask_heads, b, head, H, nb);
+    ntiles = build_visits(vis, &nvis, nkt, [&](int t) ATTN_INLINE -> unsigned {
+      return mk[ib * nb + t * BKV / kMaskBlock] ? (1u << 14) | (unsigned)t : 0u;
+    });
+  }
+  auto tile_at = [&](int p) ATTN_INLINE -> int {
+    return mask ? (int)(visit_entry(vis, p) & kVisitTile) : p;
+  };
 
   auto fill = [&](Buf& B, int kt) ATTN_INLINE {
     const int k0 = kt * BKV;
@@ -317,9 +354,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
     }
   };
 
-  auto step = [&](const Buf& cur, Buf& nxt, int kt) ATTN_INLINE {
-    if (kt + 1 < nkt) fill(nxt, kt + 1);
-    const int k0 = kt * BKV;
+  // step p: tile tile_at(p) in cur while tile tile_at(p + 1) is copied to nxt
+  auto step = [&](const Buf& cur, Buf& nxt, int p) ATTN_INLINE {
+    const int k0 = tile_at(p) * BKV;
+    if (p + 1 < ntiles) fill(nxt, tile_at(p + 1));
     if (CAUSAL && k0 + BKV - 1 > qb)
       body(cur, k0, bool_c<true>{});
     else
@@ -328,12 +366,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
     __syncthreads();
   };
 
-  fill(bufA, 0);
-  wait_async_fills();
-  __syncthreads();
-  for (int kt = 0; kt < nkt; kt += 2) {
-    step(bufA, bufB, kt);
-    if (kt + 1 < nkt) step(bufB, bufA, kt + 1);
+  if (ntiles > 0) {                               // a sparse walk may visit nothing
+    fill(bufA, tile_at(0));
+    wait_async_fills();
+    __syncthreads();
+  }
+  for (int p = 0; p < ntiles; p += 2) {
+    step(bufA, bufB, p);
+    if (p + 1 < ntiles) step(bufB, bufA, p + 1);
   }
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
@@ -369,7 +409,7 @@ static hipError_t dkdv_go(const BwdArgs& a, hipStream_t stream) {
                      static_cast<const T*>(a.Q), static_cast<const T*>(a.K),
                      static_cast<const T*>(a.V), static_cast<const T*>(a.dO), a.Dws + rows_of(a), a.Dws,
                      static_cast<T*>(a.dK), static_cast<T*>(a.dV), a.H, a.N, a.d,
-                     a.scale * kLog2e, a.scale);
+                     a.scale * kLog2e, a.scale, a.mask, a.mask_heads);
   return hipGetLastError();
 }
 
@@ -379,7 +419,8 @@ static hipError_t dq_go(const BwdArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((bwd_dq_kernel<T, D, C>), grid, dim3(256), 0, stream,
                      static_cast<const T*>(a.Q), static_cast<const T*>(a.K),
                      static_cast<const T*>(a.V), static_cast<const T*>(a.dO), a.Dws + rows_of(a), a.Dws,
-                     static_cast<T*>(a.dQ), a.H, a.N, a.d, a.scale * kLog2e, a.scale);
+                     static_cast<T*>(a.dQ), a.H, a.N, a.d, a.scale * kLog2e, a.scale, a.mask,
+                     a.mask_heads);
   return hipGetLastError();
 }
 

@@ -46,14 +46,16 @@ __device__ __forceinline__ f32x4 lds_f32x4(const float* p) {
 // dV^T += dO^T P and dK^T += Q^T dS accumulate in AGPRs (asm MFMA).  The
 // operand reads (Q, dO along the head dim; dO, Q across positions) run AH
 // fragments ahead through a whole 64-row query tile.  Causal: only the two
-// tiles on the diagonal carry the element mask.
+// tiles on the diagonal carry the element mask.  SPARSE: the walk visits only
+// the query tiles whose mask block (row of the tile, column of this key
+// block) is kept.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ nL2, const float* __restrict__ nD,
     bf16* __restrict__ dK, bf16* __restrict__ dV, int H, int N, int d, float scale_log2,
-    float scale) {
+    float scale, const unsigned char* __restrict__ mask, int mask_heads) {
   using M = Mma<bf16>;
   using frag = bf16x8;
   constexpr int BKV = 128, BQ = 64, KS = D / 16, MT = D / 32, AH = 4;
@@ -100,7 +102,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
 
   const int nqt = (N + BQ - 1) / BQ;
   const int qt0 = CAUSAL ? kvb / BQ : 0;
-  const int ntiles = nqt - qt0;
+  int ntiles = nqt - qt0;
+  // block-sparse: the kept query tiles, last first (this key block is mask
+  // column jb, a query tile of 64 rows lies in one mask row)
+  __shared__ unsigned short vis[SPARSE ? kMaxVisit : 1];
+  __shared__ int nvis;
+  if constexpr (SPARSE) {
+    const int nb = (N + kMaskBlock - 1) / kMaskBlock;
+    const unsigned char* mk = head_mask(mask, mask_heads, b, head, H, nb);
+    ntiles = build_visits(vis, &nvis, ntiles, [&](int i) ATTN_INLINE -> unsigned {
+      const int t = nqt - 1 - i;
+      return mk[(t * BQ / kMaskBlock) * nb + jb] ? (1u << 14) | (unsigned)t : 0u;
+    });
+  }
 
   unsigned copy_off[AsyncFillShape<BQ, D>::PER];
   async_fill_plan<BQ, D>(copy_off, rs, wave, lane);
@@ -110,14 +124,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
   // be the sequence's ragged last one: register path with zero padding.
   using FS = AsyncFillShape<BQ, D>;
   auto fill_whole = [&](Buf& B, int t) ATTN_INLINE {
-    const int q0 = (qt0 + t) * BQ;
+    const int q0 = t * BQ;
     async_fill_untracked<BQ, D>(QT{B.q}, Q + base + q0 * rs, copy_off, wave);
     async_fill_untracked<BQ, D>(QT{B.o}, dO + base + q0 * rs, copy_off, wave);
     if (wave == 0) fill_row64_untracked(B.l, Lh + q0, lane);
     if (wave == 1) fill_row64_untracked(B.dd, Dh + q0, lane);
   };
   auto fill = [&](Buf& B, int t) ATTN_INLINE {
-    const int q0 = (qt0 + t) * BQ;
+    const int q0 = t * BQ;
     if (q0 + BQ <= N) {
       fill_whole(B, t);
     } else {
@@ -208,7 +222,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     // the next operand goes out after the product, not before it; the last
     // refills fetch the next step's first operands
     auto refill = [&](int n) ATTN_INLINE { ring[n % AH] = opnd(n + AH); };
-    const int qa = (qt0 + t) * BQ;               // absolute first query row of the tile
+    const int qa = t * BQ;                       // first query row of the tile
     constexpr int E = 8 / L;                     // exps per product (half a sub-tile per chain)
     constexpr int M2 = 16 / L;                   // dS multiplies per product
     auto s_chain = [&](int c, f32x16& acc) ATTN_INLINE {
@@ -337,23 +351,29 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
   // Walk the query tiles from the last one back to the diagonal: every block
   // of a head starts on the same tiles at the same time, so they are shared
   // in L2 instead of each block streaming its own stretch.  Step k visits
-  // tile ntiles - 1 - k; causal: the last two steps (the diagonal tiles,
-  // BKV = 2 BQ) apply the element mask.  Tiles are copied two steps ahead
+  // tile tile_of(k) (nqt - 1 - k, or entry k of the visit list); causal: the
+  // diagonal tiles (BKV = 2 BQ), the walk's last two steps when they are
+  // visited, apply the element mask.  Tiles are copied two steps ahead
   // into a ring of four separately named buffers picked statically (the loop
   // is unrolled by four): a step reads its own tile and the previous one, and
   // a copy has two steps to land, so step k waits only for tile k's copy,
   // leaving tile k + 1's in flight.  A runtime choice between buffers would
   // make the compiler shuffle the accumulators between registers while
   // products are in flight.
-  auto tile_of = [&](int k) ATTN_INLINE { return ntiles - 1 - k; };
+  auto tile_of = [&](int k) ATTN_INLINE -> int {
+    if constexpr (SPARSE) return wave_uniform(vis[k] & kVisitTile);
+    else return nqt - 1 - k;
+  };
   frag bpp[2], bdsp[2], ring[AH];
   auto step = [&](auto has_prev, int k, const Buf& cur, const Buf& prv, Buf& ahead) ATTN_INLINE {
     if (k + 1 < ntiles) wait_async_fills_but<2 * FS::PER>();   // tile k + 1's copy may fly
     else wait_async_fills();
     lds_barrier();
     const bool ahead_on = k + 2 < ntiles;
-    const int qn = (qt0 + tile_of(k + 2)) * BQ;
-    step_body(has_prev, tile_of(k), cur, prv, CAUSAL && k + 2 >= ntiles, bpp, bdsp, ring,
+    const int qn = ahead_on ? tile_of(k + 2) * BQ : 0;
+    const int t = tile_of(k);
+    const bool masked = CAUSAL && (SPARSE ? t * BQ < kvb + BKV : k + 2 >= ntiles);
+    step_body(has_prev, t, cur, prv, masked, bpp, bdsp, ring,
               [&](int j) ATTN_INLINE { if (ahead_on) copy_slot(ahead, qn, j); });
   };
   // Steps at least two ahead of the last are unmasked and have two tiles
@@ -362,26 +382,26 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
   auto step_inner = [&](int k, const Buf& cur, const Buf& prv, Buf& ahead) ATTN_INLINE {
     wait_async_fills_but<2 * FS::PER>();
     lds_barrier();
-    const int qn = (qt0 + tile_of(k + 2)) * BQ;
+    const int qn = tile_of(k + 2) * BQ;
     step_body(bool_c<true>{}, tile_of(k), cur, prv, false, bpp, bdsp, ring,
               [&](int j) ATTN_INLINE { copy_slot(ahead, qn, j); });
   };
-  fill(buf0, tile_of(0));
-  if (ntiles > 1) fill_whole(buf1, tile_of(1));
-  step(bool_c<false>{}, 0, buf0, buf3, buf2);
-  int k = 1;
-  for (; k + 6 <= ntiles; k += 4) {
-    step_inner(k, buf1, buf0, buf3);
-    step_inner(k + 1, buf2, buf1, buf0);
-    step_inner(k + 2, buf3, buf2, buf1);
-    step_inner(k + 3, buf0, buf3, buf2);
-  }
-  if (k < ntiles) step(bool_c<true>{}, k, buf1, buf0, buf3);
-  if (k + 1 < ntiles) step(bool_c<true>{}, k + 1, buf2, buf1, buf0);
-  if (k + 2 < ntiles) step(bool_c<true>{}, k + 2, buf3, buf2, buf1);
-  if (k + 3 < ntiles) step(bool_c<true>{}, k + 3, buf0, buf3, buf2);
-  if (k + 4 < ntiles) step(bool_c<true>{}, k + 4, buf1, buf0, buf3);
-  {
+  if (ntiles > 0) {                             // a sparse walk may visit nothing
+    fill(buf0, tile_of(0));
+    if (ntiles > 1) fill_whole(buf1, tile_of(1));
+    step(bool_c<false>{}, 0, buf0, buf3, buf2);
+    int k = 1;
+    for (; k + 6 <= ntiles; k += 4) {
+      step_inner(k, buf1, buf0, buf3);
+      step_inner(k + 1, buf2, buf1, buf0);
+      step_inner(k + 2, buf3, buf2, buf1);
+      step_inner(k + 3, buf0, buf3, buf2);
+    }
+    if (k < ntiles) step(bool_c<true>{}, k, buf1, buf0, buf3);
+    if (k + 1 < ntiles) step(bool_c<true>{}, k + 1, buf2, buf1, buf0);
+    if (k + 2 < ntiles) step(bool_c<true>{}, k + 2, buf3, buf2, buf1);
+    if (k + 3 < ntiles) step(bool_c<true>{}, k + 3, buf0, buf3, buf2);
+    if (k + 4 < ntiles) step(bool_c<true>{}, k + 4, buf1, buf0, buf3);
     const int last = (ntiles - 1) & 3;         // buffer of the last step
     const Buf& lb = last == 0 ? buf0 : last == 1 ? buf1 : last == 2 ? buf2 : buf3;
     flush(lb, bpp, bdsp);
@@ -415,11 +435,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
 // Key tiles are copied two steps ahead into a ring of three separately named
 // LDS buffers.  No atomics.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL, int WQ, int NW>
+template <int D, bool CAUSAL, int WQ, int NW, bool SPARSE>
 __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ nL2, const float* __restrict__ nD,
-    bf16* __restrict__ dQ, int H, int N, int d, float scale_log2, float scale) {
+    bf16* __restrict__ dQ, int H, int N, int d, float scale_log2, float scale,
+    const unsigned char* __restrict__ mask, int mask_heads) {
   using M = Mma<bf16>;
   using frag = bf16x8;
   constexpr int NH = WQ / 32;                  // 32-row halves per wave
@@ -464,11 +485,12 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
       pin_agpr(qf[c][kk]);
       pin_agpr(of[c][kk]);
     }
-    // padded rows (q >= N): S' = -inf so P = 0 (lo part 0, never inf - inf)
+    // padded rows (q >= N) and rows with no kept key (L = -inf): S' = -inf so
+    // P = 0 (lo part 0, never inf - inf)
     const float lq = q < N ? Lh[q] : -__builtin_inff();
     const float dq = q < N ? Dh[q] : 0.f;
     const bf16 lhi = (bf16)lq, dhi = (bf16)dq;
-    const bf16 llo = q < N ? (bf16)(lq - (float)lhi) : zero;
+    const bf16 llo = lq > -__builtin_inff() ? (bf16)(lq - (float)lhi) : zero;
     const bf16 dlo = (bf16)(dq - (float)dhi);
     bl[c] = h == 0 ? frag{lhi, llo, zero, zero, zero, zero, zero, zero} : frag{};
     bd[c] = h == 0 ? frag{dhi, dlo, zero, zero, zero, zero, zero, zero} : frag{};
@@ -481,9 +503,38 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
     for (int i = 0; i < MT; ++i) { acc[c][i] = zero16(); pin_agpr(acc[c][i]); }
 
   const int kv_end = CAUSAL ? min(N, qb + BQ) : N;
-  const int ntiles = (kv_end + BKV - 1) / BKV;
+  const int ntiles_all = (kv_end + BKV - 1) / BKV;
   // first tile holding key rows above some of the block's query rows
-  const int diag0 = CAUSAL ? max(0, min(ntiles, qb / BKV)) : ntiles;
+  const int diag0 = CAUSAL ? max(0, min(ntiles_all, qb / BKV)) : ntiles_all;
+  // block-sparse: the key tiles kept by either mask row of the block's query
+  // rows (rows qb .. qb + 255 span mask rows r0 and r0 + 1), in order; a wave
+  // (64 rows, one mask row) zeroes P on the tiles its own row drops.
+  __shared__ unsigned short vis[SPARSE ? kMaxVisit : 1];
+  __shared__ int nvis;
+  static_assert(!SPARSE || (BQ == 2 * kMaskBlock && WQ * 2 == kMaskBlock),
+                "mask rows per block and per wave");
+  const int nb = (N + kMaskBlock - 1) / kMaskBlock;
+  const int ntiles = !SPARSE ? ntiles_all : build_visits(vis, &nvis, ntiles_all,
+      [&](int t) ATTN_INLINE -> unsigned {
+        const unsigned char* mk = head_mask(mask, mask_heads, b, head, H, nb);
+        const int r0 = qb / kMaskBlock, c = t * BKV / kMaskBlock;
+        const unsigned code = (mk[r0 * nb + c] ? 1u : 0u) |
+                              (r0 + 1 < nb && mk[(r0 + 1) * nb + c] ? 2u : 0u);
+        return code ? (code << 14) | (unsigned)t : 0u;
+      });
+  // walk positions below inner_end need no checks (unmasked, next two tiles
+  // whole); a sparse walk takes every step through the checked form (one loop
+  // keeps the register assignment the same all along the walk)
+  const int inner_end = !SPARSE ? min(diag0, min(ntiles - 2, N / BKV - 2)) : 0;
+  // tile index at walk position p, and whether this wave's mask row drops it
+  auto tile_at = [&](int p) ATTN_INLINE -> int {
+    if constexpr (SPARSE) return (int)(visit_entry(vis, p) & kVisitTile);
+    else return p;
+  };
+  auto kill_at = [&](int p) ATTN_INLINE -> bool {
+    if constexpr (SPARSE) return ((visit_entry(vis, p) >> (14 + wave * WQ / kMaskBlock)) & 1u) == 0u;
+    else return false;
+  };
 
   // A key tile (K and V rows) into LDS: whole tiles by direct copies (2 * PER
   // instructions per wave), the sequence's ragged last tile by the register
@@ -510,7 +561,8 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
   // and every VALU stage reads a chain that finished at least one product
   // earlier: exps of S_0 beside S_1, exps of S_1 beside dP_0, dS_0 beside
   // dP_1, dS_1 beside dQ_0.  One operand read feeds the two halves' chains
-  // from registers.  V is read during S_1, K^T during dP_1 and dQ_0, and the
+  // from registers.  V is read during S_1 and dP_0, K^T during dP_1 and dQ_0 (each
+  // half a chain ahead of its use, which keeps few fragments live), and the
   // next sub-tile's K during dQ_1, which runs after the next step's barrier
   // for a tile's last sub-tile, so a tile starts on operands already read.
   // The copies of the tile two steps ahead go out during the S_0 chains.
@@ -533,15 +585,16 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
       fence();
     }
   };
-  auto mask_half = [&](f32x16& s, int c, int ka) ATTN_INLINE {
+  // P = 0 above the diagonal (causal) or everywhere (the wave's mask row drops the tile)
+  auto mask_half = [&](f32x16& s, int c, int ka, bool kill) ATTN_INLINE {
     const int q = qw + 32 * c + l32;
 #pragma unroll
     for (int r = 0; r < 16; ++r)
-      if (ka + acc_row(r, h) > q) s[r] = 0.f;
+      if (kill || (CAUSAL && ka + acc_row(r, h) > q)) s[r] = 0.f;
   };
   // sub-tile st of B (key rows ka ..), K fragments already in kf; leaves
   // dQ_1 pending in tf and bds1
-  auto sub = [&](const Buf& B, int st, int ka, bool masked, auto&& copy) ATTN_INLINE {
+  auto sub = [&](const Buf& B, int st, int ka, bool masked, bool kill, auto&& copy) ATTN_INLINE {
     const int r0 = st * 32;
     constexpr int E = 16 / KS;                  // elements per product in the exp and dS_0 stages
     f32x16 sc[2], pc[2];
@@ -554,30 +607,30 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
       if (kk % (KS / SPS) == 0) copy(st * SPS + kk / (KS / SPS));
       fence();
     }
-    // S'_1 | P_0 = exp2(S'_0); V read
+    // S'_1 | P_0 = exp2(S'_0); first half of V read (KS / 2 products ahead)
     sc[1] = M::mma(ones, bl[1], zero16());
-    vf[0] = plan.cols(B.v, r0, 0);
     fence();
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       sc[1] = M::mma(kf[kk], qf[1][kk], sc[1]);
-      if (kk + 1 < KS) vf[kk + 1] = plan.cols(B.v, r0, kk + 1);
+      if (kk >= KS / 2) vf[kk - KS / 2] = plan.cols(B.v, r0, kk - KS / 2);
 #pragma unroll
       for (int e = 0; e < E; ++e) sc[0][kk * E + e] = fast_exp2(sc[0][kk * E + e]);
       fence();
     }
-    if (CAUSAL && masked) mask_half(sc[0], 0, ka);
-    // dP'_0 | P_1 = exp2(S'_1)
+    if ((CAUSAL && masked) || kill) mask_half(sc[0], 0, ka, kill);
+    // dP'_0 | P_1 = exp2(S'_1); second half of V read
     pc[0] = M::mma(ones, bd[0], zero16());
     fence();
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       pc[0] = M::mma(vf[kk], of[0][kk], pc[0]);
+      if (kk < KS / 2) vf[KS / 2 + kk] = plan.cols(B.v, r0, KS / 2 + kk);
 #pragma unroll
       for (int e = 0; e < E; ++e) sc[1][kk * E + e] = fast_exp2(sc[1][kk * E + e]);
       fence();
     }
-    if (CAUSAL && masked) mask_half(sc[1], 1, ka);
+    if ((CAUSAL && masked) || kill) mask_half(sc[1], 1, ka, kill);
     // dP'_1 | dS_0 = P_0 o dP'_0, packed; first half of K^T read
     pc[1] = M::mma(ones, bd[1], zero16());
     fence();
@@ -585,7 +638,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       pc[1] = M::mma(vf[kk], of[1][kk], pc[1]);
-      if (kk % 2 == 0) tf[kk / 2] = plan.rows(B.k, r0, 0, kk / 2);
+      if (kk >= KS / 2) tf[kk - KS / 2] = plan.rows(B.k, r0, 0, kk - KS / 2);
 #pragma unroll
       for (int e = 0; e < E; ++e) pc[0][kk * E + e] = sc[0][kk * E + e] * pc[0][kk * E + e];
       if (kk == KS / 2 - 1) {
@@ -622,11 +675,11 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
   // One key tile: the pending dQ_1 of the previous tile while this tile's
   // first K fragments are read, then both sub-tiles.  Before the first tile
   // the pending products add zero (dS = 0), which keeps every step alike.
-  auto tile_body = [&](int kt, const Buf& B, bool masked, auto&& copy) ATTN_INLINE {
+  auto tile_body = [&](int kt, const Buf& B, bool masked, bool kill, auto&& copy) ATTN_INLINE {
     dq_half1(B, 0);
-    sub(B, 0, kt * BKV, masked, copy);
+    sub(B, 0, kt * BKV, masked, kill, copy);
     dq_half1(B, 32);
-    sub(B, 1, kt * BKV + 32, masked, copy);
+    sub(B, 1, kt * BKV + 32, masked, kill, copy);
   };
 
   // Key tiles are copied two steps ahead into a ring of three separately
@@ -634,16 +687,19 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
   // kt waits only for tile kt's copy and leaves tile kt + 1's in flight
   // (unless that one went by the register path, the ragged last tile, which
   // leaves nothing to count against).  Tiles from diag0 on apply the causal
-  // element mask.
+  // element mask.  kt is the walk position; tile_at(kt) the tile.
   auto step = [&](int kt, const Buf& cur, Buf& ahead) ATTN_INLINE {
-    if (kt + 1 < ntiles && (kt + 2) * BKV <= N) wait_async_fills_but<2 * FS::PER>();
+    const int t1 = !SPARSE ? kt + 1 : kt + 1 < ntiles ? tile_at(kt + 1) : 0;
+    if (kt + 1 < ntiles && (t1 + 1) * BKV <= N) wait_async_fills_but<2 * FS::PER>();
     else wait_async_fills();
     lds_barrier();
     plan.rebind();
-    const int k2 = (kt + 2) * BKV;
+    const int t2 = !SPARSE ? kt + 2 : kt + 2 < ntiles ? tile_at(kt + 2) : 0;
+    const int k2 = t2 * BKV;
     const bool spread = kt + 2 < ntiles && k2 + BKV <= N;
-    if (kt + 2 < ntiles && !spread) fill(ahead, kt + 2);     // ragged: register path now
-    tile_body(kt, cur, CAUSAL && kt >= diag0,
+    if (kt + 2 < ntiles && !spread) fill(ahead, t2);         // ragged: register path now
+    const int t = tile_at(kt);
+    tile_body(t, cur, CAUSAL && t >= diag0, kill_at(kt),
               [&](int j) ATTN_INLINE { if (spread) copy_slot(ahead, k2, j); });
   };
   // Steps below the diagonal whose tile two ahead is whole need none of the
@@ -653,16 +709,16 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
     wait_async_fills_but<2 * FS::PER>();
     lds_barrier();
     plan.rebind();
-    const int k2 = (kt + 2) * BKV;
-    tile_body(kt, cur, false, [&](int j) ATTN_INLINE { copy_slot(ahead, k2, j); });
+    const int k2 = tile_at(kt + 2) * BKV;
+    tile_body(tile_at(kt), cur, false, kill_at(kt),
+              [&](int j) ATTN_INLINE { copy_slot(ahead, k2, j); });
   };
 #pragma unroll
   for (int i = 0; i < 2 * MT; ++i) tf[i] = frag{};
   bds1[0] = bds1[1] = frag{};
-  fill(buf0, 0);
-  if (ntiles > 1) fill(buf1, 1);
+  if (ntiles > 0) fill(buf0, tile_at(0));       // a sparse walk may visit nothing
+  if (ntiles > 1) fill(buf1, tile_at(1));
   int kt = 0;
-  const int inner_end = min(diag0, min(ntiles - 2, N / BKV - 2));   // steps kt < inner_end
   for (; kt + 3 <= inner_end; kt += 3) {
     step_inner(kt, buf0, buf2);
     step_inner(kt + 1, buf1, buf0);
@@ -696,31 +752,40 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
 // ---------------------------------------------------------------------------
 static inline long rows_of(const BwdArgs& a) { return (long)a.B * a.H * a.N; }
 
-template <int D, bool C>
-static hipError_t dkdv_pipe_go(const BwdArgs& a, hipStream_t stream) {
+template <int D, bool C, bool S>
+static hipError_t dkdv_pipe_run(const BwdArgs& a, hipStream_t stream) {
   dim3 grid((a.N + 127) / 128, a.H, a.B);
-  hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, C>), grid, dim3(256), 0, stream,
+  hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, C, S>), grid, dim3(256), 0, stream,
                      static_cast<const bf16*>(a.Q), static_cast<const bf16*>(a.K),
                      static_cast<const bf16*>(a.V), static_cast<const bf16*>(a.dO),
                      a.Dws + rows_of(a), a.Dws, static_cast<bf16*>(a.dK),
-                     static_cast<bf16*>(a.dV), a.H, a.N, a.d, a.scale * kLog2e, a.scale);
+                     static_cast<bf16*>(a.dV), a.H, a.N, a.d, a.scale * kLog2e, a.scale,
+                     a.mask, a.mask_heads);
   return hipGetLastError();
+}
+template <int D, bool C>
+static hipError_t dkdv_pipe_go(const BwdArgs& a, hipStream_t stream) {
+  return a.mask ? dkdv_pipe_run<D, C, true>(a, stream) : dkdv_pipe_run<D, C, false>(a, stream);
 }
 
 // 256 query rows per workgroup as DQ_NW waves of 256 / DQ_NW rows
 #ifndef ATTN_DQ_NW
 #define ATTN_DQ_NW 4
 #endif
-template <int D, bool C>
-static hipError_t dq_pipe_go(const BwdArgs& a, hipStream_t stream) {
+template <int D, bool C, bool S>
+static hipError_t dq_pipe_run(const BwdArgs& a, hipStream_t stream) {
   constexpr int NW = ATTN_DQ_NW, WQ = 256 / NW;
   dim3 grid((a.N + 255) / 256, a.H, a.B);
-  hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, C, WQ, NW>), grid, dim3(NW * 64), 0, stream,
+  hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, C, WQ, NW, S>), grid, dim3(NW * 64), 0, stream,
                      static_cast<const bf16*>(a.Q), static_cast<const bf16*>(a.K),
                      static_cast<const bf16*>(a.V), static_cast<const bf16*>(a.dO),
                      a.Dws + rows_of(a), a.Dws, static_cast<bf16*>(a.dQ), a.H, a.N, a.d,
-                     a.scale * kLog2e, a.scale);
+                     a.scale * kLog2e, a.scale, a.mask, a.mask_heads);
   return hipGetLastError();
+}
+template <int D, bool C>
+static hipError_t dq_pipe_go(const BwdArgs& a, hipStream_t stream) {
+  return a.mask ? dq_pipe_run<D, C, true>(a, stream) : dq_pipe_run<D, C, false>(a, stream);
 }
 
 #define ATTN_PIPE_DISPATCH(FN, a, stream)                                  \

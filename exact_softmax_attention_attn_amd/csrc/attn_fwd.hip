@@ -23,7 +23,9 @@ __global__ __launch_bounds__(256, 1) void fwd_lse_kernel(const T* __restrict__ Q
                                                          const T* __restrict__ K,
                                                          const T* __restrict__ V,
                                                          T* __restrict__ O, float* __restrict__ L,
-                                                         int H, int N, int d, float scale_log2) {
+                                                         int H, int N, int d, float scale_log2,
+                                                         const unsigned char* __restrict__ mask,
+                                                         int mask_heads) {
   using M = Mma<T>;
   using frag = typename M::frag;
   constexpr int BQ = 128, BKV = 64, KS = D / M::K, MT = D / 32, RS = 32 / M::K;
@@ -56,6 +58,21 @@ __global__ __launch_bounds__(256, 1) void fwd_lse_kernel(const T* __restrict__ Q
 
   const int kv_end = CAUSAL ? min(N, qb + BQ) : N;
   const int nkt = (kv_end + BKV - 1) / BKV;
+  // the walk: key tiles 0 .. nkt - 1, or (block-sparse mask) the ones whose
+  // mask block (row ib of this query block, column of the tile) is kept
+  __shared__ unsigned short vis[kMaxVisit];
+  __shared__ int nvis;
+  int ntiles = nkt;
+  if (mask) {
+    const int nb = (N + kMaskBlock - 1) / kMaskBlock;
+    const unsigned char* mk = head_mask(mask, mask_heads, b, head, H, nb);
+    ntiles = build_visits(vis, &nvis, nkt, [&](int t) ATTN_INLINE -> unsigned {
+      return mk[ib * nb + t * BKV / kMaskBlock] ? (1u << 14) | (unsigned)t : 0u;
+    });
+  }
+  auto tile_at = [&](int p) ATTN_INLINE -> int {
+    return mask ? (int)(visit_entry(vis, p) & kVisitTile) : p;
+  };
 
   auto fill = [&](Buf& B, int kt) ATTN_INLINE {
     const int k0 = kt * BKV;
@@ -124,9 +141,10 @@ __global__ __launch_bounds__(256, 1) void fwd_lse_kernel(const T* __restrict__ Q
     }
   };
 
-  auto step = [&](const Buf& cur, Buf& nxt, int kt) ATTN_INLINE {
-    if (kt + 1 < nkt) fill(nxt, kt + 1);
-    const int k0 = kt * BKV;
+  // step p: tile tile_at(p) in cur while tile tile_at(p + 1) is copied to nxt
+  auto step = [&](const Buf& cur, Buf& nxt, int p) ATTN_INLINE {
+    const int k0 = tile_at(p) * BKV;
+    if (p + 1 < ntiles) fill(nxt, tile_at(p + 1));
     if ((CAUSAL && k0 + BKV - 1 > qb) || k0 + BKV > N)
       body(cur, k0, std::integral_constant<bool, true>{});
     else
@@ -135,18 +153,23 @@ __global__ __launch_bounds__(256, 1) void fwd_lse_kernel(const T* __restrict__ Q
     __syncthreads();
   };
 
-  fill(bufA, 0);
-  wait_async_fills();
-  __syncthreads();
-  for (int kt = 0; kt < nkt; kt += 2) {
-    step(bufA, bufB, kt);
-    if (kt + 1 < nkt) step(bufB, bufA, kt + 1);
+  if (ntiles > 0) {                               // a sparse walk may visit nothing
+    fill(bufA, tile_at(0));
+    wait_async_fills();
+    __syncthreads();
   }
-  const float inv = 1.f / l;
+  for (int p = 0; p < ntiles; p += 2) {
+    step(bufA, bufB, p);
+    if (p + 1 < ntiles) step(bufB, bufA, p + 1);
+  }
+  // a row that keeps no key ends with l = 0: O = 0, L = -inf
+  const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
     store_acc_transposed<T>(acc[mt], O + base, rs, qw, mt * 32, N, d, inv, lane);
-  if (h == 0 && q < N) L[((long)b * H + head) * N + q] = (m + log2f(l)) * 0.69314718055994531f;
+  if (h == 0 && q < N)
+    L[((long)b * H + head) * N + q] =
+        l > 0.f ? (m + log2f(l)) * 0.69314718055994531f : -__builtin_inff();
 }
 
 template <typename T, int D, bool C>
@@ -155,7 +178,7 @@ static hipError_t fwd_go(const FwdArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((fwd_lse_kernel<T, D, C>), grid, dim3(256), 0, stream,
                      static_cast<const T*>(a.Q), static_cast<const T*>(a.K),
                      static_cast<const T*>(a.V), static_cast<T*>(a.O), a.L, a.H, a.N, a.d,
-                     a.scale * kLog2e);
+                     a.scale * kLog2e, a.mask, a.mask_heads);
   return hipGetLastError();
 }
 

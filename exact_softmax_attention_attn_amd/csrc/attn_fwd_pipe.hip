@@ -32,7 +32,10 @@
 // Key tiles of 64 rows (K, V) rotate through three LDS buffers; the copy of
 // tile t + 2 goes out right after the barrier that publishes tile t + 1.  Tiles
 // whose next sub-tiles need no mask and whose tile two ahead is whole run
-// without any of the edge checks.
+// without any of the edge checks.  SPARSE: the walk visits the key tiles kept
+// by either mask row of the block's query rows; a wave whose own mask row
+// drops a tile gives its scores -inf.  A row that keeps no key ends with
+// l = 0: its output is 0 and its L is -inf.
 #include <type_traits>
 
 #include "common.h"
@@ -74,10 +77,11 @@ __device__ __forceinline__ float frag_sum(const bf16x8& f, float acc) {
 
 }  // namespace
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(256, 1) void fwd_bf16_pipe_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    bf16* __restrict__ O, float* __restrict__ Lout, int H, int N, int d, float scale_log2) {
+    bf16* __restrict__ O, float* __restrict__ Lout, int H, int N, int d, float scale_log2,
+    const unsigned char* __restrict__ mask, int mask_heads) {
   using M = Mma<bf16>;
   using frag = bf16x8;
   constexpr int NH = 2, WQ = 64, NW = 4, BQ = NW * WQ, BKV = 64;
@@ -120,7 +124,32 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_pipe_kernel(
     for (int i = 0; i < MT; ++i) { acc[c][i] = zero16(); pin_agpr(acc[c][i]); }
 
   const int kv_end = CAUSAL ? min(N, qb + BQ) : N;
-  const int ntiles = (kv_end + BKV - 1) / BKV;
+  const int ntiles_all = (kv_end + BKV - 1) / BKV;
+  // block-sparse: the key tiles kept by either mask row of the block's query
+  // rows, in order (entry = tile | which mask rows keep it << 14)
+  __shared__ unsigned short vis[SPARSE ? kMaxVisit : 1];
+  __shared__ int nvis;
+  static_assert(!SPARSE || (BQ == 2 * kMaskBlock && WQ * 2 == kMaskBlock),
+                "mask rows per block and per wave");
+  const int nb = (N + kMaskBlock - 1) / kMaskBlock;
+  const int ntiles = !SPARSE ? ntiles_all : build_visits(vis, &nvis, ntiles_all,
+      [&](int t) ATTN_INLINE -> unsigned {
+        const unsigned char* mk = head_mask(mask, mask_heads, b, head, H, nb);
+        const int r0 = qb / kMaskBlock, c = t * BKV / kMaskBlock;
+        const unsigned code = (mk[r0 * nb + c] ? 1u : 0u) |
+                              (r0 + 1 < nb && mk[(r0 + 1) * nb + c] ? 2u : 0u);
+        return code ? (code << 14) | (unsigned)t : 0u;
+      });
+  // tile at walk position p (read where no LDS operation is in flight), and
+  // whether this wave's mask row drops it
+  auto tile_at = [&](int p) ATTN_INLINE -> int {
+    if constexpr (SPARSE) return (int)(visit_entry(vis, p) & kVisitTile);
+    else return p;
+  };
+  auto kill_at = [&](int p) ATTN_INLINE -> bool {
+    if constexpr (SPARSE) return ((visit_entry(vis, p) >> (14 + wave * WQ / kMaskBlock)) & 1u) == 0u;
+    else return false;
+  };
 
   using FS = AsyncFillShape<BKV, D, NW>;
   unsigned copy_off[FS::PER];
@@ -178,21 +207,21 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_pipe_kernel(
       fence();
     }
   };
-  // keys of sub-tile j above the query (causal) or past N get -inf
-  auto mask = [&](f32x16 (&s)[NH], int j) ATTN_INLINE {
-    const int ka = j * 32;
+  // keys of the sub-tile at key row ka above the query (causal) or past N get
+  // -inf, every key when the wave's mask row drops the tile (kill)
+  auto mask_sub = [&](f32x16 (&s)[NH], int ka, bool kill) ATTN_INLINE {
 #pragma unroll
     for (int c = 0; c < NH; ++c) {
       const int q = qw + 32 * c + l32;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int kv = ka + acc_row(r, h);
-        if ((CAUSAL && kv > q) || kv >= N) s[c][r] = -__builtin_inff();
+        if (kill || (CAUSAL && kv > q) || kv >= N) s[c][r] = -__builtin_inff();
       }
     }
   };
-  auto needs_mask = [&](int j) ATTN_INLINE {
-    return (CAUSAL && j * 32 + 31 > qw) || j * 32 + 32 > N;
+  auto needs_mask = [&](int ka, bool kill) ATTN_INLINE {
+    return kill || (CAUSAL && ka + 31 > qw) || ka + 32 > N;
   };
   // row max of s (raw scores, log2 units) per half
   auto row_max = [&](const f32x16 (&s)[NH], float (&mx)[NH]) ATTN_INLINE {
@@ -217,27 +246,34 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_pipe_kernel(
     lsum[c] += sum_pair(frag_sum(bp[c][1], frag_sum(bp[c][0], 0.f)));
   };
 
-  // ---- prologue: tiles 0 and 1 in flight; S_0, m = its row max
-  fill(buf0, 0);
-  if (ntiles > 1) fill(buf1, 1);
-  if (ntiles > 1 && 2 * BKV <= N) wait_async_fills_but<2 * FS::PER>();   // tile 1 may fly
-  else wait_async_fills();
-  __syncthreads();
-  s_chain(buf0, 0, sc, [&](int) ATTN_INLINE {});
-  if (needs_mask(0)) mask(sc, 0);
-  {
+  // ---- prologue: tiles 0 and 1 in flight; S_0, m = its row max (at least
+  // -1e30, so a row whose first keys are all masked stays finite)
+#pragma unroll
+  for (int c = 0; c < NH; ++c) { m[c] = -1e30f; lsum[c] = 0.f; }
+  if (ntiles > 0) {                             // a sparse walk may visit nothing
+    const int t0 = tile_at(0);
+    const int t1 = ntiles > 1 ? tile_at(1) : 0;
+    fill(buf0, t0);
+    if (ntiles > 1) fill(buf1, t1);
+    if (ntiles > 1 && (t1 + 1) * BKV <= N) wait_async_fills_but<2 * FS::PER>();   // tile 1 may fly
+    else wait_async_fills();
+    __syncthreads();
+    s_chain(buf0, 0, sc, [&](int) ATTN_INLINE {});
+    const bool kill0 = kill_at(0);
+    if (needs_mask(t0 * BKV, kill0)) mask_sub(sc, t0 * BKV, kill0);
     float mx[NH];
     row_max(sc, mx);
 #pragma unroll
-    for (int c = 0; c < NH; ++c) { m[c] = mx[c]; lsum[c] = 0.f; }
+    for (int c = 0; c < NH; ++c) m[c] = fmaxf(mx[c], -1e30f);
+    exps(sc, 0, 0, 16);
   }
-  exps(sc, 0, 0, 16);
 
-  // ---- one iteration: sub-tile j in buffer Bj; sub-tile j + 1 in buffer Bn.
+  // ---- one iteration: sub-tile j in buffer Bj; sub-tile j + 1 in buffer Bn,
+  // at key row ka_next, dropped for this wave when kill_next.
   // MASKABLE = false: the next sub-tile needs no mask (checked by the caller).
   float alpha[NH];
   auto iteration = [&](auto maskable, int j, const Buf& Bj, const Buf& Bn,
-                       bool has_next) ATTN_INLINE {
+                       bool has_next, int ka_next, bool kill_next) ATTN_INLINE {
     constexpr bool MASKABLE = decltype(maskable)::value;
     f32x16 sn[NH];
     // A: S_{j+1} | exps of S_j half 1, pack P_j and its row sums
@@ -258,7 +294,7 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_pipe_kernel(
     bool resc = false;
     auto valu_b = [&](int i) ATTN_INLINE {
       if (!has_next) return;
-      if (MASKABLE && i == 0 && needs_mask(j + 1)) mask(sn, j + 1);
+      if (MASKABLE && i == 0 && needs_mask(ka_next, kill_next)) mask_sub(sn, ka_next, kill_next);
       if (i == 1) {
         float mx[NH];
         row_max(sn, mx);
@@ -303,30 +339,37 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_pipe_kernel(
   // two ahead goes to ahead.  The barrier before sub-tile 2t + 1's iteration
   // publishes tile t + 1 (its S chain reads it) and frees tile t - 1's buffer.
   auto tile = [&](int t, const Buf& cur, const Buf& nxt, Buf& ahead) ATTN_INLINE {
-    iteration(bool_c<true>{}, 2 * t, cur, cur, true);
+    const int tt = tile_at(t);
+    const bool kt_ = kill_at(t);
+    iteration(bool_c<true>{}, 2 * t, cur, cur, true, tt * BKV + 32, kt_);
     const bool more = t + 1 < ntiles;
+    int tn = 0;
+    bool kn = false;
     if (more) {
       wait_async_fills();
       lds_barrier();
-      if (t + 2 < ntiles) fill(ahead, t + 2);
+      if (t + 2 < ntiles) fill(ahead, tile_at(t + 2));
+      tn = tile_at(t + 1);
+      kn = kill_at(t + 1);
     }
-    iteration(bool_c<true>{}, 2 * t + 1, cur, nxt, more);
+    iteration(bool_c<true>{}, 2 * t + 1, cur, nxt, more, tn * BKV, kn);
   };
   // tiles whose next sub-tiles (2t + 1, 2t + 2) need no mask for any wave and
   // whose tile two ahead is whole
   auto tile_inner = [&](int t, const Buf& cur, const Buf& nxt, Buf& ahead) ATTN_INLINE {
-    iteration(bool_c<false>{}, 2 * t, cur, cur, true);
+    iteration(bool_c<false>{}, 2 * t, cur, cur, true, 0, false);
     wait_async_fills();
     lds_barrier();
     const int k2 = (t + 2) * BKV;
     async_fill_untracked<BKV, D, NW>(KT{ahead.k}, K + base + k2 * rs, copy_off, wave);
     async_fill_untracked<BKV, D, NW>(KT{ahead.v}, V + base + k2 * rs, copy_off, wave);
-    iteration(bool_c<false>{}, 2 * t + 1, cur, nxt, true);
+    iteration(bool_c<false>{}, 2 * t + 1, cur, nxt, true, 0, false);
   };
   // inner: 64 t + 95 <= qb (causal: keys of sub-tiles up to 2t + 2 are at or
   // below every query of the block), t + 2 < ntiles, tile t + 2 whole
-  int inner_end = min(ntiles - 2, N / BKV - 2);
-  if (CAUSAL) inner_end = min(inner_end, (qb - 95) / BKV + 1);
+  // (a sparse walk takes every tile through the checked form)
+  int inner_end = SPARSE ? 0 : min(ntiles - 2, N / BKV - 2);
+  if (CAUSAL && !SPARSE) inner_end = min(inner_end, (qb - 95) / BKV + 1);
   int t = 0;
   for (; t + 3 <= inner_end; t += 3) {
     tile_inner(t, buf0, buf1, buf2);
@@ -344,24 +387,29 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_pipe_kernel(
   mma_acc_drain(acc);
 #pragma unroll
   for (int c = 0; c < NH; ++c) {
-    const float inv = 1.f / lsum[c];
+    const float inv = lsum[c] > 0.f ? 1.f / lsum[c] : 0.f;   // no kept key: O = 0
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
       store_acc_transposed<bf16>(acc[c][mt], O + base, rs, qw + 32 * c, mt * 32, N, d, inv, lane);
     const int q = qw + 32 * c + l32;
     if (h == 0 && q < N)
-      Lout[((long)b * H + head) * N + q] = (m[c] + log2f(lsum[c])) * 0.69314718055994531f;
+      Lout[((long)b * H + head) * N + q] =
+          lsum[c] > 0.f ? (m[c] + log2f(lsum[c])) * 0.69314718055994531f : -__builtin_inff();
   }
 }
 
-template <int D, bool C>
-static hipError_t fwd_pipe_go(const FwdArgs& a, hipStream_t stream) {
+template <int D, bool C, bool S>
+static hipError_t fwd_pipe_run(const FwdArgs& a, hipStream_t stream) {
   dim3 grid((a.N + 255) / 256, a.H, a.B);
-  hipLaunchKernelGGL((fwd_bf16_pipe_kernel<D, C>), grid, dim3(256), 0, stream,
+  hipLaunchKernelGGL((fwd_bf16_pipe_kernel<D, C, S>), grid, dim3(256), 0, stream,
                      static_cast<const bf16*>(a.Q), static_cast<const bf16*>(a.K),
                      static_cast<const bf16*>(a.V), static_cast<bf16*>(a.O), a.L, a.H, a.N,
-                     a.d, a.scale * kLog2e);
+                     a.d, a.scale * kLog2e, a.mask, a.mask_heads);
   return hipGetLastError();
+}
+template <int D, bool C>
+static hipError_t fwd_pipe_go(const FwdArgs& a, hipStream_t stream) {
+  return a.mask ? fwd_pipe_run<D, C, true>(a, stream) : fwd_pipe_run<D, C, false>(a, stream);
 }
 
 hipError_t launch_fwd_lse_bf16_pipe(const FwdArgs& a, hipStream_t stream) {

@@ -91,6 +91,74 @@ __device__ __forceinline__ BlockOrder block_order() {
   return {lin / nbh, bh % (int)gridDim.y, bh / (int)gridDim.y};
 }
 
+// ---------------------------------------------------------------------------
+// Block-sparse masks.  A mask keeps or drops whole blocks of kMaskBlock query
+// rows by kMaskBlock key rows (ddx PR #162, section "What changed": a filter
+// on grouping keys passes a whole group of rows or none of it); the causal
+// rule applies on top.  One (b, h) reads nb x nb bytes, row-major, nb =
+// ceil(N / kMaskBlock); mask_heads = 1 shares one mask, B * H gives each
+// (b, h) its own.
+//
+// A walk over tiles becomes a walk over a visit list: the kept tiles, in walk
+// order, compacted into LDS once per workgroup.  Entry = tile index (low 14
+// bits) | code << 14, code = which of (up to) two mask rows the workgroup's
+// query rows span keep the tile (bit 0: the first, bit 1: the second); a
+// workgroup inside one mask row uses code 1.
+// ---------------------------------------------------------------------------
+constexpr int kMaskBlock = 128;
+constexpr int kMaxVisit = 1024;          // tiles of 64 rows per walk: N <= 65536
+constexpr int kVisitTile = 0x3fff;
+
+__device__ __forceinline__ const unsigned char* head_mask(const unsigned char* mask,
+                                                          int mask_heads, int b, int head, int H,
+                                                          int nb) {
+  return mask + (mask_heads == 1 ? 0L : ((long)b * H + head) * nb * nb);
+}
+
+// Wave 0 compacts the candidates i = 0 .. n - 1 whose entry(i) is nonzero into
+// vis[0 ..), in candidate order, 64 per ballot; every thread gets the count
+// after the workgroup barrier that ends the call.
+template <typename F>
+__device__ __forceinline__ int build_visits(unsigned short* vis, int* count, int n, F entry) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int c = 0;
+    for (int i0 = 0; i0 < n; i0 += 64) {
+      const int i = i0 + lane;
+      const unsigned e = i < n ? entry(i) : 0u;
+      const unsigned long long bal = __ballot(e != 0u);
+      if (e != 0u) vis[c + __popcll(bal & ((1ull << lane) - 1ull))] = (unsigned short)e;
+      c += __popcll(bal);
+    }
+    if (lane == 0) *count = c;
+  }
+  __syncthreads();
+  return *count;
+}
+
+// Entry p of a visit list, as a wave-uniform value.  The read waits for
+// itself inside the same statement (and so for every earlier LDS operation of
+// the wave): meant for the points right before or after a barrier, where
+// nothing else is in flight, and kept out of the compiler's view so it does
+// not reschedule it among the operand reads.
+__device__ __forceinline__ unsigned visit_entry(const unsigned short* vis, int p) {
+  unsigned v;
+  const unsigned addr = (unsigned)(unsigned long)((const __attribute__((address_space(3))) unsigned short*)(vis + p));
+  asm volatile("ds_read_u16 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
+  return (unsigned)__builtin_amdgcn_readfirstlane((int)v);
+}
+
+// Entries of an ascending visit list vis[0 .. n) whose tile index is below x.
+__device__ __forceinline__ int visits_below(const unsigned short* vis, int n, int x) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if ((int)(vis[mid] & kVisitTile) < x) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
 // Before the VALU reads AGPR accumulators written by mma_acc_agpr: the last
 // 32x32 matrix instruction must have written its results back (it takes 8
 // passes of 4 cycles plus write-back latency).

@@ -18,6 +18,8 @@ struct BwdArgs {
   int causal;
   float scale;
   int dtype;  // 0 = f32, 1 = bf16
+  const unsigned char* mask = nullptr;   // block-sparse mask, or nullptr (every block kept)
+  int mask_heads = 1;
 };
 
 struct FwdArgs {
@@ -30,6 +32,8 @@ struct FwdArgs {
   int causal;
   float scale;
   int dtype;
+  const unsigned char* mask = nullptr;
+  int mask_heads = 1;
 };
 
 // Head dims are served by kernels compiled for 32, 64 or 128 columns; a

@@ -36,7 +36,8 @@ import math
 
 import numpy as np
 
-__all__ = ["Workload", "WORKLOADS", "get", "make_inputs", "make_random", "bf16_round"]
+__all__ = ["Workload", "WORKLOADS", "get", "make_inputs", "make_random", "bf16_round",
+           "MASK_BLOCK", "make_block_mask", "window_block_mask"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -119,6 +120,38 @@ def make_inputs(w: Workload, seed: int = 0) -> dict:
     do = rng.standard_normal(shape)
     return {"q": _cast(q, w.dtype), "k": _cast(k, w.dtype), "v": _cast(v, w.dtype),
             "do": _cast(do, w.dtype)}
+
+
+MASK_BLOCK = 128   # rows and keys per block of a block-sparse mask
+
+
+def make_block_mask(N: int, density: float = 0.5, seed: int = 0, heads=None,
+                    keep_diagonal: bool = True, empty_rows=()) -> np.ndarray:
+    """A random block mask: uint8 [nb, nb], or [B, H, nb, nb] for heads = (B, H).
+
+    Each block is kept with probability ``density`` (PCG64 ``default_rng``);
+    ``keep_diagonal`` keeps block (r, r) so every row keeps a key; the block
+    rows listed in ``empty_rows`` keep nothing.
+    """
+    nb = (N + MASK_BLOCK - 1) // MASK_BLOCK
+    rng = np.random.default_rng(seed)
+    shape = (nb, nb) if heads is None else tuple(heads) + (nb, nb)
+    m = (rng.random(shape) < density).astype(np.uint8)
+    if keep_diagonal:
+        idx = np.arange(nb)
+        m[..., idx, idx] = 1
+    for r in empty_rows:
+        m[..., r, :] = 0
+    return np.ascontiguousarray(m)
+
+
+def window_block_mask(N: int, window_blocks: int, sink_blocks: int = 1) -> np.ndarray:
+    """Local attention with attention sinks, at block granularity: block (r, c)
+    is kept when r - window_blocks < c <= r or c < sink_blocks."""
+    nb = (N + MASK_BLOCK - 1) // MASK_BLOCK
+    r = np.arange(nb)[:, None]
+    c = np.arange(nb)[None, :]
+    return (((c <= r) & (c > r - window_blocks)) | (c < sink_blocks)).astype(np.uint8)
 
 
 def make_random(B: int, H: int, N: int, d: int, dtype: str, seed: int = 0,

@@ -133,6 +133,38 @@ int attn_bwd_dq(const void* Q, const void* K, const void* V, const void* dO,
                 int B, int H, int N, int d, int causal, float scale, int dtype,
                 void* stream);
 
+/*
+ * Block-sparse masks.  A mask keeps or drops whole blocks of ATTN_MASK_BLOCK
+ * query rows by ATTN_MASK_BLOCK key rows, the group-level filter of ddx PR
+ * #162 ("perf(ddx-ad): transpose causal attention's contractions without
+ * their joins", section "What changed": a filter that reads only grouping
+ * keys passes every row of a group or none).  Pair (i, j) is kept iff
+ *     mask[., i / ATTN_MASK_BLOCK, j / ATTN_MASK_BLOCK] != 0
+ * and, when causal, j <= i.  Tiles of dropped blocks are never visited.
+ *   mask: device memory, uint8 [mask_heads, nb, nb] row-major, nb =
+ *         ceil(N / ATTN_MASK_BLOCK); any alignment; read only.
+ *   mask_heads: 1 (every (b, h) shares the mask) or B * H (entry b * H + h).
+ * A row that keeps no key has O = 0 and L = -inf, and contributes nothing to
+ * dK and dV; its dQ is 0.  Limits beyond the shared ones: N <= 65536
+ * (ATTN_ERR_UNSUPPORTED otherwise); mask_heads not 1 or B * H, or a null mask,
+ * is ATTN_ERR_INVALID.  The backward must be given the L of the masked
+ * forward with the same mask.
+ */
+#define ATTN_MASK_BLOCK 128
+
+/* attn_fwd_lse restricted to the pairs a block mask keeps. */
+int attn_fwd_lse_masked(const void* Q, const void* K, const void* V, void* O, float* L,
+                        const unsigned char* mask, int mask_heads,
+                        int B, int H, int N, int d, int causal, float scale, int dtype,
+                        void* stream);
+
+/* attn_bwd restricted to the pairs a block mask keeps (same three stages;
+ * the preprocess is the same, dK/dV and dQ walk only kept tiles). */
+int attn_bwd_masked(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                    const float* L, void* dQ, void* dK, void* dV, void* workspace,
+                    const unsigned char* mask, int mask_heads,
+                    int B, int H, int N, int d, int causal, float scale, int dtype, void* stream);
+
 /* Static text for a status code ("ok", "invalid argument", ...). */
 const char* attn_status_string(int status);
 

@@ -31,8 +31,9 @@ def _declared():
 
 def test_header_declares_the_entry_points():
     assert _declared() == sorted([
-        "attn_bwd", "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_preprocess",
-        "attn_bwd_workspace_bytes", "attn_fwd_lse", "attn_last_error", "attn_status_string"])
+        "attn_bwd", "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_masked", "attn_bwd_preprocess",
+        "attn_bwd_workspace_bytes", "attn_fwd_lse", "attn_fwd_lse_masked", "attn_last_error",
+        "attn_status_string"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -128,6 +129,28 @@ def test_validation_rejects_bad_arguments_without_launching(lib):
     assert lib.attn_bwd_dkdv(*([FAKE] * 7), 1, 1, 8, 8, 1, 0.0, 0, NUL) == 1
     assert lib.attn_bwd_dq(*([FAKE] * 5), NUL, 1, 1, 8, 8, 1, 0.5, 0, NUL) == 1
     assert lib.attn_bwd_dq(*([FAKE] * 6), 1, 1, 8, 256, 1, 0.5, 1, NUL) == 2
+    assert lib.attn_last_error() == b""
+
+
+def test_masked_entry_points_validate_the_mask(lib):
+    f5 = [FAKE] * 5
+    b10 = [FAKE] * 10
+
+    def fwd(mask, heads, B=1, H=1, N=8, d=8, causal=1, scale=0.5, dtype=0):
+        return lib.attn_fwd_lse_masked(*f5, mask, heads, B, H, N, d, causal, scale, dtype, NUL)
+
+    def bwd(mask, heads, B=1, H=1, N=8, d=8, causal=1, scale=0.5, dtype=0):
+        return lib.attn_bwd_masked(*b10, mask, heads, B, H, N, d, causal, scale, dtype, NUL)
+
+    for call in (fwd, bwd):
+        assert call(NUL, 1) == 1                              # no mask
+        assert call(FAKE, 0) == 1                             # mask_heads not 1 or B * H
+        assert call(FAKE, 3, B=2, H=2) == 1
+        assert call(FAKE, 1, N=65537) == 2                    # longer walks than the lists hold
+        assert call(FAKE, 1, d=136) == 2                      # the shared checks still apply
+        assert call(FAKE, 1, scale=0.0) == 1
+    p = list(b10); p[3] = NUL
+    assert lib.attn_bwd_masked(*p, FAKE, 1, 1, 1, 8, 8, 1, 0.5, 0, NUL) == 1
     assert lib.attn_last_error() == b""
 
 
