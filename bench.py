@@ -54,8 +54,20 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def pairs(B, H, N, causal=True):
-    return B * H * (N * (N + 1) // 2 if causal else N * N)
+def pairs(B, H, N, causal=True, block_mask=None, mask_block=128):
+    """Kept (query, key) pairs: causal or full, within the kept blocks of a
+    shared block mask if one is given."""
+    if block_mask is None:
+        return B * H * (N * (N + 1) // 2 if causal else N * N)
+    total = 0
+    for r, c in zip(*block_mask.nonzero()):
+        rows = min(mask_block, N - r * mask_block)
+        cols = min(mask_block, N - c * mask_block)
+        if not causal or c < r:
+            total += rows * cols
+        elif c == r:
+            total += rows * (rows + 1) // 2
+    return B * H * total
 
 
 def traffic_record():
@@ -69,7 +81,7 @@ def traffic_record():
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(w, x):
+def cpu_baseline(w, x, bm=None):
     """The oracle as it stands, on whole (batch, head) slices of the workload.
 
     Heads run one after another until CPU_BASELINE_SECONDS have passed (at
@@ -89,12 +101,12 @@ def cpu_baseline(w, x):
     for b, h in heads:
         q, k, v, do = (x[n][b:b + 1, :, h:h + 1].astype(np.float64) for n in ("q", "k", "v", "do"))
         t0 = time.perf_counter()
-        orc.attn_bwd(q, k, v, do, w.scale, w.causal)
+        orc.attn_bwd(q, k, v, do, w.scale, w.causal, bm)
         spent += time.perf_counter() - t0
         done += 1
         if spent >= CPU_BASELINE_SECONDS:
             break
-    flops = 10 * w.d * pairs(1, 1, w.N, w.causal) * done
+    flops = 10 * w.d * pairs(1, 1, w.N, w.causal, bm) * done
     return {"value": round(flops / spent / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"{done} of {len(heads)} (batch, head) slices of {w.name} (N={w.N}, d={w.d}, "
@@ -220,7 +232,15 @@ def main(argv=None):
     x = workloads.make_inputs(w, seed=0)
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     q, k, v, do = (torch.from_numpy(x[n]).to(dev).to(tdt) for n in ("q", "k", "v", "do"))
-    o, lse = binding.attn_fwd_lse(q, k, v, causal=w.causal, scale=w.scale)
+    bm = workloads.workload_mask(w)               # block-sparse workloads: a shared mask
+    mask = None if bm is None else torch.from_numpy(bm).to(dev)
+
+    def forward():
+        if mask is None:
+            return binding.attn_fwd_lse(q, k, v, causal=w.causal, scale=w.scale)
+        return binding.attn_fwd_lse_masked(q, k, v, mask, causal=w.causal, scale=w.scale)
+
+    o, lse = forward()
     dq, dk, dv = (torch.empty_like(q) for _ in range(3))
     ws = binding.new_workspace(w.B, w.H, w.N, dev)
     torch.cuda.synchronize()
@@ -231,10 +251,17 @@ def main(argv=None):
         binding.attn_bwd_preprocess(o, do, lse, ws)
         if ev is not None:
             ev[1].record()
-        binding.attn_bwd_dkdv(q, k, v, do, ws, dk, dv, causal=w.causal, scale=w.scale)
+        if mask is None:
+            binding.attn_bwd_dkdv(q, k, v, do, ws, dk, dv, causal=w.causal, scale=w.scale)
+        else:
+            binding.attn_bwd_dkdv_masked(q, k, v, do, ws, dk, dv, mask, causal=w.causal,
+                                         scale=w.scale)
         if ev is not None:
             ev[2].record()
-        binding.attn_bwd_dq(q, k, v, do, ws, dq, causal=w.causal, scale=w.scale)
+        if mask is None:
+            binding.attn_bwd_dq(q, k, v, do, ws, dq, causal=w.causal, scale=w.scale)
+        else:
+            binding.attn_bwd_dq_masked(q, k, v, do, ws, dq, mask, causal=w.causal, scale=w.scale)
         if ev is not None:
             ev[3].record()
 
@@ -256,7 +283,7 @@ def main(argv=None):
     dkdv = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     dqk = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
     ms = wall / args.steps * 1e3
-    P = pairs(w.B, w.H, w.N, w.causal)
+    P = pairs(w.B, w.H, w.N, w.causal, bm)
     flops = 10 * w.d * P
     value = flops / (ms * 1e-3) / 1e12
     dkdv_flops = 8 * w.d * P
@@ -266,12 +293,12 @@ def main(argv=None):
     # the forward (the step that supplies O and L), timed on its own after the
     # backward's timed region: 4 d FLOPs per kept pair (S and P V)
     fev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    binding.attn_fwd_lse(q, k, v, causal=w.causal, scale=w.scale)
+    forward()
     torch.cuda.synchronize()
     fwd_runs = 5
     fev[0].record()
     for _ in range(fwd_runs):
-        binding.attn_fwd_lse(q, k, v, causal=w.causal, scale=w.scale)
+        forward()
     fev[1].record()
     torch.cuda.synchronize()
     fwd_ms = fev[0].elapsed_time(fev[1]) / fwd_runs
@@ -312,7 +339,8 @@ def main(argv=None):
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
                    "causal": w.causal, "scale": w.scale, "layout": "[B,N,H,d]",
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU",
+                   **({"block_mask": w.mask, "kept_pairs": P} if bm is not None else {})},
         "pct_of_peak": round(100 * value / peak, 2),
         "stages_ms": {"preprocess": round(pre, 4), "dkdv": round(dkdv, 4), "dq": round(dqk, 4)},
         "hbm_gbs_algorithmic": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
@@ -329,7 +357,7 @@ def main(argv=None):
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle, whole heads, bounded)", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(w, x)
+        line["cpu_baseline"] = cpu_baseline(w, x, bm)
     print(json.dumps(line), flush=True)
     return 0
 

@@ -36,6 +36,10 @@ _SIGNATURES = {
     "attn_fwd_lse_masked": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
     "attn_bwd_masked": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I,
                              _I, _I, _I, _I, _I, _F, _I, _P]),
+    "attn_bwd_dkdv_masked": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I,
+                                  _I, _I, _I, _I, _I, _F, _I, _P]),
+    "attn_bwd_dq_masked": (_I, [_P, _P, _P, _P, _P, _P, _P, _I,
+                                _I, _I, _I, _I, _I, _F, _I, _P]),
     "attn_status_string": (ctypes.c_char_p, [_I]),
     "attn_last_error": (ctypes.c_char_p, []),
 }
@@ -244,3 +248,33 @@ def attn_bwd_masked(q, k, v, o, do, lse, mask, causal: bool = True, scale: float
               _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), mp, mh, B, H, N, d,
               int(bool(causal)), scale, _dtype_code(q), _stream(q.device))
     return dq, dk, dv
+
+
+def attn_bwd_dkdv_masked(q, k, v, do, workspace, dk, dv, mask, causal: bool = True,
+                         scale: float | None = None):
+    """Stage 2 of attn_bwd_masked: dK, dV (workspace from attn_bwd_preprocess)."""
+    _check_bnhd(q, k, v, do, dk, dv)
+    B, N, H, d = q.shape
+    _check_rows(workspace, B, H, N, q.device, lead=(2,))
+    scale = default_scale(d) if scale is None else float(scale)
+    mp, mh = _mask_arg(mask, B, H, N, q.device)
+    with torch.cuda.device(q.device):
+        _call("attn_bwd_dkdv_masked", _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(workspace),
+              _ptr(dk), _ptr(dv), mp, mh, B, H, N, d, int(bool(causal)), scale, _dtype_code(q),
+              _stream(q.device))
+    return dk, dv
+
+
+def attn_bwd_dq_masked(q, k, v, do, workspace, dq, mask, causal: bool = True,
+                       scale: float | None = None):
+    """Stage 3 of attn_bwd_masked: dQ (workspace from attn_bwd_preprocess)."""
+    _check_bnhd(q, k, v, do, dq)
+    B, N, H, d = q.shape
+    _check_rows(workspace, B, H, N, q.device, lead=(2,))
+    scale = default_scale(d) if scale is None else float(scale)
+    mp, mh = _mask_arg(mask, B, H, N, q.device)
+    with torch.cuda.device(q.device):
+        _call("attn_bwd_dq_masked", _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(workspace),
+              _ptr(dq), mp, mh, B, H, N, d, int(bool(causal)), scale, _dtype_code(q),
+              _stream(q.device))
+    return dq

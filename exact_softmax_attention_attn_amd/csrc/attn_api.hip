@@ -196,6 +196,38 @@ int attn_bwd_masked(const void* Q, const void* K, const void* V, const void* O, 
   return finish(attn::launch_bwd_dq(a, s));
 }
 
+int attn_bwd_dkdv_masked(const void* Q, const void* K, const void* V, const void* dO,
+                         const void* workspace, void* dK, void* dV, const unsigned char* mask,
+                         int mask_heads, int B, int H, int N, int d, int causal, float scale,
+                         int dtype, void* stream) {
+  ATTN_TRY(check_ptrs({Q, K, V, dO, workspace, dK, dV}));
+  ATTN_TRY(check_sizes(B, H, N, d));
+  ATTN_TRY(check_scale_causal(scale, causal));
+  ATTN_TRY(check_dtype_dim(d, dtype));
+  ATTN_TRY(check_mask(mask, mask_heads, B, H, N));
+  attn::BwdArgs a =
+      make_bwd(Q, K, V, dO, workspace, nullptr, dK, dV, B, H, N, d, causal, scale, dtype);
+  a.mask = mask;
+  a.mask_heads = mask_heads;
+  return finish(attn::launch_bwd_dkdv(a, static_cast<hipStream_t>(stream)));
+}
+
+int attn_bwd_dq_masked(const void* Q, const void* K, const void* V, const void* dO,
+                       const void* workspace, void* dQ, const unsigned char* mask,
+                       int mask_heads, int B, int H, int N, int d, int causal, float scale,
+                       int dtype, void* stream) {
+  ATTN_TRY(check_ptrs({Q, K, V, dO, workspace, dQ}));
+  ATTN_TRY(check_sizes(B, H, N, d));
+  ATTN_TRY(check_scale_causal(scale, causal));
+  ATTN_TRY(check_dtype_dim(d, dtype));
+  ATTN_TRY(check_mask(mask, mask_heads, B, H, N));
+  attn::BwdArgs a =
+      make_bwd(Q, K, V, dO, workspace, dQ, nullptr, nullptr, B, H, N, d, causal, scale, dtype);
+  a.mask = mask;
+  a.mask_heads = mask_heads;
+  return finish(attn::launch_bwd_dq(a, static_cast<hipStream_t>(stream)));
+}
+
 const char* attn_status_string(int status) {
   switch (status) {
     case ATTN_OK: return "ok";

@@ -5,7 +5,7 @@ arithmetic lives here, so the oracle and the HIP path can both draw from it
 without sharing any of the method.
 
 The first five workloads stand in for the pages' own workloads (no dataset
-or trained weights exist for them); two more take c5's shape beyond square
+or trained weights exist for them); three more take c5's shape beyond square
 causal attention:
 
 * ``c1_tiny``  -- the toy of ddx issue #217's repro script: 3 sequences, 2
@@ -22,6 +22,9 @@ causal attention:
   bf16 in / fp32 accumulate, scale 1/sqrt(128).
 * ``c5_full`` -- c5_long with full (non-causal) attention.
 * ``c5_ragged`` -- c5_long at 16,383 tokens, a length no tile size divides.
+* ``c5_window`` -- c5_long under a block-sparse mask: each query block keeps
+  the 16 key blocks up to its own (a 2,048-token local window) and the first
+  block (attention sink), causal inside the window.
 
 Random draws use numpy's PCG64 ``default_rng(seed)`` in fp64, in the order
 Q, K, V, dO, each of shape [B, N, H, d]; Q/K/V are multiplied by ``qkv_std``.
@@ -37,7 +40,7 @@ import math
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "get", "make_inputs", "make_random", "bf16_round",
-           "MASK_BLOCK", "make_block_mask", "window_block_mask"]
+           "MASK_BLOCK", "make_block_mask", "window_block_mask", "workload_mask"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -53,6 +56,7 @@ class Workload:
     qkv: str = "normal"   # "normal" or "sin" (the issue #217 toy recipe)
     causal: bool = True
     description: str = ""
+    mask: str = ""        # "" (no block mask) or "window<W>": window_block_mask(N, W, 1)
 
     @property
     def shape(self):
@@ -76,6 +80,9 @@ WORKLOADS = (
              causal=False, description="c5_long without the causal mask"),
     Workload("c5_ragged", 1, 16, 16383, 128, 1.0 / math.sqrt(128), "bf16", qkv_std=0.5,
              description="c5_long one token shorter: ragged last tile everywhere"),
+    Workload("c5_window", 1, 16, 16384, 128, 1.0 / math.sqrt(128), "bf16", qkv_std=0.5,
+             mask="window16",
+             description="c5_long under a block mask: 2048-token local window + first block"),
 )
 
 
@@ -152,6 +159,15 @@ def window_block_mask(N: int, window_blocks: int, sink_blocks: int = 1) -> np.nd
     r = np.arange(nb)[:, None]
     c = np.arange(nb)[None, :]
     return (((c <= r) & (c > r - window_blocks)) | (c < sink_blocks)).astype(np.uint8)
+
+
+def workload_mask(w: Workload):
+    """The workload's block mask (uint8 [nb, nb], shared by every head) or None."""
+    if not w.mask:
+        return None
+    if w.mask.startswith("window"):
+        return window_block_mask(w.N, int(w.mask[len("window"):]), 1)
+    raise ValueError(w.mask)
 
 
 def make_random(B: int, H: int, N: int, d: int, dtype: str, seed: int = 0,

@@ -165,6 +165,18 @@ int attn_bwd_masked(const void* Q, const void* K, const void* V, const void* O, 
                     const unsigned char* mask, int mask_heads,
                     int B, int H, int N, int d, int causal, float scale, int dtype, void* stream);
 
+/* Stages 2 and 3 of attn_bwd_masked (stage 1 is attn_bwd_preprocess). */
+int attn_bwd_dkdv_masked(const void* Q, const void* K, const void* V, const void* dO,
+                         const void* workspace, void* dK, void* dV,
+                         const unsigned char* mask, int mask_heads,
+                         int B, int H, int N, int d, int causal, float scale, int dtype,
+                         void* stream);
+int attn_bwd_dq_masked(const void* Q, const void* K, const void* V, const void* dO,
+                       const void* workspace, void* dQ,
+                       const unsigned char* mask, int mask_heads,
+                       int B, int H, int N, int d, int causal, float scale, int dtype,
+                       void* stream);
+
 /* Static text for a status code ("ok", "invalid argument", ...). */
 const char* attn_status_string(int status);
 

@@ -31,9 +31,9 @@ def _declared():
 
 def test_header_declares_the_entry_points():
     assert _declared() == sorted([
-        "attn_bwd", "attn_bwd_dkdv", "attn_bwd_dq", "attn_bwd_masked", "attn_bwd_preprocess",
-        "attn_bwd_workspace_bytes", "attn_fwd_lse", "attn_fwd_lse_masked", "attn_last_error",
-        "attn_status_string"])
+        "attn_bwd", "attn_bwd_dkdv", "attn_bwd_dkdv_masked", "attn_bwd_dq", "attn_bwd_dq_masked",
+        "attn_bwd_masked", "attn_bwd_preprocess", "attn_bwd_workspace_bytes", "attn_fwd_lse",
+        "attn_fwd_lse_masked", "attn_last_error", "attn_status_string"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -151,6 +151,10 @@ def test_masked_entry_points_validate_the_mask(lib):
         assert call(FAKE, 1, scale=0.0) == 1
     p = list(b10); p[3] = NUL
     assert lib.attn_bwd_masked(*p, FAKE, 1, 1, 1, 8, 8, 1, 0.5, 0, NUL) == 1
+    assert lib.attn_bwd_dkdv_masked(*([FAKE] * 7), NUL, 1, 1, 1, 8, 8, 1, 0.5, 0, NUL) == 1
+    assert lib.attn_bwd_dkdv_masked(*([FAKE] * 7), FAKE, 2, 1, 1, 8, 8, 1, 0.5, 0, NUL) == 1
+    assert lib.attn_bwd_dq_masked(*([FAKE] * 6), FAKE, 1, 1, 1, 70000, 8, 1, 0.5, 0, NUL) == 2
+    assert lib.attn_bwd_dq_masked(*([FAKE] * 5), NUL, FAKE, 1, 1, 1, 8, 8, 1, 0.5, 0, NUL) == 1
     assert lib.attn_last_error() == b""
 
 

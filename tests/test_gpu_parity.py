@@ -164,7 +164,7 @@ def test_no_device_allocation_during_backward(B):
     assert abs(free1 - free0) < (2 << 20)
 
 
-@pytest.mark.parametrize("name", ["c5_long", "c5_full", "c5_ragged"])
+@pytest.mark.parametrize("name", ["c5_long", "c5_full", "c5_ragged", "c5_window"])
 def test_c5_full_size_sampled_against_oracle(B, name):
     """N = 16,384 (or 16,383), d = 128, bf16: sampled rows and columns of two heads."""
     import torch
@@ -173,8 +173,14 @@ def test_c5_full_size_sampled_against_oracle(B, name):
     x = workloads.make_inputs(w, seed=0)
     q, k, v, do = (_dev(x[n], w.dtype) for n in ("q", "k", "v", "do"))
     _say(f"{name} forward + backward on the GPU")
-    o, lse = B.attn_fwd_lse(q, k, v, causal=w.causal, scale=w.scale)
-    dq, dk, dv = B.attn_bwd(q, k, v, o, do, lse, causal=w.causal, scale=w.scale)
+    bm = workloads.workload_mask(w)
+    if bm is None:
+        o, lse = B.attn_fwd_lse(q, k, v, causal=w.causal, scale=w.scale)
+        dq, dk, dv = B.attn_bwd(q, k, v, o, do, lse, causal=w.causal, scale=w.scale)
+    else:
+        mask = torch.from_numpy(bm).cuda()
+        o, lse = B.attn_fwd_lse_masked(q, k, v, mask, causal=w.causal, scale=w.scale)
+        dq, dk, dv = B.attn_bwd_masked(q, k, v, o, do, lse, mask, causal=w.causal, scale=w.scale)
     torch.cuda.synchronize()
     rng = np.random.default_rng(5)
     N = w.N
@@ -184,7 +190,7 @@ def test_c5_full_size_sampled_against_oracle(B, name):
     for h in (0, 11):
         _say(f"{name} oracle sample head {h}")
         s = orc.attn_bwd_sampled(x["q"], x["k"], x["v"], x["do"], w.scale, w.causal, 0, h, rows, cols,
-                                 row_block=1024)
+                                 row_block=1024, block_mask=bm)
         got_dq = dq[0, rows, h].float().cpu().numpy()
         got_o = o[0, rows, h].float().cpu().numpy()
         got_dk = dk[0, cols, h].float().cpu().numpy()

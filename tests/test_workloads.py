@@ -10,7 +10,7 @@ from exact_softmax_attention_attn_amd import workloads
 def test_workloads_with_their_shapes():
     names = [w.name for w in workloads.WORKLOADS]
     assert names == ["c1_tiny", "c2_nanogpt_cpu", "c3_single_seq", "c4_batched", "c5_long",
-                     "c5_full", "c5_ragged"]
+                     "c5_full", "c5_ragged", "c5_window"]
     assert workloads.get("c1_tiny").shape == (3, 8, 2, 4)
     assert workloads.get("c2_nanogpt_cpu").shape == (12, 64, 4, 32)
     assert workloads.get("c3_single_seq").shape == (1, 256, 1, 64)
@@ -57,3 +57,20 @@ def test_bf16_round_is_nearest_even():
     assert got[3] == 1 + 2 ** -7
     assert got[4] == -2.5
     assert np.all(got.view(np.uint32) & 0xFFFF == 0)
+
+
+def test_block_mask_generators():
+    m = workloads.window_block_mask(1000, 3, 1)             # nb = 8
+    assert m.shape == (8, 8) and m.dtype == np.uint8
+    assert m[7].tolist() == [1, 0, 0, 0, 0, 1, 1, 1]        # sink + blocks 5..7
+    assert np.all(np.triu(m, 1) == 0)
+    r = workloads.make_block_mask(1000, 0.3, seed=1, heads=(2, 3), empty_rows=(2,))
+    assert r.shape == (2, 3, 8, 8)
+    assert np.all(r[..., 2, :] == 0)
+    assert np.all(r[..., 0, 0] == 1) and np.all(r[..., 5, 5] == 1)
+    np.testing.assert_array_equal(r, workloads.make_block_mask(1000, 0.3, seed=1, heads=(2, 3),
+                                                               empty_rows=(2,)))
+    w = workloads.get("c5_window")
+    wm = workloads.workload_mask(w)
+    assert wm.shape == (128, 128) and int(wm.sum(axis=1).max()) == 17   # 16 + the sink
+    assert workloads.workload_mask(workloads.get("c5_long")) is None
