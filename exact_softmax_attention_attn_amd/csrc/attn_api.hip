@@ -38,7 +38,7 @@ int check_sizes(int B, int H, int N, int d) {
 
 int check_dtype_dim(int d, int dtype) {
   if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
-  if (d > 128) return ATTN_ERR_UNSUPPORTED;
+  if (d > (dtype == ATTN_BF16 ? 256 : 128)) return ATTN_ERR_UNSUPPORTED;
   if (dtype == ATTN_F32 && d % 4 != 0) return ATTN_ERR_UNSUPPORTED;
   if (dtype == ATTN_BF16 && d % 8 != 0) return ATTN_ERR_UNSUPPORTED;
   return ATTN_OK;

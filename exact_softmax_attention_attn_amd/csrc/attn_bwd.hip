@@ -431,11 +431,13 @@ static hipError_t dq_go(const BwdArgs& a, hipStream_t stream) {
       if ((a).causal) {                                                               \
         if (bucket == 32) return FN<bf16, 32, true>(a, stream);                       \
         if (bucket == 64) return FN<bf16, 64, true>(a, stream);                       \
-        return FN<bf16, 128, true>(a, stream);                                        \
+        if (bucket == 128) return FN<bf16, 128, true>(a, stream);                     \
+        return FN<bf16, 256, true>(a, stream);                                        \
       }                                                                               \
       if (bucket == 32) return FN<bf16, 32, false>(a, stream);                        \
       if (bucket == 64) return FN<bf16, 64, false>(a, stream);                        \
-      return FN<bf16, 128, false>(a, stream);                                         \
+      if (bucket == 128) return FN<bf16, 128, false>(a, stream);                      \
+      return FN<bf16, 256, false>(a, stream);                                         \
     }                                                                                 \
     if ((a).causal) {                                                                 \
       if (bucket == 32) return FN<float, 32, true>(a, stream);                        \

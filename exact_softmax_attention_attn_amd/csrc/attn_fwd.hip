@@ -189,11 +189,13 @@ hipError_t launch_fwd_lse(const FwdArgs& a, hipStream_t stream) {
     if (a.causal) {
       if (bucket == 32) return fwd_go<bf16, 32, true>(a, stream);
       if (bucket == 64) return fwd_go<bf16, 64, true>(a, stream);
-      return fwd_go<bf16, 128, true>(a, stream);
+      if (bucket == 128) return fwd_go<bf16, 128, true>(a, stream);
+      return fwd_go<bf16, 256, true>(a, stream);
     }
     if (bucket == 32) return fwd_go<bf16, 32, false>(a, stream);
     if (bucket == 64) return fwd_go<bf16, 64, false>(a, stream);
-    return fwd_go<bf16, 128, false>(a, stream);
+    if (bucket == 128) return fwd_go<bf16, 128, false>(a, stream);
+    return fwd_go<bf16, 256, false>(a, stream);
   }
   if (a.causal) {
     if (bucket == 32) return fwd_go<float, 32, true>(a, stream);

@@ -245,15 +245,17 @@ template <int ROWS, int D> struct Tile<bf16, ROWS, D> {
   static constexpr int ELEMS = ROWS * D;
   static constexpr int BYTES = ELEMS * 2;
   static constexpr int CPR = D / 8;                       // chunks per row
-  static_assert(CPR >= 4 && (CPR & (CPR - 1)) == 0, "head-dim bucket must be 32, 64 or 128");
+  static_assert(CPR >= 4 && CPR <= 32 && (CPR & (CPR - 1)) == 0,
+                "head-dim bucket must be 32, 64, 128 or 256");
   bf16* p;
 
-  // Bank slot of (row, physical chunk) = (row % (16 / CPR)) * CPR + chunk.
-  // With row bits r3 r2 r1 r0: CPR 16 permutes by (r1 r0 r2 r3), CPR 8 by
-  // (r1 r2 r3), CPR 4 by (r2 r3); rows sharing a slot line (same r % (16/CPR))
-  // then differ in the chunk bits that each read group above spans.
+  // Bank slot of (row, physical chunk) = (row % (16 / CPR)) * CPR + chunk for
+  // CPR <= 16, and chunk % 16 for CPR 32 (a row is two 256-byte lines, so its
+  // slots repeat).  With row bits r3 r2 r1 r0: CPR 16 and 32 permute by
+  // (r1 r0 r2 r3), CPR 8 by (r1 r2 r3), CPR 4 by (r2 r3); rows sharing a slot
+  // line then differ in the chunk bits that each read group above spans.
   __host__ __device__ __forceinline__ static int swz(int r) {
-    if constexpr (CPR == 16) return ((r & 2) << 2) | ((r & 1) << 2) | ((r >> 1) & 2) | ((r >> 3) & 1);
+    if constexpr (CPR >= 16) return ((r & 2) << 2) | ((r & 1) << 2) | ((r >> 1) & 2) | ((r >> 3) & 1);
     else if constexpr (CPR == 8) return ((r & 2) << 1) | ((r >> 1) & 2) | ((r >> 3) & 1);
     else return ((r >> 1) & 2) | ((r >> 3) & 1);
   }

@@ -36,9 +36,10 @@ struct FwdArgs {
   int mask_heads = 1;
 };
 
-// Head dims are served by kernels compiled for 32, 64 or 128 columns; a
-// smaller d runs in the next bucket with the extra columns read as zero.
-inline int head_dim_bucket(int d) { return d <= 32 ? 32 : (d <= 64 ? 64 : 128); }
+// Head dims are served by kernels compiled for 32, 64, 128 or (bf16) 256
+// columns; a smaller d runs in the next bucket with the extra columns read as
+// zero.
+inline int head_dim_bucket(int d) { return d <= 32 ? 32 : (d <= 64 ? 64 : (d <= 128 ? 128 : 256)); }
 
 hipError_t launch_bwd_preprocess(const void* O, const void* dO, const float* L, float* ws, int B,
                                  int H, int N, int d, int dtype, hipStream_t stream);

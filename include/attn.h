@@ -46,8 +46,8 @@
  *    outputs are untouched.  ATTN_ERR_HIP means a launch failed; the text of
  *    the HIP error is returned by attn_last_error() on the calling thread.
  *    Non-finite inputs are not checked; they propagate.
- *  - Limits.  B, H, N, d >= 1; d <= 128; d % 4 == 0 (f32) or d % 8 == 0
- *    (bf16); B*N*H*d and B*H*N must fit in int32 (ATTN_ERR_UNSUPPORTED
+ *  - Limits.  B, H, N, d >= 1; d <= 128 (f32) or d <= 256 (bf16); d % 4 == 0
+ *    (f32) or d % 8 == 0 (bf16); B*N*H*d and B*H*N must fit in int32 (ATTN_ERR_UNSUPPORTED
  *    otherwise); scale finite and > 0.  causal is 1 (keep j <= i) or 0 (keep
  *    every pair).
  */

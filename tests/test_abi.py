@@ -117,7 +117,8 @@ def test_validation_rejects_bad_arguments_without_launching(lib):
         assert _fwd(lib, f5, **kw) == 1
         assert _bwd(lib, b10, **kw) == 1
     # unsupported head dims and dtypes
-    for kw in ({"d": 136}, {"d": 6}, {"d": 4, "dtype": 1}, {"d": 12, "dtype": 1}, {"dtype": 2},
+    for kw in ({"d": 136}, {"d": 264, "dtype": 1}, {"d": 6}, {"d": 4, "dtype": 1},
+               {"d": 12, "dtype": 1}, {"dtype": 2},
                {"dtype": -1}, {"B": 70000}, {"H": 70000}, {"B": 65535, "H": 65535, "N": 1024}):
         assert _fwd(lib, f5, **kw) == 2, kw
         assert _bwd(lib, b10, **kw) == 2, kw
@@ -128,7 +129,7 @@ def test_validation_rejects_bad_arguments_without_launching(lib):
     assert lib.attn_bwd_dkdv(*([FAKE] * 6), NUL, 1, 1, 8, 8, 1, 0.5, 0, NUL) == 1
     assert lib.attn_bwd_dkdv(*([FAKE] * 7), 1, 1, 8, 8, 1, 0.0, 0, NUL) == 1
     assert lib.attn_bwd_dq(*([FAKE] * 5), NUL, 1, 1, 8, 8, 1, 0.5, 0, NUL) == 1
-    assert lib.attn_bwd_dq(*([FAKE] * 6), 1, 1, 8, 256, 1, 0.5, 1, NUL) == 2
+    assert lib.attn_bwd_dq(*([FAKE] * 6), 1, 1, 8, 264, 1, 0.5, 1, NUL) == 2
     assert lib.attn_last_error() == b""
 
 

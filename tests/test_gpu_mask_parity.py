@@ -68,6 +68,7 @@ CASES = [
     (1, 2, 300, 64, "f32", True, "random_heads"),        # generic kernels, float32
     (2, 1, 260, 32, "f32", False, "random_empty"),
     (1, 2, 257, 40, "bf16", False, "random"),            # generic bf16 (odd head dim)
+    (1, 2, 400, 256, "bf16", True, "random_empty"),      # head dim 256
 ]
 
 

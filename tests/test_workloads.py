@@ -10,7 +10,7 @@ from exact_softmax_attention_attn_amd import workloads
 def test_workloads_with_their_shapes():
     names = [w.name for w in workloads.WORKLOADS]
     assert names == ["c1_tiny", "c2_nanogpt_cpu", "c3_single_seq", "c4_batched", "c5_long",
-                     "c5_full", "c5_ragged", "c5_window"]
+                     "c5_full", "c5_ragged", "c5_window", "c5_d256"]
     assert workloads.get("c1_tiny").shape == (3, 8, 2, 4)
     assert workloads.get("c2_nanogpt_cpu").shape == (12, 64, 4, 32)
     assert workloads.get("c3_single_seq").shape == (1, 256, 1, 64)
@@ -19,6 +19,7 @@ def test_workloads_with_their_shapes():
     assert workloads.get("c5_full").shape == (1, 16384, 16, 128)
     assert not workloads.get("c5_full").causal
     assert workloads.get("c5_ragged").shape == (1, 16383, 16, 128)
+    assert workloads.get("c5_d256").shape == (1, 16384, 8, 256)
     assert all(workloads.get(n).causal for n in names if n != "c5_full")
     for w in workloads.WORKLOADS:
         assert math.isclose(w.scale, 1 / math.sqrt(w.d)) or w.name == "c1_tiny"
