@@ -86,7 +86,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const unsigned char* __restrict__ mask, int mask_heads) {
   using M = Mma<T>;
   using frag = typename M::frag;
-  constexpr int BKV = 128, BQ = 64, KS = D / M::K, MT = D / 32, RS = 32 / M::K;
+  constexpr int BKV = 128, BQ = 64, KS = D / M::K, RS = 32 / M::K;
+  // Head dims above 128 (bf16, 256 bucket): each workgroup accumulates DA = 128
+  // of the output's columns (part = which DA) and recomputes S and dP over the
+  // full head dim, so a (b, h) runs on D / DA workgroups per block; their
+  // register footprint then stays that of the 128 bucket.
+  constexpr int DA = D > 128 ? 128 : D, MA = DA / 32, NSPLIT = D / DA;
   using QT = Tile<T, BQ, D>;
   struct __align__(16) Buf {
     T q[QT::ELEMS];
@@ -98,7 +103,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
   const BlockOrder bo = block_order();
-  const int jb = bo.rank, head = bo.head, b = bo.b;   // rank 0 = longest walk
+  const int jb = bo.rank, head = bo.head / NSPLIT, b = bo.b;   // rank 0 = longest walk
+  const int dofs = (bo.head % NSPLIT) * DA;          // first output column of this workgroup
   const long rs = (long)H * d;                       // elements between positions
   const long base = ((long)b * N * H + head) * d;    // (b, 0, head, 0)
   const float* Lh = L2 + ((long)b * H + head) * N;
@@ -111,9 +117,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   load_row_frags<T, D>(kf, K + base, rs, kv, N, d, h);
   load_row_frags<T, D>(vf, V + base, rs, kv, N, d, h);
 
-  f32x16 dv_acc[MT], dk_acc[MT];
+  f32x16 dv_acc[MA], dk_acc[MA];
 #pragma unroll
-  for (int i = 0; i < MT; ++i) { dv_acc[i] = zero16(); dk_acc[i] = zero16(); }
+  for (int i = 0; i < MA; ++i) { dv_acc[i] = zero16(); dk_acc[i] = zero16(); }
 
   const int nqt = (N + BQ - 1) / BQ;
   const int qt0 = CAUSAL ? kvb / BQ : 0;
@@ -154,10 +160,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     }
   };
 
-  auto body = [&](const Buf& B, int q0, auto masked_c) ATTN_INLINE {
-    constexpr bool MASKED = decltype(masked_c)::value;
+  // One body for masked and unmasked tiles, its two sub-tiles in a loop: at
+  // head dim 256 two inlined copies would not fit in registers.
+  auto body = [&](const Buf& B, int q0, bool MASKED) ATTN_INLINE {
     const QT qt_{const_cast<T*>(B.q)}, ot_{const_cast<T*>(B.o)};
-#pragma unroll
+#pragma unroll 1
     for (int st = 0; st < BQ / 32; ++st) {
       const int qa = q0 + st * 32;                 // first query row of the sub-tile
       if (MASKED && qa + 31 < kv0) continue;       // every pair above the diagonal
@@ -191,8 +198,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 #pragma unroll
       for (int ss = 0; ss < RS; ++ss)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          dv_acc[mt] = M::mma(ot_.along_rows(mt * 32 + l32, st * 32, ss, h), bp[ss], dv_acc[mt]);
+        for (int mt = 0; mt < MA; ++mt)
+          dv_acc[mt] = M::mma(ot_.along_rows(dofs + mt * 32 + l32, st * 32, ss, h), bp[ss],
+                              dv_acc[mt]);
       // dS = P o (dP - D)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -207,8 +215,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 #pragma unroll
       for (int ss = 0; ss < RS; ++ss)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          dk_acc[mt] = M::mma(qt_.along_rows(mt * 32 + l32, st * 32, ss, h), bds[ss], dk_acc[mt]);
+        for (int mt = 0; mt < MA; ++mt)
+          dk_acc[mt] = M::mma(qt_.along_rows(dofs + mt * 32 + l32, st * 32, ss, h), bds[ss],
+                              dk_acc[mt]);
     }
   };
 
@@ -216,10 +225,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   auto step = [&](const Buf& cur, Buf& nxt, int p) ATTN_INLINE {
     const int q0 = tile_at(p) * BQ;
     if (p + 1 < ntiles) fill(nxt, tile_at(p + 1));
-    if (CAUSAL && q0 < kvb + BKV)
-      body(cur, q0, bool_c<true>{});
-    else
-      body(cur, q0, bool_c<false>{});
+    body(cur, q0, CAUSAL && q0 < kvb + BKV);
     wait_async_fills();
     __syncthreads();
   };
@@ -235,9 +241,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   }
 
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    store_acc_transposed<T>(dv_acc[mt], dV + base, rs, kv0, mt * 32, N, d, 1.f, lane);
-    store_acc_transposed<T>(dk_acc[mt], dK + base, rs, kv0, mt * 32, N, d, scale, lane);
+  for (int mt = 0; mt < MA; ++mt) {
+    store_acc_transposed<T>(dv_acc[mt], dV + base, rs, kv0, dofs + mt * 32, N, d, 1.f, lane);
+    store_acc_transposed<T>(dk_acc[mt], dK + base, rs, kv0, dofs + mt * 32, N, d, scale, lane);
   }
 }
 
@@ -257,7 +263,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
     const unsigned char* __restrict__ mask, int mask_heads) {
   using M = Mma<T>;
   using frag = typename M::frag;
-  constexpr int BQ = 128, BKV = 64, KS = D / M::K, MT = D / 32, RS = 32 / M::K;
+  constexpr int BQ = 128, BKV = 64, KS = D / M::K, RS = 32 / M::K;
+  // Head dims above 128 (bf16, 256 bucket): each workgroup accumulates DA = 128
+  // of the output's columns (part = which DA) and recomputes S and dP over the
+  // full head dim, so a (b, h) runs on D / DA workgroups per block; their
+  // register footprint then stays that of the 128 bucket.
+  constexpr int DA = D > 128 ? 128 : D, MA = DA / 32, NSPLIT = D / DA;
   using KT = Tile<T, BKV, D>;
   struct __align__(16) Buf {
     T k[KT::ELEMS];
@@ -269,7 +280,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
   const int nqb = gridDim.x;
   const BlockOrder bo = block_order();
   const int ib = CAUSAL ? (nqb - 1 - bo.rank) : bo.rank;   // longest first
-  const int head = bo.head, b = bo.b;
+  const int head = bo.head / NSPLIT, b = bo.b;
+  const int dofs = (bo.head % NSPLIT) * DA;          // first output column of this workgroup
   const long rs = (long)H * d;
   const long base = ((long)b * N * H + head) * d;
   const float* Lh = L2 + ((long)b * H + head) * N;
@@ -284,9 +296,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
   const float Lq = q < N ? Lh[q] : -__builtin_inff();   // -L2 stored; padded rows: P = 0
   const float Dq = q < N ? Dh[q] : 0.f;                  // -D stored
 
-  f32x16 acc[MT];
+  f32x16 acc[MA];
 #pragma unroll
-  for (int i = 0; i < MT; ++i) acc[i] = zero16();
+  for (int i = 0; i < MA; ++i) acc[i] = zero16();
 
   const int kv_end = CAUSAL ? min(N, qb + BQ) : N;
   const int nkt = (kv_end + BKV - 1) / BKV;
@@ -349,8 +361,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
 #pragma unroll
       for (int ss = 0; ss < RS; ++ss)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          acc[mt] = M::mma(kt_.along_rows(mt * 32 + l32, st * 32, ss, h), bds[ss], acc[mt]);
+        for (int mt = 0; mt < MA; ++mt)
+          acc[mt] = M::mma(kt_.along_rows(dofs + mt * 32 + l32, st * 32, ss, h), bds[ss], acc[mt]);
     }
   };
 
@@ -376,8 +388,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
     if (p + 1 < ntiles) step(bufB, bufA, p + 1);
   }
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-    store_acc_transposed<T>(acc[mt], dQ + base, rs, qw, mt * 32, N, d, scale, lane);
+  for (int mt = 0; mt < MA; ++mt)
+    store_acc_transposed<T>(acc[mt], dQ + base, rs, qw, dofs + mt * 32, N, d, scale, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -402,9 +414,12 @@ hipError_t launch_bwd_preprocess(const void* O, const void* dO, const float* L, 
 
 static inline long rows_of(const BwdArgs& a) { return (long)a.B * a.H * a.N; }
 
+// the 256 bucket runs two workgroups per block, one per 128 output columns
+template <int D> constexpr int column_parts() { return D > 128 ? D / 128 : 1; }
+
 template <typename T, int D, bool C>
 static hipError_t dkdv_go(const BwdArgs& a, hipStream_t stream) {
-  dim3 grid((a.N + 127) / 128, a.H, a.B);
+  dim3 grid((a.N + 127) / 128, a.H * column_parts<D>(), a.B);
   hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, C>), grid, dim3(256), 0, stream,
                      static_cast<const T*>(a.Q), static_cast<const T*>(a.K),
                      static_cast<const T*>(a.V), static_cast<const T*>(a.dO), a.Dws + rows_of(a), a.Dws,
@@ -415,7 +430,7 @@ static hipError_t dkdv_go(const BwdArgs& a, hipStream_t stream) {
 
 template <typename T, int D, bool C>
 static hipError_t dq_go(const BwdArgs& a, hipStream_t stream) {
-  dim3 grid((a.N + 127) / 128, a.H, a.B);
+  dim3 grid((a.N + 127) / 128, a.H * column_parts<D>(), a.B);
   hipLaunchKernelGGL((bwd_dq_kernel<T, D, C>), grid, dim3(256), 0, stream,
                      static_cast<const T*>(a.Q), static_cast<const T*>(a.K),
                      static_cast<const T*>(a.V), static_cast<const T*>(a.dO), a.Dws + rows_of(a), a.Dws,

@@ -28,7 +28,11 @@ __global__ __launch_bounds__(256, 1) void fwd_lse_kernel(const T* __restrict__ Q
                                                          int mask_heads) {
   using M = Mma<T>;
   using frag = typename M::frag;
-  constexpr int BQ = 128, BKV = 64, KS = D / M::K, MT = D / 32, RS = 32 / M::K;
+  constexpr int BQ = 128, BKV = 64, KS = D / M::K, RS = 32 / M::K;
+  // Head dims above 128 (bf16, 256 bucket): each workgroup accumulates DA = 128
+  // of O's columns (part = which DA) and recomputes the scores over the full
+  // head dim; the part-0 workgroup writes L.
+  constexpr int DA = D > 128 ? 128 : D, MA = DA / 32, NSPLIT = D / DA;
   using KT = Tile<T, BKV, D>;
   struct __align__(16) Buf {
     T k[KT::ELEMS];
@@ -40,7 +44,8 @@ __global__ __launch_bounds__(256, 1) void fwd_lse_kernel(const T* __restrict__ Q
   const int nqb = gridDim.x;
   const BlockOrder bo = block_order();
   const int ib = CAUSAL ? (nqb - 1 - bo.rank) : bo.rank;   // longest first
-  const int head = bo.head, b = bo.b;
+  const int head = bo.head / NSPLIT, b = bo.b;
+  const int dofs = (bo.head % NSPLIT) * DA;          // first output column of this workgroup
   const long rs = (long)H * d;
   const long base = ((long)b * N * H + head) * d;
 
@@ -50,9 +55,9 @@ __global__ __launch_bounds__(256, 1) void fwd_lse_kernel(const T* __restrict__ Q
   frag qf[KS];
   load_row_frags<T, D>(qf, Q + base, rs, q, N, d, h);
 
-  f32x16 acc[MT];
+  f32x16 acc[MA];
 #pragma unroll
-  for (int i = 0; i < MT; ++i) acc[i] = zero16();
+  for (int i = 0; i < MA; ++i) acc[i] = zero16();
   float m = -1e30f;   // running max of the scaled scores, log2 units
   float l = 0.f;      // running sum of exp2(score - m)
 
@@ -120,7 +125,7 @@ __global__ __launch_bounds__(256, 1) void fwd_lse_kernel(const T* __restrict__ Q
         l *= alpha;
         m = m_new;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;
+        for (int mt = 0; mt < MA; ++mt) acc[mt] *= alpha;
       }
       float sum = 0.f;
 #pragma unroll
@@ -135,8 +140,8 @@ __global__ __launch_bounds__(256, 1) void fwd_lse_kernel(const T* __restrict__ Q
       for (int ss = 0; ss < RS; ++ss) {
         const frag bp = M::pack(s, ss);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          acc[mt] = M::mma(vt_.along_rows(mt * 32 + l32, st * 32, ss, h), bp, acc[mt]);
+        for (int mt = 0; mt < MA; ++mt)
+          acc[mt] = M::mma(vt_.along_rows(dofs + mt * 32 + l32, st * 32, ss, h), bp, acc[mt]);
       }
     }
   };
@@ -165,16 +170,16 @@ __global__ __launch_bounds__(256, 1) void fwd_lse_kernel(const T* __restrict__ Q
   // a row that keeps no key ends with l = 0: O = 0, L = -inf
   const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-    store_acc_transposed<T>(acc[mt], O + base, rs, qw, mt * 32, N, d, inv, lane);
-  if (h == 0 && q < N)
+  for (int mt = 0; mt < MA; ++mt)
+    store_acc_transposed<T>(acc[mt], O + base, rs, qw, dofs + mt * 32, N, d, inv, lane);
+  if (h == 0 && q < N && dofs == 0)
     L[((long)b * H + head) * N + q] =
         l > 0.f ? (m + log2f(l)) * 0.69314718055994531f : -__builtin_inff();
 }
 
 template <typename T, int D, bool C>
 static hipError_t fwd_go(const FwdArgs& a, hipStream_t stream) {
-  dim3 grid((a.N + 127) / 128, a.H, a.B);
+  dim3 grid((a.N + 127) / 128, a.H * (D > 128 ? D / 128 : 1), a.B);
   hipLaunchKernelGGL((fwd_lse_kernel<T, D, C>), grid, dim3(256), 0, stream,
                      static_cast<const T*>(a.Q), static_cast<const T*>(a.K),
                      static_cast<const T*>(a.V), static_cast<T*>(a.O), a.L, a.H, a.N, a.d,
