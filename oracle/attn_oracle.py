@@ -71,6 +71,8 @@ __all__ = [
     "loss_value",
     "pair_count",
     "bwd_flops",
+    "head_bwd_bwd",
+    "attn_bwd_bwd",
 ]
 
 
@@ -356,6 +358,65 @@ def attn_bwd_sampled(Q, K, V, dO, scale: float, causal: bool, b: int, h: int,
         dk[t] = scale * (ds_col @ q)
     out["dK"] = dk
     out["dV"] = dv
+    return out
+
+
+# --------------------------------------------------------------------------
+# Backward of the backward ("FlashBoB", abstract: exact differentiation
+# through the backward pass; two row-wise scalars determine all outputs
+# through affine transformations).  Given cotangents gQ, gK, gV of the
+# backward's outputs dQ, dK, dV, return the gradients of
+#     l2 = <gQ, dQ> + <gK, dK> + <gV, dV>
+# with respect to Q, K, V and dO.  Written out from the chain rule:
+#   <gV, dV> = <P, A>,   A = dO gV^T
+#   <gQ, dQ> + <gK, dK> = <dS, G>,   G = scale (gQ K^T + Q gK^T)
+# so l2 = sum_ij P_ij (A_ij + (dP_ij - D_i) G_ij), with D_i = sum_j P_ij dP_ij.
+#   d l2 / d dP = W = P o (G - r),   r_i = sum_j P_ij G_ij
+#   d l2 / d P  = A + (dP - D) o (G - r) - D r   (the last term is constant
+#                 along a row and cancels in the softmax backward), so
+#   d l2 / d S  = dS2 = P o (Psi - E),  Psi = A + (dP - D) o (G - r),
+#                 E_i = sum_j P_ij Psi_ij
+# and, with S = scale Q K^T, dP = dO V^T, A = dO gV^T and G as above:
+#   hQ = scale (dS2 K + dS gK),   hK = scale (dS2^T Q + dS^T gQ),
+#   hV = W^T dO,                  hdO = P gV + W V.
+# r and E are the two row scalars.
+# --------------------------------------------------------------------------
+
+def head_bwd_bwd(q, k, v, do, gq, gk, gv, scale: float, causal: bool, block_mask=None,
+                 mask_block: int = MASK_BLOCK):
+    """One (batch, head): hQ, hK, hV, hdO [N, d] and the row scalars r, E [N]."""
+    _, _, p = head_forward(q, k, v, scale, causal, block_mask, mask_block)
+    dp = do @ v.T
+    ds, d = softmax_backward(p, dp)
+    g = scale * (gq @ k.T + q @ gk.T)
+    a = do @ gv.T
+    r = (p * g).sum(axis=1)
+    w = p * (g - r[:, None])
+    psi = a + (dp - d[:, None]) * (g - r[:, None])
+    e = (p * psi).sum(axis=1)
+    ds2 = p * (psi - e[:, None])
+    hq = scale * (ds2 @ k + ds @ gk)
+    hk = scale * (ds2.T @ q + ds.T @ gq)
+    hv = w.T @ do
+    hdo = p @ gv + w @ v
+    return hq, hk, hv, hdo, r, e
+
+
+def attn_bwd_bwd(Q, K, V, dO, gQ, gK, gV, scale: float, causal: bool = True, block_mask=None,
+                 mask_block: int = MASK_BLOCK):
+    """hQ, hK, hV, hdO [B, N, H, d] and r, E [B, H, N] for every (batch, head)."""
+    X = [_f64(t) for t in (Q, K, V, dO, gQ, gK, gV)]
+    B, N, H, _ = X[0].shape
+    out = {n: np.empty_like(X[i]) for n, i in (("hQ", 0), ("hK", 1), ("hV", 2), ("hdO", 3))}
+    out["r"] = np.empty((B, H, N))
+    out["E"] = np.empty((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            res = head_bwd_bwd(*(t[b, :, h] for t in X), scale, causal,
+                               _head_mask(block_mask, b, h), mask_block)
+            for n, x in zip(("hQ", "hK", "hV", "hdO"), res[:4]):
+                out[n][b, :, h] = x
+            out["r"][b, h], out["E"][b, h] = res[4], res[5]
     return out
 
 
