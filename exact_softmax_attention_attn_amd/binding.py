@@ -40,6 +40,8 @@ _SIGNATURES = {
                                   _I, _I, _I, _I, _I, _F, _I, _P]),
     "attn_bwd_dq_masked": (_I, [_P, _P, _P, _P, _P, _P, _P, _I,
                                 _I, _I, _I, _I, _I, _F, _I, _P]),
+    "attn_bwd_bwd_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
+    "attn_bwd_bwd": (_I, [_P] * 14 + [_I, _I, _I, _I, _I, _F, _I, _P]),
     "attn_status_string": (ctypes.c_char_p, [_I]),
     "attn_last_error": (ctypes.c_char_p, []),
 }
@@ -278,3 +280,27 @@ def attn_bwd_dq_masked(q, k, v, do, workspace, dq, mask, causal: bool = True,
               _ptr(dq), mp, mh, B, H, N, d, int(bool(causal)), scale, _dtype_code(q),
               _stream(q.device))
     return dq
+
+
+def attn_bwd_bwd(q, k, v, o, do, lse, gq, gk, gv, causal: bool = True,
+                 scale: float | None = None, hq=None, hk=None, hv=None, hdo=None,
+                 workspace=None):
+    """Gradients of <gQ,dQ> + <gK,dK> + <gV,dV> w.r.t. Q, K, V, dO: (hQ, hK, hV, hdO).
+    workspace: [4, B, H, N] float32 (-D, -L log2(e), r, E)."""
+    _check_bnhd(q, k, v, o, do, gq, gk, gv)
+    B, N, H, d = q.shape
+    _check_rows(lse, B, H, N, q.device)
+    scale = default_scale(d) if scale is None else float(scale)
+    hq = torch.empty_like(q) if hq is None else hq
+    hk = torch.empty_like(q) if hk is None else hk
+    hv = torch.empty_like(q) if hv is None else hv
+    hdo = torch.empty_like(q) if hdo is None else hdo
+    _check_bnhd(q, hq, hk, hv, hdo)
+    if workspace is None:
+        workspace = torch.empty((4, B, H, N), dtype=torch.float32, device=q.device)
+    _check_rows(workspace, B, H, N, q.device, lead=(4,))
+    with torch.cuda.device(q.device):
+        _call("attn_bwd_bwd", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(gq),
+              _ptr(gk), _ptr(gv), _ptr(hq), _ptr(hk), _ptr(hv), _ptr(hdo), _ptr(workspace),
+              B, H, N, d, int(bool(causal)), scale, _dtype_code(q), _stream(q.device))
+    return hq, hk, hv, hdo

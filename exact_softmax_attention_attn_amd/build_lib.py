@@ -17,7 +17,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libattn.so")
-SOURCES = ("attn_api.hip", "attn_fwd.hip", "attn_fwd_pipe.hip", "attn_bwd.hip", "attn_bwd_pipe.hip")
+SOURCES = ("attn_api.hip", "attn_fwd.hip", "attn_fwd_pipe.hip", "attn_bwd.hip", "attn_bwd_pipe.hip",
+           "attn_bob.hip")
 # The pipelined kernels keep long-lived operands in AGPRs (pinned in the
 # source) and want every MFMA result and accumulator in VGPRs, where the VALU
 # can read them without copies.

@@ -228,6 +228,30 @@ int attn_bwd_dq_masked(const void* Q, const void* K, const void* V, const void* 
   return finish(attn::launch_bwd_dq(a, static_cast<hipStream_t>(stream)));
 }
 
+size_t attn_bwd_bwd_workspace_bytes(int B, int H, int N, int d) {
+  if (check_sizes(B, H, N, d) != ATTN_OK) return 0;
+  return 4 * (size_t)B * (size_t)H * (size_t)N * sizeof(float);
+}
+
+int attn_bwd_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                 const float* L, const void* gQ, const void* gK, const void* gV, void* hQ,
+                 void* hK, void* hV, void* hdO, void* workspace, int B, int H, int N, int d,
+                 int causal, float scale, int dtype, void* stream) {
+  ATTN_TRY(check_ptrs({Q, K, V, O, dO, L, gQ, gK, gV, hQ, hK, hV, hdO, workspace}));
+  ATTN_TRY(check_sizes(B, H, N, d));
+  ATTN_TRY(check_scale_causal(scale, causal));
+  ATTN_TRY(check_dtype_dim(d, dtype));
+  if (d > (dtype == ATTN_BF16 ? 128 : 64)) return ATTN_ERR_UNSUPPORTED;
+  attn::BobArgs a;
+  a.Q = Q; a.K = K; a.V = V; a.O = O; a.dO = dO; a.L = L;
+  a.gQ = gQ; a.gK = gK; a.gV = gV;
+  a.hQ = hQ; a.hK = hK; a.hV = hV; a.hdO = hdO;
+  a.ws = static_cast<float*>(workspace);
+  a.B = B; a.H = H; a.N = N; a.d = d;
+  a.causal = causal; a.scale = scale; a.dtype = dtype;
+  return finish(attn::launch_bwd_bwd(a, static_cast<hipStream_t>(stream)));
+}
+
 const char* attn_status_string(int status) {
   switch (status) {
     case ATTN_OK: return "ok";

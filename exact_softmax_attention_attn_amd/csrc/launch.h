@@ -36,6 +36,29 @@ struct FwdArgs {
   int mask_heads = 1;
 };
 
+// Backward of the backward: forward inputs, the output cotangent dO and the
+// first backward's cotangents gQ, gK, gV -> hQ, hK, hV, hdO.
+struct BobArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const void* O;
+  const void* dO;
+  const float* L;
+  const void* gQ;
+  const void* gK;
+  const void* gV;
+  void* hQ;
+  void* hK;
+  void* hV;
+  void* hdO;
+  float* ws;   // -D, -L log2(e), r, E, each [B, H, N]
+  int B, H, N, d;
+  int causal;
+  float scale;
+  int dtype;
+};
+
 // Head dims are served by kernels compiled for 32, 64, 128 or (bf16) 256
 // columns; a smaller d runs in the next bucket with the extra columns read as
 // zero.
@@ -49,5 +72,6 @@ hipError_t launch_fwd_lse(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dkdv_bf16_pipe(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dq_bf16_pipe(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_lse_bf16_pipe(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_bwd(const BobArgs& a, hipStream_t stream);
 
 }  // namespace attn

@@ -41,7 +41,8 @@ import math
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "get", "make_inputs", "make_random", "bf16_round",
-           "MASK_BLOCK", "make_block_mask", "window_block_mask", "workload_mask"]
+           "MASK_BLOCK", "make_block_mask", "window_block_mask", "workload_mask",
+           "make_cotangents"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -163,6 +164,14 @@ def window_block_mask(N: int, window_blocks: int, sink_blocks: int = 1) -> np.nd
     r = np.arange(nb)[:, None]
     c = np.arange(nb)[None, :]
     return (((c <= r) & (c > r - window_blocks)) | (c < sink_blocks)).astype(np.uint8)
+
+
+def make_cotangents(B: int, H: int, N: int, d: int, dtype: str, seed: int = 0) -> dict:
+    """Cotangents gQ, gK, gV of the backward's outputs, ~ N(0, 1) [B, N, H, d]
+    (PCG64 ``default_rng(seed + 1000)``, drawn in that order), cast like inputs."""
+    rng = np.random.default_rng(seed + 1000)
+    shape = (B, N, H, d)
+    return {n: _cast(rng.standard_normal(shape), dtype) for n in ("gq", "gk", "gv")}
 
 
 def workload_mask(w: Workload):

@@ -177,6 +177,33 @@ int attn_bwd_dq_masked(const void* Q, const void* K, const void* V, const void* 
                        int B, int H, int N, int d, int causal, float scale, int dtype,
                        void* stream);
 
+/*
+ * Backward of the backward.  The first backward maps (Q, K, V, dO) to
+ * (dQ, dK, dV); given cotangents gQ, gK, gV of its outputs, this returns the
+ * gradients of  l2 = <gQ, dQ> + <gK, dK> + <gV, dV>  with respect to Q, K, V
+ * and dO (exact differentiation through the backward pass, as in the FlashBoB
+ * paper's abstract: two row-wise scalars fix every output).  With P, dP, D
+ * and dS as in attn_bwd, G = scale (gQ K^T + Q gK^T), A = dO gV^T,
+ *   r_i = sum_j P_ij G_ij,   E_i = sum_j (P_ij A_ij + dS_ij G_ij),
+ *   W = P o (G - r),         dS2 = P o (A + (dP - D) o (G - r) - E),
+ *   hQ = scale (dS2 K + dS gK),  hK = scale (dS2^T Q + dS^T gQ),
+ *   hV = W^T dO,                 hdO = P gV + W V.
+ *   in : Q, K, V, O, dO, gQ, gK, gV [B, N, H, d] (dtype); L [B, H, N] float32
+ *        from attn_fwd_lse
+ *   out: hQ, hK, hV, hdO [B, N, H, d] (dtype)
+ *   workspace: >= attn_bwd_bwd_workspace_bytes(B, H, N, d) bytes, 16-byte
+ *        aligned; overwritten with -D, -L log2(e), r and E.
+ * Four launches on one stream: the preprocess, a query-block pass for r and
+ * E, a key-block pass for hK, hV and a query-block pass for hQ, hdO; no N x N
+ * array in memory.  Limits beyond the shared ones: d <= 128 (bf16) or d <= 64
+ * (f32), ATTN_ERR_UNSUPPORTED otherwise.
+ */
+size_t attn_bwd_bwd_workspace_bytes(int B, int H, int N, int d);
+int attn_bwd_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                 const float* L, const void* gQ, const void* gK, const void* gV,
+                 void* hQ, void* hK, void* hV, void* hdO, void* workspace,
+                 int B, int H, int N, int d, int causal, float scale, int dtype, void* stream);
+
 /* Static text for a status code ("ok", "invalid argument", ...). */
 const char* attn_status_string(int status);
 

@@ -31,9 +31,10 @@ def _declared():
 
 def test_header_declares_the_entry_points():
     assert _declared() == sorted([
-        "attn_bwd", "attn_bwd_dkdv", "attn_bwd_dkdv_masked", "attn_bwd_dq", "attn_bwd_dq_masked",
-        "attn_bwd_masked", "attn_bwd_preprocess", "attn_bwd_workspace_bytes", "attn_fwd_lse",
-        "attn_fwd_lse_masked", "attn_last_error", "attn_status_string"])
+        "attn_bwd", "attn_bwd_bwd", "attn_bwd_bwd_workspace_bytes", "attn_bwd_dkdv",
+        "attn_bwd_dkdv_masked", "attn_bwd_dq", "attn_bwd_dq_masked", "attn_bwd_masked",
+        "attn_bwd_preprocess", "attn_bwd_workspace_bytes", "attn_fwd_lse", "attn_fwd_lse_masked",
+        "attn_last_error", "attn_status_string"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -156,6 +157,26 @@ def test_masked_entry_points_validate_the_mask(lib):
     assert lib.attn_bwd_dkdv_masked(*([FAKE] * 7), FAKE, 2, 1, 1, 8, 8, 1, 0.5, 0, NUL) == 1
     assert lib.attn_bwd_dq_masked(*([FAKE] * 6), FAKE, 1, 1, 1, 70000, 8, 1, 0.5, 0, NUL) == 2
     assert lib.attn_bwd_dq_masked(*([FAKE] * 5), NUL, FAKE, 1, 1, 1, 8, 8, 1, 0.5, 0, NUL) == 1
+    assert lib.attn_last_error() == b""
+
+
+def test_bwd_bwd_entry_point_validates(lib):
+    p14 = [FAKE] * 14
+
+    def call(ptrs=p14, B=1, H=1, N=8, d=8, causal=1, scale=0.5, dtype=0):
+        return lib.attn_bwd_bwd(*ptrs, B, H, N, d, causal, scale, dtype, NUL)
+
+    for i in range(14):
+        p = list(p14); p[i] = NUL
+        assert call(p) == 1
+        p[i] = MIS
+        assert call(p) == 1
+    assert call(N=0) == 1 and call(scale=-1.0) == 1 and call(causal=3) == 1
+    assert call(d=68) == 2                      # f32 stops at 64
+    assert call(d=136, dtype=1) == 2            # bf16 stops at 128
+    assert call(dtype=5) == 2
+    assert lib.attn_bwd_bwd_workspace_bytes(2, 3, 10, 64) == 4 * 60 * 4
+    assert lib.attn_bwd_bwd_workspace_bytes(0, 3, 10, 64) == 0
     assert lib.attn_last_error() == b""
 
 

@@ -1,0 +1,93 @@
+"""Backward of the backward: HIP path vs the fp64 oracle through the C ABI.
+
+Relative Frobenius error per output tensor (hQ, hK, hV, hdO) and for the two
+row scalars r and E the kernels leave in the workspace.  Two feeds of O and L
+as in the first backward's tests: the library's own forward, and the
+oracle's O and L cast to the device type.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+
+from exact_softmax_attention_attn_amd import workloads
+from oracle import attn_oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+
+
+def _say(msg):
+    print(f"[gpu bob case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def B():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from exact_softmax_attention_attn_amd import binding
+    binding.load()
+    return binding
+
+
+def _dev(x, dtype):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to("cuda")
+    return t if dtype == "f32" else t.to(torch.bfloat16)
+
+
+def _host(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def rel_fro(got, ref):
+    return float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30))
+
+
+CASES = [
+    # B, H, N, d, dtype, causal
+    (3, 2, 8, 4, "f32", True),
+    (2, 2, 77, 32, "f32", False),
+    (1, 2, 300, 64, "f32", True),
+    (1, 2, 257, 64, "bf16", True),
+    (1, 2, 300, 128, "bf16", False),
+    (1, 1, 700, 128, "bf16", True),
+    (2, 1, 129, 40, "bf16", True),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "x".join(map(str, c)))
+def test_bwd_bwd_parity(B, case):
+    import torch
+    Bn, H, N, d, dtype, causal = case
+    scale = 1.0 / math.sqrt(d)
+    x = workloads.make_random(Bn, H, N, d, dtype, seed=N + d,
+                              qkv_std=0.5 if dtype == "bf16" else 1.0)
+    x.update(workloads.make_cotangents(Bn, H, N, d, dtype, seed=N))
+    xs = {n: x[n].astype(np.float64) for n in x}
+    O, L = orc.attn_fwd(xs["q"], xs["k"], xs["v"], scale, causal)
+    ref = orc.attn_bwd_bwd(xs["q"], xs["k"], xs["v"], xs["do"], xs["gq"], xs["gk"], xs["gv"],
+                           scale, causal)
+    t = {n: _dev(x[n], dtype) for n in x}
+    for feed in ("own", "oracle"):
+        _say(f"{case} feed={feed}")
+        if feed == "own":
+            o, lse = B.attn_fwd_lse(t["q"], t["k"], t["v"], causal=causal, scale=scale)
+        else:
+            o = _dev(O, dtype)
+            lse = torch.from_numpy(np.ascontiguousarray(L, dtype=np.float32)).cuda()
+        ws = torch.empty((4, Bn, H, N), dtype=torch.float32, device="cuda")
+        hq, hk, hv, hdo = B.attn_bwd_bwd(t["q"], t["k"], t["v"], o, t["do"], lse, t["gq"],
+                                         t["gk"], t["gv"], causal=causal, scale=scale,
+                                         workspace=ws)
+        torch.cuda.synchronize()
+        errs = {"hQ": rel_fro(_host(hq), ref["hQ"]), "hK": rel_fro(_host(hk), ref["hK"]),
+                "hV": rel_fro(_host(hv), ref["hV"]), "hdO": rel_fro(_host(hdo), ref["hdO"]),
+                "r": rel_fro(_host(ws[2]), ref["r"]), "E": rel_fro(_host(ws[3]), ref["E"])}
+        assert all(np.isfinite(v) for v in errs.values()), (case, feed, errs)
+        assert max(errs.values()) <= TOL[dtype], (case, feed, errs)
