@@ -81,7 +81,7 @@ def traffic_record():
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(w, x, bm=None):
+def cpu_baseline(w, x, bm=None, cot=None):
     """The oracle as it stands, on whole (batch, head) slices of the workload.
 
     Heads run one after another until CPU_BASELINE_SECONDS have passed (at
@@ -101,17 +101,22 @@ def cpu_baseline(w, x, bm=None):
     for b, h in heads:
         q, k, v, do = (x[n][b:b + 1, :, h:h + 1].astype(np.float64) for n in ("q", "k", "v", "do"))
         t0 = time.perf_counter()
-        orc.attn_bwd(q, k, v, do, w.scale, w.causal, bm)
+        if cot is None:
+            orc.attn_bwd(q, k, v, do, w.scale, w.causal, bm)
+        else:
+            gq, gk, gv = (cot[n][b:b + 1, :, h:h + 1].astype(np.float64) for n in ("gq", "gk", "gv"))
+            orc.attn_bwd_bwd(q, k, v, do, gq, gk, gv, w.scale, w.causal, bm)
         spent += time.perf_counter() - t0
         done += 1
         if spent >= CPU_BASELINE_SECONDS:
             break
-    flops = 10 * w.d * pairs(1, 1, w.N, w.causal, bm) * done
+    flops = (10 if cot is None else 44) * w.d * pairs(1, 1, w.N, w.causal, bm) * done
     return {"value": round(flops / spent / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"{done} of {len(heads)} (batch, head) slices of {w.name} (N={w.N}, d={w.d}, "
-                      f"{'causal' if w.causal else 'full'}), fp64 numpy oracle attn_bwd, "
-                      f"{spent:.1f} s; TFLOP/s from 10*d*pairs of the slices run"}
+                      f"{'causal' if w.causal else 'full'}), fp64 numpy oracle "
+                      f"{'attn_bwd' if cot is None else 'attn_bwd_bwd'}, "
+                      f"{spent:.1f} s; TFLOP/s from {10 if cot is None else 44}*d*pairs of the slices run"}
 
 
 def summarize_pmc(fetch_dirs, write_dirs, calib_mib):
@@ -243,9 +248,28 @@ def main(argv=None):
     o, lse = forward()
     dq, dk, dv = (torch.empty_like(q) for _ in range(3))
     ws = binding.new_workspace(w.B, w.H, w.N, dev)
+    cot = None
+    if w.op == "bob":
+        # the backward of the backward: cotangents of dQ, dK, dV in, hQ, hK, hV, hdO out
+        cot = workloads.make_cotangents(w.B, w.H, w.N, w.d, w.dtype, seed=0)
+        gq, gk, gv = (torch.from_numpy(cot[n]).to(dev).to(tdt) for n in ("gq", "gk", "gv"))
+        hq, hdo = torch.empty_like(q), torch.empty_like(q)
+        ws = torch.empty((4, w.B, w.H, w.N), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
+    def step_bob(ev=None):
+        if ev is not None:
+            ev[0].record()
+            ev[1].record()
+            ev[2].record()
+        binding.attn_bwd_bwd(q, k, v, o, do, lse, gq, gk, gv, causal=w.causal, scale=w.scale,
+                             hq=hq, hk=dk, hv=dv, hdo=hdo, workspace=ws)
+        if ev is not None:
+            ev[3].record()
+
     def step(ev=None):
+        if w.op == "bob":
+            return step_bob(ev)
         if ev is not None:
             ev[0].record()
         binding.attn_bwd_preprocess(o, do, lse, ws)
@@ -284,10 +308,18 @@ def main(argv=None):
     dqk = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
     ms = wall / args.steps * 1e3
     P = pairs(w.B, w.H, w.N, w.causal, bm)
-    flops = 10 * w.d * P
+    # FLOPs per kept pair: the backward's five contractions (10 d); the
+    # backward of the backward's 22 products of 2 d each as scheduled (S, dP,
+    # G as two, A in each of its three passes, plus hK, hV, hQ, hdO: 44 d)
+    per_pair = 44 * w.d if w.op == "bob" else 10 * w.d
+    flops = per_pair * P
     value = flops / (ms * 1e-3) / 1e12
-    dkdv_flops = 8 * w.d * P
-    achieved = dkdv_flops / (dkdv * 1e-3) / 1e12
+    if w.op == "bob":
+        # one call (four launches): the roofline covers all of it
+        achieved = flops / (dqk * 1e-3) / 1e12
+    else:
+        dkdv_flops = 8 * w.d * P
+        achieved = dkdv_flops / (dkdv * 1e-3) / 1e12
     peak = PEAK[w.dtype]
 
     # the forward (the step that supplies O and L), timed on its own after the
@@ -324,6 +356,8 @@ def main(argv=None):
 
     # the dK/dV kernel that ran: the pipelined one serves bf16 with d = 64 or 128
     dkdv_kernel = DOMINANT_KERNEL if (w.dtype == "bf16" and w.d in (64, 128)) else "bwd_dkdv_kernel"
+    if w.op == "bob":
+        dkdv_kernel = "attn_bwd_bwd (preprocess + bob_q_kernel x2 + bob_kv_kernel)"
     esz = 2 if w.dtype == "bf16" else 4
     alg_bytes = 8 * w.B * w.N * w.H * w.d * esz + 4 * w.B * w.H * w.N
     line = {
@@ -341,10 +375,11 @@ def main(argv=None):
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
                    "causal": w.causal, "scale": w.scale, "layout": "[B,N,H,d]",
-                   "parallelism": "single GPU",
+                   "parallelism": "single GPU", "op": w.op, "flops_per_pair": per_pair,
                    **({"block_mask": w.mask, "kept_pairs": P} if bm is not None else {})},
         "pct_of_peak": round(100 * value / peak, 2),
-        "stages_ms": {"preprocess": round(pre, 4), "dkdv": round(dkdv, 4), "dq": round(dqk, 4)},
+        "stages_ms": ({"bwd_bwd": round(dqk, 4)} if w.op == "bob" else
+                      {"preprocess": round(pre, 4), "dkdv": round(dkdv, 4), "dq": round(dqk, 4)}),
         "hbm_gbs_algorithmic": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
         "fwd_lse": {"ms": round(fwd_ms, 4),
                     "tflops": round(4 * w.d * P / (fwd_ms * 1e-3) / 1e12, 3)},
@@ -359,7 +394,7 @@ def main(argv=None):
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle, whole heads, bounded)", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(w, x, bm)
+        line["cpu_baseline"] = cpu_baseline(w, x, bm, cot if w.op == "bob" else None)
     print(json.dumps(line), flush=True)
     return 0
 

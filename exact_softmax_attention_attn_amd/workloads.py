@@ -5,8 +5,8 @@ arithmetic lives here, so the oracle and the HIP path can both draw from it
 without sharing any of the method.
 
 The first five workloads stand in for the pages' own workloads (no dataset
-or trained weights exist for them); four more take c5's shape beyond square
-causal attention or to head dim 256:
+or trained weights exist for them); five more take c5's shape beyond square
+causal attention, to head dim 256, or through the backward of the backward:
 
 * ``c1_tiny``  -- the toy of ddx issue #217's repro script: 3 sequences, 2
   heads, 8 positions, 4 channels per head, scale 1/2, and Q/K/V filled with
@@ -23,6 +23,8 @@ causal attention or to head dim 256:
 * ``c5_full`` -- c5_long with full (non-causal) attention.
 * ``c5_ragged`` -- c5_long at 16,383 tokens, a length no tile size divides.
 * ``c5_d256`` -- 16,384 tokens, 8 heads of head dim 256 (c5_long's FLOPs).
+* ``c5_bob`` -- c5_long's inputs through the backward of the backward, with
+  cotangents gQ, gK, gV from ``make_cotangents``.
 * ``c5_window`` -- c5_long under a block-sparse mask: each query block keeps
   the 16 key blocks up to its own (a 2,048-token local window) and the first
   block (attention sink), causal inside the window.
@@ -59,6 +61,7 @@ class Workload:
     causal: bool = True
     description: str = ""
     mask: str = ""        # "" (no block mask) or "window<W>": window_block_mask(N, W, 1)
+    op: str = "bwd"       # "bwd" (the backward) or "bob" (the backward of the backward)
 
     @property
     def shape(self):
@@ -85,6 +88,9 @@ WORKLOADS = (
     Workload("c5_window", 1, 16, 16384, 128, 1.0 / math.sqrt(128), "bf16", qkv_std=0.5,
              mask="window16",
              description="c5_long under a block mask: 2048-token local window + first block"),
+    # the backward of the backward at c5_long's shape (cotangents from make_cotangents)
+    Workload("c5_bob", 1, 16, 16384, 128, 1.0 / math.sqrt(128), "bf16", qkv_std=0.5, op="bob",
+             description="c5_long through the backward of the backward"),
     # head dim 256 at the same FLOPs as c5_long (half the heads)
     Workload("c5_d256", 1, 8, 16384, 256, 1.0 / 16.0, "bf16", qkv_std=0.5,
              description="16384 tokens x 8 heads x d 256, bf16"),

@@ -73,6 +73,7 @@ __all__ = [
     "bwd_flops",
     "head_bwd_bwd",
     "attn_bwd_bwd",
+    "attn_bwd_bwd_sampled",
 ]
 
 
@@ -417,6 +418,70 @@ def attn_bwd_bwd(Q, K, V, dO, gQ, gK, gV, scale: float, causal: bool = True, blo
             for n, x in zip(("hQ", "hK", "hV", "hdO"), res[:4]):
                 out[n][b, :, h] = x
             out["r"][b, h], out["E"][b, h] = res[4], res[5]
+    return out
+
+
+def attn_bwd_bwd_sampled(Q, K, V, dO, gQ, gK, gV, scale: float, causal: bool, b: int, h: int,
+                         rows, cols, row_block: int = 512):
+    """Selected outputs of ``head_bwd_bwd`` for one (b, h) without N x N memory.
+
+    hQ and hdO for the query rows ``rows``, hK and hV for the key rows
+    ``cols``, and the row scalars for every row.  Row quantities (L, D, r, E)
+    come from whole score rows evaluated ``row_block`` rows at a time; a key
+    column then needs its column of P, dP, G and A, rebuilt from those
+    scalars.  Each value is the same definition as ``head_bwd_bwd``.
+    """
+    q, k, v, do, gq, gk, gv = (_f64(t[b, :, h]) for t in (Q, K, V, dO, gQ, gK, gV))
+    n = q.shape[0]
+    rows = np.asarray(rows, dtype=np.int64)
+    cols = np.asarray(cols, dtype=np.int64)
+
+    def block(r0, r1):
+        s = scale * (q[r0:r1] @ k.T)
+        if causal:
+            s = np.where(np.arange(n)[None, :] <= np.arange(r0, r1)[:, None], s, -np.inf)
+        m, w, z = softmax_rows(s)
+        p, lse = _normalise(m, w, z)
+        dp = do[r0:r1] @ v.T
+        dd = (p * dp).sum(axis=1)
+        ds = p * (dp - dd[:, None])
+        g = scale * (gq[r0:r1] @ k.T + q[r0:r1] @ gk.T)
+        a = do[r0:r1] @ gv.T
+        r = (p * g).sum(axis=1)
+        e = (p * (a + (dp - dd[:, None]) * (g - r[:, None]))).sum(axis=1)
+        return lse, dd, r, e, p, dp, ds, g, a
+
+    L, D, R, E = (np.empty(n) for _ in range(4))
+    for r0 in range(0, n, row_block):
+        r1 = min(n, r0 + row_block)
+        L[r0:r1], D[r0:r1], R[r0:r1], E[r0:r1] = block(r0, r1)[:4]
+    out = {"rows": rows, "cols": cols, "L": L, "D": D, "r": R, "E": E}
+    hq = np.empty((rows.size, q.shape[1]))
+    hdo = np.empty((rows.size, q.shape[1]))
+    for t, i in enumerate(rows):
+        _, dd, r, e, p, dp, ds, g, a = block(int(i), int(i) + 1)
+        w = p * (g - r[:, None])
+        ds2 = p * (a + (dp - dd[:, None]) * (g - r[:, None]) - e[:, None])
+        hq[t] = scale * (ds2 @ k + ds @ gk)[0]
+        hdo[t] = (p @ gv + w @ v)[0]
+    hk = np.empty((cols.size, q.shape[1]))
+    hv = np.empty((cols.size, q.shape[1]))
+    live = np.isfinite(L)
+    for t, j in enumerate(cols):
+        keep = live.copy()
+        if causal:
+            keep &= np.arange(n) >= j
+        s_col = scale * (q @ k[j])
+        p_col = np.exp(np.where(keep, s_col - np.where(live, L, 0.0), -np.inf))
+        dp_col = do @ v[j]
+        g_col = scale * (gq @ k[j] + q @ gk[j])
+        a_col = do @ gv[j]
+        ds_col = p_col * (dp_col - D)
+        w_col = p_col * (g_col - R)
+        ds2_col = p_col * (a_col + (dp_col - D) * (g_col - R) - E)
+        hk[t] = scale * (ds2_col @ q + ds_col @ gq)
+        hv[t] = w_col @ do
+    out.update(hQ=hq, hdO=hdo, hK=hk, hV=hv)
     return out
 
 

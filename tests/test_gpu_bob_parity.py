@@ -91,3 +91,34 @@ def test_bwd_bwd_parity(B, case):
                 "r": rel_fro(_host(ws[2]), ref["r"]), "E": rel_fro(_host(ws[3]), ref["E"])}
         assert all(np.isfinite(v) for v in errs.values()), (case, feed, errs)
         assert max(errs.values()) <= TOL[dtype], (case, feed, errs)
+
+
+def test_c5_bob_full_size_sampled_against_oracle(B):
+    """N = 16,384, d = 128, bf16: sampled rows and columns of two heads."""
+    import torch
+    w = workloads.get("c5_bob")
+    _say("c5_bob inputs")
+    x = workloads.make_inputs(w, seed=0)
+    x.update(workloads.make_cotangents(w.B, w.H, w.N, w.d, w.dtype, seed=0))
+    t = {n: _dev(x[n], w.dtype) for n in x}
+    _say("c5_bob forward + backward of the backward on the GPU")
+    o, lse = B.attn_fwd_lse(t["q"], t["k"], t["v"], causal=True, scale=w.scale)
+    ws = torch.empty((4, w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+    hq, hk, hv, hdo = B.attn_bwd_bwd(t["q"], t["k"], t["v"], o, t["do"], lse, t["gq"], t["gk"],
+                                     t["gv"], causal=True, scale=w.scale, workspace=ws)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(6)
+    N = w.N
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, 8191, 8192, N - 1], rng.integers(0, N, 24)]))
+    cols = np.unique(np.concatenate([[0, 1, 127, 128, 8191, 8192, N - 1], rng.integers(0, N, 24)]))
+    for h in (0, 9):
+        _say(f"c5_bob oracle sample head {h}")
+        s = orc.attn_bwd_bwd_sampled(x["q"], x["k"], x["v"], x["do"], x["gq"], x["gk"], x["gv"],
+                                     w.scale, True, 0, h, rows, cols, row_block=1024)
+        errs = {"hQ": rel_fro(_host(hq[0, rows, h]), s["hQ"]),
+                "hdO": rel_fro(_host(hdo[0, rows, h]), s["hdO"]),
+                "hK": rel_fro(_host(hk[0, cols, h]), s["hK"]),
+                "hV": rel_fro(_host(hv[0, cols, h]), s["hV"]),
+                "r": rel_fro(_host(ws[2, 0, h]), s["r"]), "E": rel_fro(_host(ws[3, 0, h]), s["E"])}
+        print("c5_bob sampled errors", h, errs, flush=True)
+        assert max(errs.values()) <= TOL["bf16"], (h, errs)

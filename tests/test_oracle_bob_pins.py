@@ -125,3 +125,17 @@ def test_zero_cotangents_give_zero_and_gv_alone_is_linear():
     a, b = _bob(x, 0.5, False), _bob(two, 0.5, False)
     for n in ("hQ", "hK", "hV", "hdO"):
         np.testing.assert_allclose(b[n], 2 * a[n], rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_sampled_evaluator_equals_full_oracle(causal):
+    x = _rand(2, 2, 70, 16, seed=11)
+    full = _bob(x, 0.25, causal)
+    rows, cols = [0, 1, 33, 69], [0, 5, 64, 69]
+    s = orc.attn_bwd_bwd_sampled(x["q"], x["k"], x["v"], x["do"], x["gq"], x["gk"], x["gv"],
+                                 0.25, causal, 1, 0, rows, cols, row_block=16)
+    for name, idx in (("hQ", rows), ("hdO", rows), ("hK", cols), ("hV", cols)):
+        np.testing.assert_allclose(s[name], full[name][1, idx, 0], rtol=1e-11, atol=1e-13,
+                                   err_msg=name)
+    np.testing.assert_allclose(s["r"], full["r"][1, 0], rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(s["E"], full["E"][1, 0], rtol=1e-11, atol=1e-13)
