@@ -3,7 +3,8 @@
 Builds ``lds_layout_check.hip`` as a host program against the kernels' own
 header and runs it.  It enumerates the per-lane LDS addresses of every
 operand read of the pipelined backward kernels (128-bit row reads and
-64-bit transposing reads, head dims 64 and 128) and asserts that each group
+64-bit transposing reads, head dims 64 and 128; and 256, whose tiles the
+generic kernels read at the same addresses) and asserts that each group
 of lanes that may be served in one 256-byte LDS cycle touches 64 distinct
 banks; it also checks that the asynchronous tile copy stores every logical
 16-byte chunk exactly once, at the slot the reads address.
