@@ -1,0 +1,114 @@
+"""Bitwise repeatability of every kernel family, through the C ABI.
+
+The dQ pass accumulates in a fixed order with no atomics, and every other
+accumulation is owned by one workgroup, so the same call on the same inputs
+must give the same bits.  The unmasked pipelined path is covered in
+test_gpu_parity.py; this covers the block-masked path, the generic kernels
+(float32, and bf16 head dim 256 with its column split), the forward, and the
+backward of the backward.  Each case runs three times and compares bits.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+
+from exact_softmax_attention_attn_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(f"[gpu determinism case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def B():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from exact_softmax_attention_attn_amd import binding
+    binding.load()
+    return binding
+
+
+def _dev(x, dtype):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to("cuda")
+    return t if dtype == "f32" else t.to(torch.bfloat16)
+
+
+def _bits(t):
+    import torch
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+def _same(a, b):
+    import torch
+    return all(torch.equal(_bits(x), _bits(y)) for x, y in zip(a, b))
+
+
+# B, H, N, d, dtype, causal, masked
+CASES = [
+    (1, 2, 1000, 128, "bf16", True, True),     # pipelined kernels, block mask
+    (2, 2, 700, 64, "bf16", False, True),
+    (1, 2, 300, 64, "f32", True, False),       # generic kernels, float32
+    (1, 2, 400, 256, "bf16", True, False),     # head dim 256, column split
+    (1, 1, 333, 256, "bf16", False, True),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "x".join(map(str, c)))
+def test_forward_and_backward_repeat_bitwise(B, case):
+    import torch
+    Bn, H, N, d, dtype, causal, masked = case
+    _say(str(case))
+    x = workloads.make_random(Bn, H, N, d, dtype, seed=N + d,
+                              qkv_std=0.5 if dtype == "bf16" else 1.0)
+    q, k, v, do = (_dev(x[n], dtype) for n in ("q", "k", "v", "do"))
+    scale = 1.0 / math.sqrt(d)
+    mask = None
+    if masked:
+        m = workloads.make_block_mask(N, 0.6, seed=N, heads=(Bn, H), empty_rows=(1,))
+        mask = torch.from_numpy(m).cuda()
+
+    def run():
+        if mask is None:
+            o, lse = B.attn_fwd_lse(q, k, v, causal=causal, scale=scale)
+            g = B.attn_bwd(q, k, v, o, do, lse, causal=causal, scale=scale)
+        else:
+            o, lse = B.attn_fwd_lse_masked(q, k, v, mask, causal=causal, scale=scale)
+            g = B.attn_bwd_masked(q, k, v, o, do, lse, mask, causal=causal, scale=scale)
+        return (o, lse) + tuple(g)
+
+    first = run()
+    for _ in range(2):
+        assert _same(first, run()), case
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("case", [(1, 2, 600, 128, "bf16", True), (1, 2, 200, 64, "f32", False)],
+                         ids=lambda c: "x".join(map(str, c)))
+def test_backward_of_backward_repeats_bitwise(B, case):
+    import torch
+    Bn, H, N, d, dtype, causal = case
+    _say(f"bob {case}")
+    x = workloads.make_random(Bn, H, N, d, dtype, seed=N + d,
+                              qkv_std=0.5 if dtype == "bf16" else 1.0)
+    x.update(workloads.make_cotangents(Bn, H, N, d, dtype, seed=N))
+    t = {n: _dev(x[n], dtype) for n in x}
+    scale = 1.0 / math.sqrt(d)
+    o, lse = B.attn_fwd_lse(t["q"], t["k"], t["v"], causal=causal, scale=scale)
+
+    def run():
+        ws = torch.empty((4, Bn, H, N), dtype=torch.float32, device="cuda")
+        out = B.attn_bwd_bwd(t["q"], t["k"], t["v"], o, t["do"], lse, t["gq"], t["gk"],
+                             t["gv"], causal=causal, scale=scale, workspace=ws)
+        return tuple(out) + (ws[2], ws[3])
+
+    first = run()
+    for _ in range(2):
+        assert _same(first, run()), case
+    torch.cuda.synchronize()
