@@ -87,11 +87,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   using M = Mma<T>;
   using frag = typename M::frag;
   constexpr int BKV = 128, BQ = 64, KS = D / M::K, RS = 32 / M::K;
-  // Head dims above 128 (bf16, 256 bucket): each workgroup accumulates DA = 128
-  // of the output's columns (part = which DA) and recomputes S and dP over the
-  // full head dim, so a (b, h) runs on D / DA workgroups per block; their
-  // register footprint then stays that of the 128 bucket.
-  constexpr int DA = D > 128 ? 128 : D, MA = DA / 32, NSPLIT = D / DA;
+  // Wide heads (bf16 256 bucket, float32 128 bucket): each workgroup
+  // accumulates DA of the output's columns (part = which DA) and recomputes S
+  // and dP over the full head dim, so a (b, h) runs on D / DA workgroups per
+  // block.
+  constexpr int DA = out_cols<T, D>(), MA = DA / 32, NSPLIT = D / DA;
   using QT = Tile<T, BQ, D>;
   struct __align__(16) Buf {
     T q[QT::ELEMS];
@@ -264,11 +264,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
   using M = Mma<T>;
   using frag = typename M::frag;
   constexpr int BQ = 128, BKV = 64, KS = D / M::K, RS = 32 / M::K;
-  // Head dims above 128 (bf16, 256 bucket): each workgroup accumulates DA = 128
-  // of the output's columns (part = which DA) and recomputes S and dP over the
-  // full head dim, so a (b, h) runs on D / DA workgroups per block; their
-  // register footprint then stays that of the 128 bucket.
-  constexpr int DA = D > 128 ? 128 : D, MA = DA / 32, NSPLIT = D / DA;
+  // Wide heads (bf16 256 bucket, float32 128 bucket): each workgroup
+  // accumulates DA of the output's columns (part = which DA) and recomputes S
+  // and dP over the full head dim, so a (b, h) runs on D / DA workgroups per
+  // block.
+  constexpr int DA = out_cols<T, D>(), MA = DA / 32, NSPLIT = D / DA;
   using KT = Tile<T, BKV, D>;
   struct __align__(16) Buf {
     T k[KT::ELEMS];
@@ -414,12 +414,12 @@ hipError_t launch_bwd_preprocess(const void* O, const void* dO, const float* L, 
 
 static inline long rows_of(const BwdArgs& a) { return (long)a.B * a.H * a.N; }
 
-// the 256 bucket runs two workgroups per block, one per 128 output columns
-template <int D> constexpr int column_parts() { return D > 128 ? D / 128 : 1; }
+// workgroups per block: one per out_cols output columns
+template <typename T, int D> constexpr int column_parts() { return D / out_cols<T, D>(); }
 
 template <typename T, int D, bool C>
 static hipError_t dkdv_go(const BwdArgs& a, hipStream_t stream) {
-  dim3 grid((a.N + 127) / 128, a.H * column_parts<D>(), a.B);
+  dim3 grid((a.N + 127) / 128, a.H * column_parts<T, D>(), a.B);
   hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, C>), grid, dim3(256), 0, stream,
                      static_cast<const T*>(a.Q), static_cast<const T*>(a.K),
                      static_cast<const T*>(a.V), static_cast<const T*>(a.dO), a.Dws + rows_of(a), a.Dws,
@@ -430,7 +430,7 @@ static hipError_t dkdv_go(const BwdArgs& a, hipStream_t stream) {
 
 template <typename T, int D, bool C>
 static hipError_t dq_go(const BwdArgs& a, hipStream_t stream) {
-  dim3 grid((a.N + 127) / 128, a.H * column_parts<D>(), a.B);
+  dim3 grid((a.N + 127) / 128, a.H * column_parts<T, D>(), a.B);
   hipLaunchKernelGGL((bwd_dq_kernel<T, D, C>), grid, dim3(256), 0, stream,
                      static_cast<const T*>(a.Q), static_cast<const T*>(a.K),
                      static_cast<const T*>(a.V), static_cast<const T*>(a.dO), a.Dws + rows_of(a), a.Dws,

@@ -29,10 +29,10 @@ __global__ __launch_bounds__(256, 1) void fwd_lse_kernel(const T* __restrict__ Q
   using M = Mma<T>;
   using frag = typename M::frag;
   constexpr int BQ = 128, BKV = 64, KS = D / M::K, RS = 32 / M::K;
-  // Head dims above 128 (bf16, 256 bucket): each workgroup accumulates DA = 128
-  // of O's columns (part = which DA) and recomputes the scores over the full
-  // head dim; the part-0 workgroup writes L.
-  constexpr int DA = D > 128 ? 128 : D, MA = DA / 32, NSPLIT = D / DA;
+  // Wide heads (bf16 256 bucket, float32 128 bucket): each workgroup
+  // accumulates DA of O's columns (part = which DA) and recomputes the scores
+  // over the full head dim; the part-0 workgroup writes L.
+  constexpr int DA = out_cols<T, D>(), MA = DA / 32, NSPLIT = D / DA;
   using KT = Tile<T, BKV, D>;
   struct __align__(16) Buf {
     T k[KT::ELEMS];
@@ -179,7 +179,7 @@ __global__ __launch_bounds__(256, 1) void fwd_lse_kernel(const T* __restrict__ Q
 
 template <typename T, int D, bool C>
 static hipError_t fwd_go(const FwdArgs& a, hipStream_t stream) {
-  dim3 grid((a.N + 127) / 128, a.H * (D > 128 ? D / 128 : 1), a.B);
+  dim3 grid((a.N + 127) / 128, a.H * (D / out_cols<T, D>()), a.B);
   hipLaunchKernelGGL((fwd_lse_kernel<T, D, C>), grid, dim3(256), 0, stream,
                      static_cast<const T*>(a.Q), static_cast<const T*>(a.K),
                      static_cast<const T*>(a.V), static_cast<T*>(a.O), a.L, a.H, a.N, a.d,

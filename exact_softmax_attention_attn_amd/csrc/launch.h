@@ -64,6 +64,15 @@ struct BobArgs {
 // zero.
 inline int head_dim_bucket(int d) { return d <= 32 ? 32 : (d <= 64 ? 64 : (d <= 128 ? 128 : 256)); }
 
+// Output columns one workgroup of a generic kernel accumulates: the whole head
+// dim up to 128 (bf16) or 64 (float32, whose operands take twice the
+// registers).  Wider heads split their output columns over D / out_cols
+// workgroups per block, each rebuilding the scores over the full head dim, so
+// the register footprint stays that of the largest unsplit bucket.
+template <typename T, int D> constexpr int out_cols() {
+  return sizeof(T) == 2 ? (D > 128 ? 128 : D) : (D > 64 ? 64 : D);
+}
+
 hipError_t launch_bwd_preprocess(const void* O, const void* dO, const float* L, float* ws, int B,
                                  int H, int N, int d, int dtype, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t stream);

@@ -109,7 +109,8 @@ EDGE = [
     (1, 2, 65, 64, "bf16", True),
     (1, 1, 1000, 64, "f32", True),
     (1, 1, 1000, 128, "bf16", True),
-    (2, 1, 200, 128, "f32", True),
+    (2, 1, 200, 128, "f32", True),      # float32 128 bucket: two column parts per block
+    (1, 2, 150, 128, "f32", False),
     (1, 2, 129, 8, "bf16", True),
     (1, 2, 300, 40, "bf16", True),
     (1, 1, 300, 128, "bf16", True),   # odd tile counts per key block
