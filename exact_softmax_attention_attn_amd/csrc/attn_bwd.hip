@@ -22,7 +22,8 @@ template <bool B> using bool_c = std::integral_constant<bool, B>;
 // L2[b, h, n] = L[b, h, n] * log2(e), the row scalar in the base-2 units the
 // kernels exponentiate in.  Both are stored negated (-D, -L2): the kernels
 // add them, which lets them enter a matrix instruction as its C input.
-// 16 lanes per row, 16 rows per 256-thread block.
+// 16 lanes per row; a 256-thread block takes 16 consecutive positions of one
+// (b, h), so its 16 results land side by side in the [B, H, N] outputs.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_preprocess_kernel(const T* __restrict__ O,
@@ -33,10 +34,14 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(const T* __restrict
                                                              int H, int N, int d) {
   constexpr int VEC = Mma<T>::CHUNK;
   const int sub = threadIdx.x & 15;
-  const long row = (long)blockIdx.x * 16 + (threadIdx.x >> 4);  // row = (b * N + n) * H + h
-  const long rows = (long)B * N * H;
+  const int chunks = (N + 15) / 16;
+  const long bh = blockIdx.x / chunks;                          // = b * H + h
+  const int n = (int)(blockIdx.x % chunks) * 16 + (threadIdx.x >> 4);
+  const int h = (int)(bh % H);
+  const long b = bh / H;
+  const long row = (b * N + n) * H + h;                         // input row of [B, N, H, d]
   float acc = 0.f;
-  if (row < rows) {
+  if (n < N) {
     const T* o = O + row * d;
     const T* g = dO + row * d;
     for (int c = sub * VEC; c < d; c += 16 * VEC) {
@@ -55,12 +60,8 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(const T* __restrict
   }
 #pragma unroll
   for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);
-  if (row < rows && sub == 0) {
-    const int h = (int)(row % H);
-    const long bn = row / H;
-    const int n = (int)(bn % N);
-    const int b = (int)(bn / N);
-    const long i = ((long)b * H + h) * N + n;
+  if (n < N && sub == 0) {
+    const long i = bh * N + n;
     Dout[i] = -acc;
     // a row with no kept key (L = -inf) stores -inf, so every P of it is 0
     L2out[i] = L[i] == -__builtin_inff() ? -__builtin_inff() : -L[i] * kLog2e;
@@ -399,7 +400,7 @@ template <typename T>
 hipError_t launch_bwd_preprocess_t(const void* O, const void* dO, const float* L, float* ws, int B,
                                    int H, int N, int d, hipStream_t stream) {
   const long rows = (long)B * N * H;
-  const unsigned grid = (unsigned)((rows + 15) / 16);
+  const unsigned grid = (unsigned)((long)B * H * ((N + 15) / 16));
   hipLaunchKernelGGL(bwd_preprocess_kernel<T>, dim3(grid), dim3(256), 0, stream,
                      static_cast<const T*>(O), static_cast<const T*>(dO), L, ws, ws + rows, B, H,
                      N, d);
