@@ -194,3 +194,11 @@ def test_one_hip_runtime_is_mapped(lib):
     maps = open("/proc/self/maps").read()
     hip = set(l.split()[-1] for l in maps.splitlines() if "libamdhip64" in l)
     assert len(hip) == 1, hip
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
+    # no CPU fallback: with the library absent, loading (and so every call) raises
+    from exact_softmax_attention_attn_amd import binding
+    monkeypatch.setattr(binding, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        binding.load(str(tmp_path / "libattn.so"))
