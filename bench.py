@@ -14,6 +14,11 @@ launch stream, against the bf16 dense MFMA peak.  `cpu_baseline` times the
 fp64 oracle on whole (batch, head) slices of the same workload on the host
 cores (a bounded sample of about CPU_BASELINE_SECONDS).
 
+Other workloads (--workload) time other steps the same way: the backward of
+the backward (op "bob", 44 * d FLOPs per kept pair, its one call as the
+roofline) and the forward alone (op "fwd", 4 * d per kept pair: S and P V,
+its one kernel as the roofline, the oracle's forward as the CPU baseline).
+
 Secondary denominators, measured after the timed region on the same GPU:
 `denominators.copy_gbs` (a 1 GiB cast copy, bytes read + written per second)
 and `denominators.gemm_bf16_tflops` (plain 8192^3 bf16 matrix products through
@@ -81,7 +86,7 @@ def traffic_record():
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(w, x, bm=None, cot=None):
+def cpu_baseline(w, x, bm=None, cot=None, op="bwd"):
     """The oracle as it stands, on whole (batch, head) slices of the workload.
 
     Heads run one after another until CPU_BASELINE_SECONDS have passed (at
@@ -101,7 +106,9 @@ def cpu_baseline(w, x, bm=None, cot=None):
     for b, h in heads:
         q, k, v, do = (x[n][b:b + 1, :, h:h + 1].astype(np.float64) for n in ("q", "k", "v", "do"))
         t0 = time.perf_counter()
-        if cot is None:
+        if op == "fwd":
+            orc.attn_fwd(q, k, v, w.scale, w.causal, bm)
+        elif cot is None:
             orc.attn_bwd(q, k, v, do, w.scale, w.causal, bm)
         else:
             gq, gk, gv = (cot[n][b:b + 1, :, h:h + 1].astype(np.float64) for n in ("gq", "gk", "gv"))
@@ -110,13 +117,14 @@ def cpu_baseline(w, x, bm=None, cot=None):
         done += 1
         if spent >= CPU_BASELINE_SECONDS:
             break
-    flops = (10 if cot is None else 44) * w.d * pairs(1, 1, w.N, w.causal, bm) * done
+    per = 4 if op == "fwd" else (10 if cot is None else 44)
+    fn = "attn_fwd" if op == "fwd" else ("attn_bwd" if cot is None else "attn_bwd_bwd")
+    flops = per * w.d * pairs(1, 1, w.N, w.causal, bm) * done
     return {"value": round(flops / spent / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"{done} of {len(heads)} (batch, head) slices of {w.name} (N={w.N}, d={w.d}, "
-                      f"{'causal' if w.causal else 'full'}), fp64 numpy oracle "
-                      f"{'attn_bwd' if cot is None else 'attn_bwd_bwd'}, "
-                      f"{spent:.1f} s; TFLOP/s from {10 if cot is None else 44}*d*pairs of the slices run"}
+                      f"{'causal' if w.causal else 'full'}), fp64 numpy oracle {fn}, "
+                      f"{spent:.1f} s; TFLOP/s from {per}*d*pairs of the slices run"}
 
 
 def summarize_pmc(fetch_dirs, write_dirs, calib_mib):
@@ -267,9 +275,20 @@ def main(argv=None):
         if ev is not None:
             ev[3].record()
 
+    def step_fwd(ev=None):
+        if ev is not None:
+            ev[0].record()
+            ev[1].record()
+            ev[2].record()
+        forward()
+        if ev is not None:
+            ev[3].record()
+
     def step(ev=None):
         if w.op == "bob":
             return step_bob(ev)
+        if w.op == "fwd":
+            return step_fwd(ev)
         if ev is not None:
             ev[0].record()
         binding.attn_bwd_preprocess(o, do, lse, ws)
@@ -310,12 +329,13 @@ def main(argv=None):
     P = pairs(w.B, w.H, w.N, w.causal, bm)
     # FLOPs per kept pair: the backward's five contractions (10 d); the
     # backward of the backward's 22 products of 2 d each as scheduled (S, dP,
-    # G as two, A in each of its three passes, plus hK, hV, hQ, hdO: 44 d)
-    per_pair = 44 * w.d if w.op == "bob" else 10 * w.d
+    # G as two, A in each of its three passes, plus hK, hV, hQ, hdO: 44 d);
+    # the forward's two (S and P V: 4 d)
+    per_pair = {"bob": 44 * w.d, "fwd": 4 * w.d}.get(w.op, 10 * w.d)
     flops = per_pair * P
     value = flops / (ms * 1e-3) / 1e12
-    if w.op == "bob":
-        # one call (four launches): the roofline covers all of it
+    if w.op in ("bob", "fwd"):
+        # one call: the roofline covers all of it (the forward is one kernel)
         achieved = flops / (dqk * 1e-3) / 1e12
     else:
         dkdv_flops = 8 * w.d * P
@@ -358,8 +378,14 @@ def main(argv=None):
     dkdv_kernel = DOMINANT_KERNEL if (w.dtype == "bf16" and w.d in (64, 128)) else "bwd_dkdv_kernel"
     if w.op == "bob":
         dkdv_kernel = "attn_bwd_bwd (preprocess + bob_q_kernel x2 + bob_kv_kernel)"
+    if w.op == "fwd":
+        dkdv_kernel = ("fwd_bf16_pipe_kernel" if (w.dtype == "bf16" and w.d in (64, 128))
+                       else "fwd_lse_kernel")
     esz = 2 if w.dtype == "bf16" else 4
-    alg_bytes = 8 * w.B * w.N * w.H * w.d * esz + 4 * w.B * w.H * w.N
+    if w.op == "fwd":   # Q, K, V read, O and L written
+        alg_bytes = 4 * w.B * w.N * w.H * w.d * esz + 4 * w.B * w.H * w.N
+    else:
+        alg_bytes = 8 * w.B * w.N * w.H * w.d * esz + 4 * w.B * w.H * w.N
     line = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -379,6 +405,7 @@ def main(argv=None):
                    **({"block_mask": w.mask, "kept_pairs": P} if bm is not None else {})},
         "pct_of_peak": round(100 * value / peak, 2),
         "stages_ms": ({"bwd_bwd": round(dqk, 4)} if w.op == "bob" else
+                      {"fwd_lse": round(dqk, 4)} if w.op == "fwd" else
                       {"preprocess": round(pre, 4), "dkdv": round(dkdv, 4), "dq": round(dqk, 4)}),
         "hbm_gbs_algorithmic": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
         "fwd_lse": {"ms": round(fwd_ms, 4),
@@ -394,7 +421,7 @@ def main(argv=None):
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle, whole heads, bounded)", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(w, x, bm, cot if w.op == "bob" else None)
+        line["cpu_baseline"] = cpu_baseline(w, x, bm, cot if w.op == "bob" else None, w.op)
     print(json.dumps(line), flush=True)
     return 0
 

@@ -28,6 +28,7 @@ causal attention, to head dim 256, or through the backward of the backward:
 * ``c5_window`` -- c5_long under a block-sparse mask: each query block keeps
   the 16 key blocks up to its own (a 2,048-token local window) and the first
   block (attention sink), causal inside the window.
+* ``c5_fwd`` -- c5_long's inputs through the forward alone (O and L).
 
 Random draws use numpy's PCG64 ``default_rng(seed)`` in fp64, in the order
 Q, K, V, dO, each of shape [B, N, H, d]; Q/K/V are multiplied by ``qkv_std``.
@@ -61,7 +62,7 @@ class Workload:
     causal: bool = True
     description: str = ""
     mask: str = ""        # "" (no block mask) or "window<W>": window_block_mask(N, W, 1)
-    op: str = "bwd"       # "bwd" (the backward) or "bob" (the backward of the backward)
+    op: str = "bwd"       # "bwd" (the backward), "bob" (the backward of the backward), "fwd"
 
     @property
     def shape(self):
@@ -94,6 +95,9 @@ WORKLOADS = (
     # head dim 256 at the same FLOPs as c5_long (half the heads)
     Workload("c5_d256", 1, 8, 16384, 256, 1.0 / 16.0, "bf16", qkv_std=0.5,
              description="16384 tokens x 8 heads x d 256, bf16"),
+    # the forward that supplies O and L, at c5_long's shape
+    Workload("c5_fwd", 1, 16, 16384, 128, 1.0 / math.sqrt(128), "bf16", qkv_std=0.5, op="fwd",
+             description="c5_long through the forward (O and L)"),
 )
 
 

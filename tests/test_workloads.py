@@ -10,7 +10,7 @@ from exact_softmax_attention_attn_amd import workloads
 def test_workloads_with_their_shapes():
     names = [w.name for w in workloads.WORKLOADS]
     assert names == ["c1_tiny", "c2_nanogpt_cpu", "c3_single_seq", "c4_batched", "c5_long",
-                     "c5_full", "c5_ragged", "c5_window", "c5_bob", "c5_d256"]
+                     "c5_full", "c5_ragged", "c5_window", "c5_bob", "c5_d256", "c5_fwd"]
     assert workloads.get("c1_tiny").shape == (3, 8, 2, 4)
     assert workloads.get("c2_nanogpt_cpu").shape == (12, 64, 4, 32)
     assert workloads.get("c3_single_seq").shape == (1, 256, 1, 64)
