@@ -129,8 +129,7 @@ __global__ __launch_bounds__(256, 1) void bob_q_kernel(
         a = M::mma(gvt_.along_cols(st * 32 + l32, kk, h), of[kk], a);
       }
       // register r = key row ka + acc_row(r, h), column = query row q
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
+      auto elem = [&](int r) ATTN_INLINE {
         float p = fast_exp2(__builtin_fmaf(s[r], scale_log2, Lq));
         if (masked && ka + acc_row(r, h) > q) p = 0.f;
         const float dpd = dp[r] + Dq;                 // dP - D
@@ -145,26 +144,45 @@ __global__ __launch_bounds__(256, 1) void bob_q_kernel(
           g[r] = p * (a[r] + dpd * (gg - rq) - eq);     // dS2
           a[r] = w;                                     // W
         }
-      }
-      if constexpr (PASS == 2) {
-        frag bp[RS], bds[RS], bds2[RS], bw[RS];
+      };
+      if constexpr (PASS == 1) {
 #pragma unroll
-        for (int ss = 0; ss < RS; ++ss) {
+        for (int r = 0; r < 16; ++r) elem(r);
+      } else {
+        // The first half of the registers (K steps 0 .. RS/2 - 1) is packed
+        // first; its products run while the VALU works on the second half.
+        constexpr int HS = RS / 2, NG = HS * MT;
+        frag bp[RS], bds[RS], bds2[RS], bw[RS];
+        auto pack = [&](int ss) ATTN_INLINE {
           bp[ss] = M::pack(s, ss);
           bds[ss] = M::pack(dp, ss);
           bds2[ss] = M::pack(g, ss);
           bw[ss] = M::pack(a, ss);
-        }
+        };
         // hQ^T += K^T dS2^T + gK^T dS^T;  hdO^T += gV^T P^T + V^T W^T
+        auto prods = [&](int ss, int mt) ATTN_INLINE {
+          acc_q[mt] = M::mma(kt_.along_rows(mt * 32 + l32, st * 32, ss, h), bds2[ss], acc_q[mt]);
+          acc_q[mt] = M::mma(gkt_.along_rows(mt * 32 + l32, st * 32, ss, h), bds[ss], acc_q[mt]);
+          acc_o[mt] = M::mma(gvt_.along_rows(mt * 32 + l32, st * 32, ss, h), bp[ss], acc_o[mt]);
+          acc_o[mt] = M::mma(vt_.along_rows(mt * 32 + l32, st * 32, ss, h), bw[ss], acc_o[mt]);
+        };
 #pragma unroll
-        for (int ss = 0; ss < RS; ++ss)
+        for (int r = 0; r < 8; ++r) elem(r);
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            acc_q[mt] = M::mma(kt_.along_rows(mt * 32 + l32, st * 32, ss, h), bds2[ss], acc_q[mt]);
-            acc_q[mt] = M::mma(gkt_.along_rows(mt * 32 + l32, st * 32, ss, h), bds[ss], acc_q[mt]);
-            acc_o[mt] = M::mma(gvt_.along_rows(mt * 32 + l32, st * 32, ss, h), bp[ss], acc_o[mt]);
-            acc_o[mt] = M::mma(vt_.along_rows(mt * 32 + l32, st * 32, ss, h), bw[ss], acc_o[mt]);
-          }
+        for (int ss = 0; ss < HS; ++ss) pack(ss);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < NG; ++i) {
+          prods(i / MT, i % MT);
+#pragma unroll
+          for (int r = 8 + 8 * i / NG; r < 8 + 8 * (i + 1) / NG; ++r) elem(r);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int ss = HS; ss < RS; ++ss) pack(ss);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < NG; ++i) prods(HS + i / MT, i % MT);
       }
     }
   };
@@ -303,42 +321,59 @@ __global__ __launch_bounds__(256, 1) void bob_kv_kernel(
         dp = M::mma(oc, vf[ks], dp);
         a = M::mma(oc, gvf[ks], a);
       }
-      // register r = query row qa + acc_row(r, h), column = key row kv
+      // register r = query row qa + acc_row(r, h), column = key row kv; the
+      // row scalars of registers 4 gi .. 4 gi + 3
+      f32x4 lg[4], dg[4], rg[4], eg[4];
 #pragma unroll
       for (int gi = 0; gi < 4; ++gi) {
         const int i0 = st * 32 + 8 * gi + 4 * h;
-        const f32x4 lg = *reinterpret_cast<const f32x4*>(&B.l[i0]);
-        const f32x4 dg = *reinterpret_cast<const f32x4*>(&B.dd[i0]);
-        const f32x4 rg = *reinterpret_cast<const f32x4*>(&B.r[i0]);
-        const f32x4 eg = *reinterpret_cast<const f32x4*>(&B.e[i0]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * gi + i;
-          float p = fast_exp2(__builtin_fmaf(s[r], scale_log2, lg[i]));
-          if (masked && kv > qa + acc_row(r, h)) p = 0.f;
-          const float dpd = dp[r] + dg[i];            // dP - D
-          const float gg = g[r] * scale;              // G
-          dp[r] = p * dpd;                            // dS
-          s[r] = p * (a[r] + dpd * (gg - rg[i]) - eg[i]);   // dS2
-          a[r] = p * (gg - rg[i]);                    // W
-        }
+        lg[gi] = *reinterpret_cast<const f32x4*>(&B.l[i0]);
+        dg[gi] = *reinterpret_cast<const f32x4*>(&B.dd[i0]);
+        rg[gi] = *reinterpret_cast<const f32x4*>(&B.r[i0]);
+        eg[gi] = *reinterpret_cast<const f32x4*>(&B.e[i0]);
       }
+      auto elem = [&](int r) ATTN_INLINE {
+        const int gi = r / 4, i = r % 4;
+        float p = fast_exp2(__builtin_fmaf(s[r], scale_log2, lg[gi][i]));
+        if (masked && kv > qa + acc_row(r, h)) p = 0.f;
+        const float dpd = dp[r] + dg[gi][i];        // dP - D
+        const float gg = g[r] * scale;              // G
+        dp[r] = p * dpd;                            // dS
+        s[r] = p * (a[r] + dpd * (gg - rg[gi][i]) - eg[gi][i]);   // dS2
+        a[r] = p * (gg - rg[gi][i]);                // W
+      };
+      // The first half of the registers (K steps 0 .. RS/2 - 1) is packed
+      // first; its products run while the VALU works on the second half.
+      constexpr int HS = RS / 2, NG = HS * MT;
       frag bds[RS], bds2[RS], bw[RS];
-#pragma unroll
-      for (int ss = 0; ss < RS; ++ss) {
+      auto pack = [&](int ss) ATTN_INLINE {
         bds[ss] = M::pack(dp, ss);
         bds2[ss] = M::pack(s, ss);
         bw[ss] = M::pack(a, ss);
-      }
+      };
       // hV^T += dO^T W;  hK^T += Q^T dS2 + gQ^T dS
+      auto prods = [&](int ss, int mt) ATTN_INLINE {
+        acc_v[mt] = M::mma(ot_.along_rows(mt * 32 + l32, st * 32, ss, h), bw[ss], acc_v[mt]);
+        acc_k[mt] = M::mma(qt_.along_rows(mt * 32 + l32, st * 32, ss, h), bds2[ss], acc_k[mt]);
+        acc_k[mt] = M::mma(gqt_.along_rows(mt * 32 + l32, st * 32, ss, h), bds[ss], acc_k[mt]);
+      };
 #pragma unroll
-      for (int ss = 0; ss < RS; ++ss)
+      for (int r = 0; r < 8; ++r) elem(r);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          acc_v[mt] = M::mma(ot_.along_rows(mt * 32 + l32, st * 32, ss, h), bw[ss], acc_v[mt]);
-          acc_k[mt] = M::mma(qt_.along_rows(mt * 32 + l32, st * 32, ss, h), bds2[ss], acc_k[mt]);
-          acc_k[mt] = M::mma(gqt_.along_rows(mt * 32 + l32, st * 32, ss, h), bds[ss], acc_k[mt]);
-        }
+      for (int ss = 0; ss < HS; ++ss) pack(ss);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < NG; ++i) {
+        prods(i / MT, i % MT);
+#pragma unroll
+        for (int r = 8 + 8 * i / NG; r < 8 + 8 * (i + 1) / NG; ++r) elem(r);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int ss = HS; ss < RS; ++ss) pack(ss);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < NG; ++i) prods(HS + i / MT, i % MT);
     }
   };
 
