@@ -121,17 +121,26 @@ __global__ __launch_bounds__(256, 1) void bob_q_kernel(
         s = M::mma(kc, qf[kk], s);
         g = M::mma(kc, gqf[kk], g);
       }
+      // register r = key row ka + acc_row(r, h), column = query row q.  S is
+      // complete here: P = exp2(S scale log2 e - L2) is formed beside the G,
+      // dP and A products (scheduling fences keep the interleave).
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
         g = M::mma(gkt_.along_cols(st * 32 + l32, kk, h), qf[kk], g);
         const frag vc = vt_.along_cols(st * 32 + l32, kk, h);
         dp = M::mma(vc, of[kk], dp);
         a = M::mma(gvt_.along_cols(st * 32 + l32, kk, h), of[kk], a);
+#pragma unroll
+        for (int r = 16 * kk / KS; r < 16 * (kk + 1) / KS; ++r) {
+          float p = fast_exp2(__builtin_fmaf(s[r], scale_log2, Lq));
+          if (masked && ka + acc_row(r, h) > q) p = 0.f;
+          s[r] = p;
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      // register r = key row ka + acc_row(r, h), column = query row q
       auto elem = [&](int r) ATTN_INLINE {
-        float p = fast_exp2(__builtin_fmaf(s[r], scale_log2, Lq));
-        if (masked && ka + acc_row(r, h) > q) p = 0.f;
+        const float p = s[r];
         const float dpd = dp[r] + Dq;                 // dP - D
         const float gg = g[r] * scale;                // G
         if constexpr (PASS == 1) {
@@ -314,13 +323,6 @@ __global__ __launch_bounds__(256, 1) void bob_kv_kernel(
         s = M::mma(qc, kf[ks], s);
         g = M::mma(qc, gkf[ks], g);
       }
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        g = M::mma(gqt_.along_cols(st * 32 + l32, ks, h), kf[ks], g);
-        const frag oc = ot_.along_cols(st * 32 + l32, ks, h);
-        dp = M::mma(oc, vf[ks], dp);
-        a = M::mma(oc, gvf[ks], a);
-      }
       // register r = query row qa + acc_row(r, h), column = key row kv; the
       // row scalars of registers 4 gi .. 4 gi + 3
       f32x4 lg[4], dg[4], rg[4], eg[4];
@@ -332,10 +334,25 @@ __global__ __launch_bounds__(256, 1) void bob_kv_kernel(
         rg[gi] = *reinterpret_cast<const f32x4*>(&B.r[i0]);
         eg[gi] = *reinterpret_cast<const f32x4*>(&B.e[i0]);
       }
+      // S is complete here: P is formed beside the G, dP and A products
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        g = M::mma(gqt_.along_cols(st * 32 + l32, ks, h), kf[ks], g);
+        const frag oc = ot_.along_cols(st * 32 + l32, ks, h);
+        dp = M::mma(oc, vf[ks], dp);
+        a = M::mma(oc, gvf[ks], a);
+#pragma unroll
+        for (int r = 16 * ks / KS; r < 16 * (ks + 1) / KS; ++r) {
+          float p = fast_exp2(__builtin_fmaf(s[r], scale_log2, lg[r / 4][r % 4]));
+          if (masked && kv > qa + acc_row(r, h)) p = 0.f;
+          s[r] = p;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
       auto elem = [&](int r) ATTN_INLINE {
         const int gi = r / 4, i = r % 4;
-        float p = fast_exp2(__builtin_fmaf(s[r], scale_log2, lg[gi][i]));
-        if (masked && kv > qa + acc_row(r, h)) p = 0.f;
+        const float p = s[r];
         const float dpd = dp[r] + dg[gi][i];        // dP - D
         const float gg = g[r] * scale;              // G
         dp[r] = p * dpd;                            // dS
