@@ -26,21 +26,25 @@ int finish(hipError_t e) {
   return ATTN_OK;
 }
 
-// Sizes: each >= 1; grid limits (B, H <= 65535; B*H*N < 2^31); byte counts fit.
+// Sizes: each >= 1; grid limits (B, H <= 65535); B*H*N < 2^31 rows, so with
+// d <= 256 every element offset (64-bit in the kernels) is below 2^39.
 int check_sizes(int B, int H, int N, int d) {
   if (B < 1 || H < 1 || N < 1 || d < 1) return ATTN_ERR_INVALID;
   if (B > 65535 || H > 65535) return ATTN_ERR_UNSUPPORTED;
   const int64_t rows = (int64_t)B * H * N;
   if (rows >= ((int64_t)1 << 31)) return ATTN_ERR_UNSUPPORTED;
-  if (rows * d >= ((int64_t)1 << 40)) return ATTN_ERR_UNSUPPORTED;
   return ATTN_OK;
 }
 
-int check_dtype_dim(int d, int dtype) {
+// Head dim and dtype; then the generic kernels' grid: wide heads run
+// column_parts(d, dtype) workgroups per block along the grid's y axis, so
+// H * parts must stay within its 65535 limit.
+int check_dtype_dim(int H, int d, int dtype) {
   if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
   if (d > (dtype == ATTN_BF16 ? 256 : 128)) return ATTN_ERR_UNSUPPORTED;
   if (dtype == ATTN_F32 && d % 4 != 0) return ATTN_ERR_UNSUPPORTED;
   if (dtype == ATTN_BF16 && d % 8 != 0) return ATTN_ERR_UNSUPPORTED;
+  if ((int64_t)H * attn::column_parts(d, dtype) > 65535) return ATTN_ERR_UNSUPPORTED;
   return ATTN_OK;
 }
 
@@ -94,7 +98,7 @@ int attn_fwd_lse(const void* Q, const void* K, const void* V, void* O, float* L,
   ATTN_TRY(check_ptrs({Q, K, V, O, L}));
   ATTN_TRY(check_sizes(B, H, N, d));
   ATTN_TRY(check_scale_causal(scale, causal));
-  ATTN_TRY(check_dtype_dim(d, dtype));
+  ATTN_TRY(check_dtype_dim(H, d, dtype));
   attn::FwdArgs a;
   a.Q = Q; a.K = K; a.V = V; a.O = O; a.L = L;
   a.B = B; a.H = H; a.N = N; a.d = d;
@@ -108,7 +112,7 @@ int attn_fwd_lse_masked(const void* Q, const void* K, const void* V, void* O, fl
   ATTN_TRY(check_ptrs({Q, K, V, O, L}));
   ATTN_TRY(check_sizes(B, H, N, d));
   ATTN_TRY(check_scale_causal(scale, causal));
-  ATTN_TRY(check_dtype_dim(d, dtype));
+  ATTN_TRY(check_dtype_dim(H, d, dtype));
   ATTN_TRY(check_mask(mask, mask_heads, B, H, N));
   attn::FwdArgs a;
   a.Q = Q; a.K = K; a.V = V; a.O = O; a.L = L;
@@ -127,7 +131,7 @@ int attn_bwd_preprocess(const void* O, const void* dO, const float* L, void* wor
                         int H, int N, int d, int dtype, void* stream) {
   ATTN_TRY(check_ptrs({O, dO, L, workspace}));
   ATTN_TRY(check_sizes(B, H, N, d));
-  ATTN_TRY(check_dtype_dim(d, dtype));
+  ATTN_TRY(check_dtype_dim(H, d, dtype));
   return finish(attn::launch_bwd_preprocess(O, dO, L, static_cast<float*>(workspace), B, H, N, d,
                                             dtype, static_cast<hipStream_t>(stream)));
 }
@@ -138,7 +142,7 @@ int attn_bwd_dkdv(const void* Q, const void* K, const void* V, const void* dO,
   ATTN_TRY(check_ptrs({Q, K, V, dO, workspace, dK, dV}));
   ATTN_TRY(check_sizes(B, H, N, d));
   ATTN_TRY(check_scale_causal(scale, causal));
-  ATTN_TRY(check_dtype_dim(d, dtype));
+  ATTN_TRY(check_dtype_dim(H, d, dtype));
   const attn::BwdArgs a =
       make_bwd(Q, K, V, dO, workspace, nullptr, dK, dV, B, H, N, d, causal, scale, dtype);
   return finish(attn::launch_bwd_dkdv(a, static_cast<hipStream_t>(stream)));
@@ -150,7 +154,7 @@ int attn_bwd_dq(const void* Q, const void* K, const void* V, const void* dO,
   ATTN_TRY(check_ptrs({Q, K, V, dO, workspace, dQ}));
   ATTN_TRY(check_sizes(B, H, N, d));
   ATTN_TRY(check_scale_causal(scale, causal));
-  ATTN_TRY(check_dtype_dim(d, dtype));
+  ATTN_TRY(check_dtype_dim(H, d, dtype));
   const attn::BwdArgs a =
       make_bwd(Q, K, V, dO, workspace, dQ, nullptr, nullptr, B, H, N, d, causal, scale, dtype);
   return finish(attn::launch_bwd_dq(a, static_cast<hipStream_t>(stream)));
@@ -162,7 +166,7 @@ int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const v
   ATTN_TRY(check_ptrs({Q, K, V, O, dO, L, dQ, dK, dV, workspace}));
   ATTN_TRY(check_sizes(B, H, N, d));
   ATTN_TRY(check_scale_causal(scale, causal));
-  ATTN_TRY(check_dtype_dim(d, dtype));
+  ATTN_TRY(check_dtype_dim(H, d, dtype));
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = attn::launch_bwd_preprocess(O, dO, L, static_cast<float*>(workspace), B, H, N,
                                              d, dtype, s);
@@ -181,7 +185,7 @@ int attn_bwd_masked(const void* Q, const void* K, const void* V, const void* O, 
   ATTN_TRY(check_ptrs({Q, K, V, O, dO, L, dQ, dK, dV, workspace}));
   ATTN_TRY(check_sizes(B, H, N, d));
   ATTN_TRY(check_scale_causal(scale, causal));
-  ATTN_TRY(check_dtype_dim(d, dtype));
+  ATTN_TRY(check_dtype_dim(H, d, dtype));
   ATTN_TRY(check_mask(mask, mask_heads, B, H, N));
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = attn::launch_bwd_preprocess(O, dO, L, static_cast<float*>(workspace), B, H, N,
@@ -203,7 +207,7 @@ int attn_bwd_dkdv_masked(const void* Q, const void* K, const void* V, const void
   ATTN_TRY(check_ptrs({Q, K, V, dO, workspace, dK, dV}));
   ATTN_TRY(check_sizes(B, H, N, d));
   ATTN_TRY(check_scale_causal(scale, causal));
-  ATTN_TRY(check_dtype_dim(d, dtype));
+  ATTN_TRY(check_dtype_dim(H, d, dtype));
   ATTN_TRY(check_mask(mask, mask_heads, B, H, N));
   attn::BwdArgs a =
       make_bwd(Q, K, V, dO, workspace, nullptr, dK, dV, B, H, N, d, causal, scale, dtype);
@@ -219,7 +223,7 @@ int attn_bwd_dq_masked(const void* Q, const void* K, const void* V, const void* 
   ATTN_TRY(check_ptrs({Q, K, V, dO, workspace, dQ}));
   ATTN_TRY(check_sizes(B, H, N, d));
   ATTN_TRY(check_scale_causal(scale, causal));
-  ATTN_TRY(check_dtype_dim(d, dtype));
+  ATTN_TRY(check_dtype_dim(H, d, dtype));
   ATTN_TRY(check_mask(mask, mask_heads, B, H, N));
   attn::BwdArgs a =
       make_bwd(Q, K, V, dO, workspace, dQ, nullptr, nullptr, B, H, N, d, causal, scale, dtype);
@@ -240,7 +244,7 @@ int attn_bwd_bwd(const void* Q, const void* K, const void* V, const void* O, con
   ATTN_TRY(check_ptrs({Q, K, V, O, dO, L, gQ, gK, gV, hQ, hK, hV, hdO, workspace}));
   ATTN_TRY(check_sizes(B, H, N, d));
   ATTN_TRY(check_scale_causal(scale, causal));
-  ATTN_TRY(check_dtype_dim(d, dtype));
+  ATTN_TRY(check_dtype_dim(H, d, dtype));
   if (d > (dtype == ATTN_BF16 ? 128 : 64)) return ATTN_ERR_UNSUPPORTED;
   attn::BobArgs a;
   a.Q = Q; a.K = K; a.V = V; a.O = O; a.dO = dO; a.L = L;

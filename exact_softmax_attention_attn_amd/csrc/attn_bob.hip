@@ -1,10 +1,11 @@
 // Backward of the backward: gradients of l2 = <gQ, dQ> + <gK, dK> + <gV, dV>
 // with respect to Q, K, V and dO, with no N x N intermediate in memory.
 //
-// The FlashBoB paper's abstract ("FlashBoB: exact, I/O-efficient backward-
-// over-backward for softmax attention") states the structure used here: two
-// row-wise scalars fix every output through affine maps, which gives a
-// two-pass schedule over recomputed tiles.  Written out from the chain rule,
+// Source: the page headed "Approaching I/O-optimality for Approximate
+// Attention", its first abstract (FlashBoB), which sets the goal -- the exact
+// gradient of the backward pass, with no N x N array in memory -- and says
+// that a pair of per-row quantities is all such a pass needs beyond the
+// recomputed tiles.  The formulas below are derived here from the chain rule,
 // with P, dP = dO V^T, D and dS = P o (dP - D) as in the first backward:
 //   G = scale (gQ K^T + Q gK^T)    (cotangent of dS)
 //   A = dO gV^T                    (cotangent of P through dV)
@@ -107,13 +108,19 @@ __global__ __launch_bounds__(256, 1) void bob_q_kernel(
     fill_sync(KT{B.gv}, gV + base, rs, k0, N, d, tid);
   };
 
+  // masked tiles keep key rows up to the lane's query (causal) and below N:
+  // the zero rows padding the sequence's ragged last tile give S = 0, so
+  // P = exp(-L), which overflows for L below about -88 and must not reach the
+  // products (0 * inf)
+  const int klim = CAUSAL ? q : N - 1;              // last kept key of the lane's query
+  const int wlim = CAUSAL ? qw + 31 : N - 1;        // ... of any query of the wave
   auto body = [&](const Buf& B, int k0, bool masked) ATTN_INLINE {
     const KT kt_{const_cast<T*>(B.k)}, vt_{const_cast<T*>(B.v)};
     const KT gkt_{const_cast<T*>(B.gk)}, gvt_{const_cast<T*>(B.gv)};
 #pragma unroll 1
     for (int st = 0; st < BKV / 32; ++st) {
       const int ka = k0 + st * 32;
-      if (masked && ka > qw + 31) continue;          // every pair above the diagonal
+      if (masked && ka > wlim) continue;             // every pair masked
       f32x16 s = zero16(), dp = zero16(), g = zero16(), a = zero16();
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
@@ -134,7 +141,7 @@ __global__ __launch_bounds__(256, 1) void bob_q_kernel(
 #pragma unroll
         for (int r = 16 * kk / KS; r < 16 * (kk + 1) / KS; ++r) {
           float p = fast_exp2(__builtin_fmaf(s[r], scale_log2, Lq));
-          if (masked && ka + acc_row(r, h) > q) p = 0.f;
+          if (masked && ka + acc_row(r, h) > klim) p = 0.f;
           s[r] = p;
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -199,7 +206,7 @@ __global__ __launch_bounds__(256, 1) void bob_q_kernel(
   auto step = [&](const Buf& cur, Buf& nxt, int kt) ATTN_INLINE {
     if (kt + 1 < nkt) fill(nxt, kt + 1);
     const int k0 = kt * BKV;
-    body(cur, k0, CAUSAL && k0 + BKV - 1 > qb);
+    body(cur, k0, (CAUSAL && k0 + BKV - 1 > qb) || k0 + BKV > N);
     wait_async_fills();
     __syncthreads();
   };

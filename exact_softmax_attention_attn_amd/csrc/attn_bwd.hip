@@ -332,13 +332,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
     fill_sync(KT{B.v}, V + base, rs, k0, N, d, tid);
   };
 
+  // MASKED tiles keep key rows up to the lane's query (causal) and below N:
+  // the zero rows padding the sequence's ragged last tile give S = 0, so
+  // P = exp(-L), which overflows for L below about -88 and must not reach the
+  // products (0 * inf)
+  const int klim = CAUSAL ? q : N - 1;              // last kept key of the lane's query
+  const int wlim = CAUSAL ? qw + 31 : N - 1;        // ... of any query of the wave
   auto body = [&](const Buf& B, int k0, auto masked_c) ATTN_INLINE {
     constexpr bool MASKED = decltype(masked_c)::value;
     const KT kt_{const_cast<T*>(B.k)}, vt_{const_cast<T*>(B.v)};
 #pragma unroll
     for (int st = 0; st < BKV / 32; ++st) {
       const int ka = k0 + st * 32;
-      if (MASKED && ka > qw + 31) continue;        // every pair above the diagonal
+      if (MASKED && ka > wlim) continue;           // every pair masked
       frag ak[KS], av[KS];
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) ak[kk] = kt_.along_cols(st * 32 + l32, kk, h);
@@ -353,7 +359,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float p = fast_exp2(__builtin_fmaf(s[r], scale_log2, Lq));
-        if (MASKED && ka + acc_row(r, h) > q) p = 0.f;
+        if (MASKED && ka + acc_row(r, h) > klim) p = 0.f;
         dp[r] = p * (dp[r] + Dq);
       }
       frag bds[RS];
@@ -371,7 +377,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
   auto step = [&](const Buf& cur, Buf& nxt, int p) ATTN_INLINE {
     const int k0 = tile_at(p) * BKV;
     if (p + 1 < ntiles) fill(nxt, tile_at(p + 1));
-    if (CAUSAL && k0 + BKV - 1 > qb)
+    if ((CAUSAL && k0 + BKV - 1 > qb) || k0 + BKV > N)
       body(cur, k0, bool_c<true>{});
     else
       body(cur, k0, bool_c<false>{});

@@ -9,8 +9,10 @@
 //    reads next (S, dP) land in VGPRs;
 //  - the streamed tile operands are read from LDS a few fragments ahead of the
 //    product that consumes them, in a fixed order held by scheduling fences;
-//  - the row scalars (-L log2 e and -D) are added by the matrix cores, so the
-//    VALU is left with one exp2 and one multiply per score;
+//  - the scores are scaled in float32 (one FMA with the row's -L log2 e per
+//    score, ahead of its exp2), so they are the forward's to float32
+//    rounding; -D is added by the matrix cores, so dS = P o (dP - D) is one
+//    multiply per score;
 //  - streamed tiles are copied global->LDS two steps ahead into a ring of
 //    three separately named buffers, with direct-to-LDS copies that the
 //    compiler does not track and explicit waits before each hand-off.
@@ -36,13 +38,13 @@ __device__ __forceinline__ f32x4 lds_f32x4(const float* p) {
 
 // ---------------------------------------------------------------------------
 // dK, dV (bf16).  Workgroup = 4 waves = 128 key rows of one (b, h); wave w
-// owns key rows kv0 + [0, 32).  Its K rows (pre-multiplied by scale log2e)
-// and V rows sit in AGPRs as the B operands of S = Q K^T and dP = dO V^T
-// (column n = key row), so the results hold query rows along the registers:
-// the row scalars -L log2e and -D then enter as the MFMA's C input, read from
-// LDS straight into the accumulator registers, and
-//   S' = Q (c K)^T - L2 = log2 of P,   dP' = dO V^T - D
-// leave one exp2 and one multiply per element:  P = exp2(S'), dS = P o dP'.
+// owns key rows kv0 + [0, 32).  Its K and V rows sit in AGPRs as the B
+// operands of S = Q K^T and dP = dO V^T (column n = key row), so the results
+// hold query rows along the registers and the row scalars -L log2e and -D are
+// per register: -D enters as the MFMA's C input, read from LDS straight into
+// the accumulator registers, and -L2 is the addend of one FMA per element, so
+//   P = exp2(c S - L2)  (c = scale log2 e, in float32: the forward's scores
+//   to float32 rounding),   dP' = dO V^T - D,   dS = P o dP'.
 // dV^T += dO^T P and dK^T += Q^T dS accumulate in AGPRs (asm MFMA).  The
 // operand reads (Q, dO along the head dim; dO, Q across positions) run AH
 // fragments ahead through a whole 64-row query tile.  Causal: only the two
@@ -87,8 +89,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
   load_row_frags<bf16, D>(vf, V + base, rs, kv, N, d, h);
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-    for (int t = 0; t < 8; ++t) kf[ks][t] = (bf16)((float)kf[ks][t] * scale_log2);
     pin_agpr(kf[ks]);
     pin_agpr(vf[ks]);
   }
@@ -152,8 +152,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
   // Each VALU stage reads a chain that finished at least one chain earlier:
   // the exps of S_a run beside dK_p and dP_a, dS_a beside S_b, the exps of
   // S_b beside dV_a and dP_b, dS_b beside dK_a; P_b and dS_b leave packed for
-  // the next step.  The row scalars that enter S and dP as C inputs are read
-  // from LDS one chain ahead, and operand reads run AH fragments ahead
+  // the next step.  The row scalars (-L2 for the exps, -D as dP's C input)
+  // are read from LDS one chain ahead, and operand reads run AH fragments ahead
   // through the step, so no chain starts on a fresh LDS read.
   constexpr int L = KS;                       // = 2 * MT
   static_assert(L == 2 * MT, "chain length");
@@ -166,6 +166,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
       for (int i = 0; i < 4; ++i) v[4 * g + i] = x[i];
     }
     return v;
+  };
+  // P from a raw score and its row's -L2
+  auto pexp = [&](float sraw, float nl2) ATTN_INLINE {
+    return fast_exp2(__builtin_fmaf(sraw, scale_log2, nl2));
   };
   auto mask_rows = [&](f32x16& p, int qa) ATTN_INLINE {
 #pragma unroll
@@ -234,7 +238,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
         fence();
       }
     };
-    f32x16 sa = row_scalars(B.l, 0);             // S_a's C input, read during dV_p
+    const f32x16 la = row_scalars(B.l, 0);       // -L2 of S_a's rows, read during dV_p
+    f32x16 sa = zero16();
     fence();
     // dV_p
     if constexpr (HP) {
@@ -258,18 +263,18 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
         slot(C_DKP, i);
       }
 #pragma unroll
-      for (int e = 0; e < E; ++e) sa[i * E + e] = fast_exp2(sa[i * E + e]);
+      for (int e = 0; e < E; ++e) sa[i * E + e] = pexp(sa[i * E + e], la[i * E + e]);
       fence();
     }
     // dP_a | exps of S_a, second half
-    f32x16 sb = row_scalars(B.l, 32);            // S_b's C input
+    const f32x16 lb = row_scalars(B.l, 32);      // -L2 of S_b's rows
 #pragma unroll
     for (int i = 0; i < L; ++i) {
       pa = M::mma(ring[(C_DPA * L + i) % AH], vf[i], pa);
       refill(C_DPA * L + i);
       slot(C_DPA, i);
 #pragma unroll
-      for (int e = 0; e < E; ++e) sa[8 + i * E + e] = fast_exp2(sa[8 + i * E + e]);
+      for (int e = 0; e < E; ++e) sa[8 + i * E + e] = pexp(sa[8 + i * E + e], la[8 + i * E + e]);
       fence();
     }
     if (CAUSAL && masked) mask_rows(sa, qa);
@@ -278,6 +283,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     pin_operand(bpa[1]);
     fence();
     // S_b | dS_a = P_a o dP'_a
+    f32x16 sb = zero16();
 #pragma unroll
     for (int i = 0; i < L; ++i) {
       sb = M::mma(ring[(C_SB * L + i) % AH], kf[i], sb);
@@ -299,7 +305,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
       refill(C_DVA * L + i);
       slot(C_DVA, i);
 #pragma unroll
-      for (int e = 0; e < E; ++e) sb[i * E + e] = fast_exp2(sb[i * E + e]);
+      for (int e = 0; e < E; ++e) sb[i * E + e] = pexp(sb[i * E + e], lb[i * E + e]);
       fence();
     }
     // dP_b | exps of S_b, second half
@@ -309,7 +315,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
       refill(C_DPB * L + i);
       slot(C_DPB, i);
 #pragma unroll
-      for (int e = 0; e < E; ++e) sb[8 + i * E + e] = fast_exp2(sb[8 + i * E + e]);
+      for (int e = 0; e < E; ++e) sb[8 + i * E + e] = pexp(sb[8 + i * E + e], lb[8 + i * E + e]);
       fence();
     }
     if (CAUSAL && masked) mask_rows(sb, qa + 32);
@@ -419,19 +425,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
 
 // ---------------------------------------------------------------------------
 // dQ (bf16).  Workgroup = NW waves = 256 query rows of one (b, h); wave w owns
-// query rows qw + [0, WQ) as two halves of 32 rows.  Q (pre-multiplied by
-// scale log2e) and dO of the wave's rows and its dQ^T accumulators live in
-// AGPRs for the whole kernel.  With two halves each LDS operand fragment
-// feeds two matrix instructions.  Per key sub-tile of 32 rows:
-//   S'^T = K (c Q)^T - L2,  dP'^T = V dO^T - D,  P = exp2(S'),
+// query rows qw + [0, WQ) as two halves of 32 rows.  Q and dO of the wave's
+// rows and its dQ^T accumulators live in AGPRs for the whole kernel.  With two
+// halves each LDS operand fragment feeds two matrix instructions.  Per key
+// sub-tile of 32 rows:
+//   S^T = K Q^T,  dP'^T = V dO^T - D,  P = exp2(c S - L2)  (c = scale log2 e),
 //   dS = P o dP',  dQ^T += K^T dS^T.
-// The query rows run along the lanes here, so the row scalars cannot enter as
-// a per-register C input; instead each chain starts with one extra product of
-// a constant "ones" fragment and a fragment carrying the row scalar split
-// into two bf16 parts (hi + lo, exact to about 2^-16 relative), which adds the
-// scalar to every element.  That costs one matrix instruction per chain and
-// saves an add per element on the VALU.  The two halves' chains run one
-// after the other, so each VALU stage sits beside a chain it does not feed.
+// The scores are scaled in float32 (one FMA with the lane's -L2 per element,
+// the query rows run along the lanes), so they are the forward's scores to
+// float32 rounding.  -D cannot enter as a per-register C input either; each dP
+// chain starts with one extra product of a constant "ones" fragment and a
+// fragment carrying -D split into two bf16 parts (hi + lo, exact to about
+// 2^-16 relative), which adds it to every element.  The two halves' chains run
+// one after the other, so each VALU stage sits beside a chain it does not feed.
 // Key tiles are copied two steps ahead into a ring of three separately named
 // LDS buffers.  No atomics.
 // ---------------------------------------------------------------------------
@@ -468,9 +474,10 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
   const int qw = qb + wave * WQ;               // this wave's first query row
   LanePlan<D> plan(lane);
   frag qf[NH][KS], of[NH][KS];
-  // bias operands: ones[k] = 1 for k in {0, 1}; bl/bd[k] = (hi, lo) of the
-  // lane's row scalar for k in {0, 1}; zero elsewhere (K slots 8h .. 8h + 7)
-  frag ones, bl[NH], bd[NH];
+  // bias operands: ones[k] = 1 for k in {0, 1}; bd[k] = (hi, lo) of the lane's
+  // -D for k in {0, 1}; zero elsewhere (K slots 8h .. 8h + 7)
+  frag ones, bd[NH];
+  float nl2[NH];                               // -L log2 e of the lane's query, per half
   const bf16 one = (bf16)1.f, zero = (bf16)0.f;
   ones = h == 0 ? frag{one, one, zero, zero, zero, zero, zero, zero} : frag{};
 #pragma unroll
@@ -480,19 +487,14 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
     load_row_frags<bf16, D>(of[c], dO + base, rs, q, N, d, h);
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qf[c][kk][e] = (bf16)((float)qf[c][kk][e] * scale_log2);
       pin_agpr(qf[c][kk]);
       pin_agpr(of[c][kk]);
     }
-    // padded rows (q >= N) and rows with no kept key (L = -inf): S' = -inf so
-    // P = 0 (lo part 0, never inf - inf)
-    const float lq = q < N ? Lh[q] : -__builtin_inff();
+    // padded rows (q >= N) and rows with no kept key (stored -inf): P = 0
+    nl2[c] = q < N ? Lh[q] : -__builtin_inff();
     const float dq = q < N ? Dh[q] : 0.f;
-    const bf16 lhi = (bf16)lq, dhi = (bf16)dq;
-    const bf16 llo = lq > -__builtin_inff() ? (bf16)(lq - (float)lhi) : zero;
+    const bf16 dhi = (bf16)dq;
     const bf16 dlo = (bf16)(dq - (float)dhi);
-    bl[c] = h == 0 ? frag{lhi, llo, zero, zero, zero, zero, zero, zero} : frag{};
     bd[c] = h == 0 ? frag{dhi, dlo, zero, zero, zero, zero, zero, zero} : frag{};
   }
 
@@ -585,12 +587,17 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
       fence();
     }
   };
-  // P = 0 above the diagonal (causal) or everywhere (the wave's mask row drops the tile)
+  // P = 0 above the diagonal (causal), on the padded keys of the sequence's
+  // ragged last tile (whose zero rows give S = 0 and so P = exp(-L), which
+  // overflows for L below about -88), or everywhere (the wave's mask row
+  // drops the tile)
   auto mask_half = [&](f32x16& s, int c, int ka, bool kill) ATTN_INLINE {
     const int q = qw + 32 * c + l32;
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      if (kill || (CAUSAL && ka + acc_row(r, h) > q)) s[r] = 0.f;
+    for (int r = 0; r < 16; ++r) {
+      const int k = ka + acc_row(r, h);
+      if (kill || (CAUSAL && k > q) || k >= N) s[r] = 0.f;
+    }
   };
   // sub-tile st of B (key rows ka ..), K fragments already in kf; leaves
   // dQ_1 pending in tf and bds1
@@ -598,28 +605,29 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
     const int r0 = st * 32;
     constexpr int E = 16 / KS;                  // elements per product in the exp and dS_0 stages
     f32x16 sc[2], pc[2];
-    // S'_0^T = ones bl_0^T + K (c Q_0)^T
-    sc[0] = M::mma(ones, bl[0], zero16());
+    // S_0^T = K Q_0^T
+    sc[0] = M::mma(kf[0], qf[0][0], zero16());
+    copy(st * SPS);
     fence();
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
+    for (int kk = 1; kk < KS; ++kk) {
       sc[0] = M::mma(kf[kk], qf[0][kk], sc[0]);
       if (kk % (KS / SPS) == 0) copy(st * SPS + kk / (KS / SPS));
       fence();
     }
-    // S'_1 | P_0 = exp2(S'_0); first half of V read (KS / 2 products ahead)
-    sc[1] = M::mma(ones, bl[1], zero16());
-    fence();
+    // S_1 | P_0 = exp2(c S_0 - L2); first half of V read (KS / 2 products ahead)
+    sc[1] = zero16();
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       sc[1] = M::mma(kf[kk], qf[1][kk], sc[1]);
       if (kk >= KS / 2) vf[kk - KS / 2] = plan.cols(B.v, r0, kk - KS / 2);
 #pragma unroll
-      for (int e = 0; e < E; ++e) sc[0][kk * E + e] = fast_exp2(sc[0][kk * E + e]);
+      for (int e = 0; e < E; ++e)
+        sc[0][kk * E + e] = fast_exp2(__builtin_fmaf(sc[0][kk * E + e], scale_log2, nl2[0]));
       fence();
     }
-    if ((CAUSAL && masked) || kill) mask_half(sc[0], 0, ka, kill);
-    // dP'_0 | P_1 = exp2(S'_1); second half of V read
+    if (masked || kill) mask_half(sc[0], 0, ka, kill);
+    // dP'_0 | P_1 = exp2(c S_1 - L2); second half of V read
     pc[0] = M::mma(ones, bd[0], zero16());
     fence();
 #pragma unroll
@@ -627,10 +635,11 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
       pc[0] = M::mma(vf[kk], of[0][kk], pc[0]);
       if (kk < KS / 2) vf[KS / 2 + kk] = plan.cols(B.v, r0, KS / 2 + kk);
 #pragma unroll
-      for (int e = 0; e < E; ++e) sc[1][kk * E + e] = fast_exp2(sc[1][kk * E + e]);
+      for (int e = 0; e < E; ++e)
+        sc[1][kk * E + e] = fast_exp2(__builtin_fmaf(sc[1][kk * E + e], scale_log2, nl2[1]));
       fence();
     }
-    if ((CAUSAL && masked) || kill) mask_half(sc[1], 1, ka, kill);
+    if (masked || kill) mask_half(sc[1], 1, ka, kill);
     // dP'_1 | dS_0 = P_0 o dP'_0, packed; first half of K^T read
     pc[1] = M::mma(ones, bd[1], zero16());
     fence();
@@ -687,7 +696,8 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
   // kt waits only for tile kt's copy and leaves tile kt + 1's in flight
   // (unless that one went by the register path, the ragged last tile, which
   // leaves nothing to count against).  Tiles from diag0 on apply the causal
-  // element mask.  kt is the walk position; tile_at(kt) the tile.
+  // element mask, and a ragged last tile masks its padded keys.  kt is the
+  // walk position; tile_at(kt) the tile.
   auto step = [&](int kt, const Buf& cur, Buf& ahead) ATTN_INLINE {
     const int t1 = !SPARSE ? kt + 1 : kt + 1 < ntiles ? tile_at(kt + 1) : 0;
     if (kt + 1 < ntiles && (t1 + 1) * BKV <= N) wait_async_fills_but<2 * FS::PER>();
@@ -699,7 +709,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
     const bool spread = kt + 2 < ntiles && k2 + BKV <= N;
     if (kt + 2 < ntiles && !spread) fill(ahead, t2);         // ragged: register path now
     const int t = tile_at(kt);
-    tile_body(t, cur, CAUSAL && t >= diag0, kill_at(kt),
+    tile_body(t, cur, (CAUSAL && t >= diag0) || (t + 1) * BKV > N, kill_at(kt),
               [&](int j) ATTN_INLINE { if (spread) copy_slot(ahead, k2, j); });
   };
   // Steps below the diagonal whose tile two ahead is whole need none of the

@@ -8,18 +8,20 @@
 // the row's normaliser of the scaled scores.
 //
 // Workgroup = 4 waves = 256 query rows of one (b, h); wave w owns query rows
-// qw + [0, 64) as two halves of 32.  Q (pre-multiplied by scale log2e) is the B
-// operand of S^T = K (c Q)^T and stays in AGPRs, so each lane owns one query
-// row of each half, and the O^T accumulators stay in AGPRs.  Each K and V
-// operand read from LDS feeds both halves.
+// qw + [0, 64) as two halves of 32.  Q is the B operand of S^T = K Q^T and
+// stays in AGPRs, so each lane owns one query row of each half, and the O^T
+// accumulators stay in AGPRs.  Each K and V operand read from LDS feeds both
+// halves.
 //
-// Online softmax in log2 units, kept per query: m (running max) and l (running
-// sum of exp2(s - m)).  m moves only when a row's new max exceeds it by more
-// than 8 (P stays below 2^8); the accumulators are then rescaled, which is
-// rare once the max has settled.
+// Online softmax in log2 units, kept per query: m (running max of c s, c =
+// scale log2 e) and l (running sum of exp2(c s - m)); the scale is applied in
+// float32 by the FMA that feeds each exp2, so the backward kernels rebuild
+// these scores to float32 rounding.  m moves only when a row's new max
+// exceeds it by more than 8 (P stays below 2^8); the accumulators are then
+// rescaled, which is rare once the max has settled.
 //
 // Per key sub-tile j of 32 rows, two chains of products:
-//   A: S_{j+1}^T = K (c Q)^T                | exps of S_j half 1, pack P_j,
+//   A: S_{j+1}^T = K Q^T                    | exps of S_j half 1, pack P_j,
 //                                             row sums of P_j
 //   B: O^T_c += V^T P_j^T (c = 0, 1)        | mask, row max, rescale decision
 //                                             and half-0 exps of S_{j+1}
@@ -111,11 +113,7 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_pipe_kernel(
   for (int c = 0; c < NH; ++c) {
     load_row_frags<bf16, D>(qf[c], Q + base, rs, qw + 32 * c + l32, N, d, h);
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qf[c][kk][e] = (bf16)((float)qf[c][kk][e] * scale_log2);
-      pin_agpr(qf[c][kk]);
-    }
+    for (int kk = 0; kk < KS; ++kk) pin_agpr(qf[c][kk]);
   }
   f32x16 acc[NH][MT];
 #pragma unroll
@@ -223,20 +221,21 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_pipe_kernel(
   auto needs_mask = [&](int ka, bool kill) ATTN_INLINE {
     return kill || (CAUSAL && ka + 31 > qw) || ka + 32 > N;
   };
-  // row max of s (raw scores, log2 units) per half
+  // row max of c s (log2 units) per half, taken on the raw scores (c > 0
+  // keeps their order)
   auto row_max = [&](const f32x16 (&s)[NH], float (&mx)[NH]) ATTN_INLINE {
 #pragma unroll
     for (int c = 0; c < NH; ++c) {
       float x = s[c][0];
 #pragma unroll
       for (int r = 1; r < 16; ++r) x = fmaxf(x, s[c][r]);
-      mx[c] = max_pair(x);
+      mx[c] = max_pair(x) * scale_log2;
     }
   };
-  // P = exp2(s - m) for elements [e0, e1) of half c
+  // P = exp2(c s - m) for elements [e0, e1) of half c
   auto exps = [&](f32x16 (&s)[NH], int c, int e0, int e1) ATTN_INLINE {
 #pragma unroll
-    for (int r = e0; r < e1; ++r) s[c][r] = fast_exp2(s[c][r] - m[c]);
+    for (int r = e0; r < e1; ++r) s[c][r] = fast_exp2(__builtin_fmaf(s[c][r], scale_log2, -m[c]));
   };
   auto pack_and_sum = [&](int c) ATTN_INLINE {
     bp[c][0] = M::pack(sc[c], 0);

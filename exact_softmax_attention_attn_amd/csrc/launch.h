@@ -72,6 +72,12 @@ inline int head_dim_bucket(int d) { return d <= 32 ? 32 : (d <= 64 ? 64 : (d <= 
 template <typename T, int D> constexpr int out_cols() {
   return sizeof(T) == 2 ? (D > 128 ? 128 : D) : (D > 64 ? 64 : D);
 }
+// The same split at run time: workgroups per block of the generic kernels for
+// head dim d and dtype (0 = f32, 1 = bf16); their grid's y extent is H times this.
+inline int column_parts(int d, int dtype) {
+  const int bucket = head_dim_bucket(d);
+  return dtype == 1 ? (bucket > 128 ? 2 : 1) : (bucket > 64 ? 2 : 1);
+}
 
 hipError_t launch_bwd_preprocess(const void* O, const void* dO, const float* L, float* ws, int B,
                                  int H, int N, int d, int dtype, hipStream_t stream);

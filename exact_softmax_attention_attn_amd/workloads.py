@@ -45,7 +45,7 @@ import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "get", "make_inputs", "make_random", "bf16_round",
            "MASK_BLOCK", "make_block_mask", "window_block_mask", "workload_mask",
-           "make_cotangents"]
+           "make_cotangents", "make_peaked", "make_shifted"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -198,3 +198,37 @@ def make_random(B: int, H: int, N: int, d: int, dtype: str, seed: int = 0,
     """Normal inputs of any shape (edge cases: ragged N, small d, N = 1, ...)."""
     w = Workload("random", B, H, N, d, 1.0 / math.sqrt(d), dtype, qkv_std=qkv_std)
     return make_inputs(w, seed)
+
+
+def make_peaked(B: int, H: int, N: int, d: int, dtype: str, seed: int = 0,
+                qkv_std: float = 2.0, growth: float = 3.0) -> dict:
+    """Sharply peaked softmax rows whose maximum keeps rising along the sequence.
+
+    Q, K, V ~ N(0, qkv_std^2) and dO ~ N(0, 1) as in ``make_inputs``; then key
+    row j is multiplied by 1 + growth * j / N, so later keys score higher and
+    a row's running maximum climbs as the walk reaches them.  Rounded like
+    the other inputs.
+    """
+    x = make_random(B, H, N, d, "f32", seed=seed, qkv_std=qkv_std)
+    ramp = (1.0 + growth * np.arange(N) / N)[None, :, None, None]
+    x["k"] = x["k"].astype(np.float64) * ramp
+    return {n: _cast(v, dtype) for n, v in x.items()}
+
+
+def make_shifted(B: int, H: int, N: int, d: int, dtype: str, seed: int = 0,
+                 q_shift: float = 1296.0, k_shift: float = 1.0, qkv_std: float = 0.5) -> dict:
+    """Inputs whose scores all sit far below zero by the same amount per row.
+
+    Normal inputs as in ``make_random``; then channel 0 of every query is set
+    to +q_shift and channel 0 of every key to -k_shift: the keys share a
+    component anti-aligned with every query, which lowers every score by
+    scale * q_shift * k_shift (a constant per row, to which the softmax is
+    blind) and leaves the rest of the scores as they were.  Both shifts must
+    be exactly representable in the device type.
+    """
+    assert _cast(np.array([q_shift, k_shift]), dtype).tolist() == [q_shift, k_shift]
+    x = make_random(B, H, N, d, "f32", seed=seed, qkv_std=qkv_std)
+    x["q"][..., 0] = q_shift
+    x["k"][..., 0] = -k_shift
+    return {n: _cast(v, dtype) for n, v in x.items()}
+

@@ -46,10 +46,12 @@
  *    outputs are untouched.  ATTN_ERR_HIP means a launch failed; the text of
  *    the HIP error is returned by attn_last_error() on the calling thread.
  *    Non-finite inputs are not checked; they propagate.
- *  - Limits.  B, H, N, d >= 1; d <= 128 (f32) or d <= 256 (bf16); d % 4 == 0
- *    (f32) or d % 8 == 0 (bf16); B*N*H*d and B*H*N must fit in int32 (ATTN_ERR_UNSUPPORTED
- *    otherwise); scale finite and > 0.  causal is 1 (keep j <= i) or 0 (keep
- *    every pair).
+ *  - Limits.  B, H, N, d >= 1 (ATTN_ERR_INVALID otherwise); d <= 128 (f32) or
+ *    d <= 256 (bf16); d % 4 == 0 (f32) or d % 8 == 0 (bf16); B, H <= 65535,
+ *    and H <= 32767 where the head's output columns split over two workgroups
+ *    (bf16 with d > 128, f32 with d > 64); B*H*N < 2^31, so B*N*H*d < 2^39
+ *    (ATTN_ERR_UNSUPPORTED otherwise); scale finite and > 0.  causal is 1
+ *    (keep j <= i) or 0 (keep every pair).
  */
 #ifndef ATTN_H_
 #define ATTN_H_
@@ -181,8 +183,11 @@ int attn_bwd_dq_masked(const void* Q, const void* K, const void* V, const void* 
  * Backward of the backward.  The first backward maps (Q, K, V, dO) to
  * (dQ, dK, dV); given cotangents gQ, gK, gV of its outputs, this returns the
  * gradients of  l2 = <gQ, dQ> + <gK, dK> + <gV, dV>  with respect to Q, K, V
- * and dO (exact differentiation through the backward pass, as in the FlashBoB
- * paper's abstract: two row-wise scalars fix every output).  With P, dP, D
+ * and dO: the exact gradient of the backward pass, whose goal (no N x N array
+ * in memory, a pair of per-row quantities beyond the recomputed tiles) is set
+ * by the page "Approaching I/O-optimality for Approximate Attention", its
+ * first abstract (FlashBoB); the formulas are derived from the chain rule.
+ * With P, dP, D
  * and dS as in attn_bwd, G = scale (gQ K^T + Q gK^T), A = dO gV^T,
  *   r_i = sum_j P_ij G_ij,   E_i = sum_j (P_ij A_ij + dS_ij G_ij),
  *   W = P o (G - r),         dS2 = P o (A + (dP - D) o (G - r) - E),

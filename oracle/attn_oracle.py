@@ -68,9 +68,7 @@ __all__ = [
     "attn_bwd",
     "attn_bwd_sampled",
     "literal_backward_head",
-    "loss_value",
     "pair_count",
-    "bwd_flops",
     "head_bwd_bwd",
     "attn_bwd_bwd",
     "attn_bwd_bwd_sampled",
@@ -196,14 +194,15 @@ def head_backward(q, k, v, do, scale: float, causal: bool, block_mask=None,
                   mask_block: int = MASK_BLOCK):
     """Exact gradient of sum(dO o O) for one (batch, head), every table materialised.
 
-    Returns dQ, dK, dV [N, d], D [N], dS row sums [N], P [N, N].
+    Returns dQ, dK, dV [N, d], D [N], dS row sums [N], P [N, N], and the
+    forward's O [N, d] and L [N] (``head_forward``'s, computed on the way).
     """
-    _, _, p = head_forward(q, k, v, scale, causal, block_mask, mask_block)
+    o, lse, p = head_forward(q, k, v, scale, causal, block_mask, mask_block)
     dv = p.T @ do                      # p @ v transposed against the output cotangent
     dp = do @ v.T                      # dP = dO V^T (issue #243, item 2)
     ds, d = softmax_backward(p, dp)
     dq, dk = grad_q_k(ds, q, k, scale)
-    return dq, dk, dv, d, ds.sum(axis=1), p
+    return dq, dk, dv, d, ds.sum(axis=1), p, o, lse
 
 
 def literal_backward_head(q, k, v, do, scale: float, causal: bool):
@@ -267,22 +266,26 @@ def attn_fwd(Q, K, V, scale: float, causal: bool = True, block_mask=None,
 
 def attn_bwd(Q, K, V, dO, scale: float, causal: bool = True, block_mask=None,
              mask_block: int = MASK_BLOCK):
-    """dQ, dK, dV [B, N, H, d] plus diagnostics D and dS row sums [B, H, N]."""
+    """dQ, dK, dV [B, N, H, d] plus diagnostics D and dS row sums [B, H, N], and
+    the forward's O [B, N, H, d] and L [B, H, N] (the same values as ``attn_fwd``)."""
     Q, K, V, dO = _f64(Q), _f64(K), _f64(V), _f64(dO)
     B, N, H, _ = Q.shape
     dQ = np.empty_like(Q)
     dK = np.empty_like(K)
     dV = np.empty_like(V)
+    O = np.empty_like(V)
+    L = np.empty((B, H, N))
     D = np.empty((B, H, N))
     ds_rows = np.empty((B, H, N))
     for b in range(B):
         for h in range(H):
-            dq, dk, dv, d, dsr, _ = head_backward(
+            dq, dk, dv, d, dsr, _, o, lse = head_backward(
                 Q[b, :, h], K[b, :, h], V[b, :, h], dO[b, :, h], scale, causal,
                 _head_mask(block_mask, b, h), mask_block)
             dQ[b, :, h], dK[b, :, h], dV[b, :, h] = dq, dk, dv
+            O[b, :, h], L[b, h] = o, lse
             D[b, h], ds_rows[b, h] = d, dsr
-    return {"dQ": dQ, "dK": dK, "dV": dV, "D": D, "dS_rowsum": ds_rows}
+    return {"dQ": dQ, "dK": dK, "dV": dV, "D": D, "dS_rowsum": ds_rows, "O": O, "L": L}
 
 
 def attn_bwd_sampled(Q, K, V, dO, scale: float, causal: bool, b: int, h: int,
@@ -363,9 +366,10 @@ def attn_bwd_sampled(Q, K, V, dO, scale: float, causal: bool, b: int, h: int,
 
 
 # --------------------------------------------------------------------------
-# Backward of the backward ("FlashBoB", abstract: exact differentiation
-# through the backward pass; two row-wise scalars determine all outputs
-# through affine transformations).  Given cotangents gQ, gK, gV of the
+# Backward of the backward (the page "Approaching I/O-optimality for
+# Approximate Attention", first abstract, FlashBoB: the exact gradient of the
+# backward pass, for which a pair of per-row quantities suffices beyond the
+# recomputed scores).  Given cotangents gQ, gK, gV of the
 # backward's outputs dQ, dK, dV, return the gradients of
 #     l2 = <gQ, dQ> + <gK, dK> + <gV, dV>
 # with respect to Q, K, V and dO.  Written out from the chain rule:
@@ -486,14 +490,8 @@ def attn_bwd_bwd_sampled(Q, K, V, dO, gQ, gK, gV, scale: float, causal: bool, b:
 
 
 # --------------------------------------------------------------------------
-# Scalars used by pins and by the FLOP accounting
+# Pair count (pinned against the score-table row counts the pages print)
 # --------------------------------------------------------------------------
-
-def loss_value(Q, K, V, dO, scale: float, causal: bool = True) -> float:
-    """l = sum(dO o O): the scalar whose gradient attn_bwd returns."""
-    O, _ = attn_fwd(Q, K, V, scale, causal)
-    return float((_f64(dO) * O).sum())
-
 
 def pair_count(B: int, H: int, N: int, causal: bool = True) -> int:
     """Number of kept (i, j) pairs: B*H*N(N+1)/2 causal (diagonal kept), else B*H*N^2.
@@ -505,11 +503,3 @@ def pair_count(B: int, H: int, N: int, causal: bool = True) -> int:
         return 0
     keep = causal_keep(N, N) if causal else np.ones((N, N), dtype=bool)
     return int(B * H * int(keep.sum()))
-
-
-def bwd_flops(B: int, H: int, N: int, d: int, causal: bool = True) -> int:
-    """Metric FLOPs of the backward: five contractions x 2d FLOP x kept pairs.
-
-    The five are S = QK^T, dP = dO V^T, dV = P^T dO, dQ = dS K, dK = dS^T Q.
-    """
-    return 10 * d * pair_count(B, H, N, causal)

@@ -123,6 +123,17 @@ def test_validation_rejects_bad_arguments_without_launching(lib):
                {"dtype": -1}, {"B": 70000}, {"H": 70000}, {"B": 65535, "H": 65535, "N": 1024}):
         assert _fwd(lib, f5, **kw) == 2, kw
         assert _bwd(lib, b10, **kw) == 2, kw
+    # wide heads split their output columns over two workgroups per block
+    # along the grid's y axis (bf16 d > 128, f32 d > 64): H * 2 must fit 65535
+    for kw in ({"H": 32768, "d": 256, "dtype": 1}, {"H": 40000, "d": 136, "dtype": 1},
+               {"H": 32768, "d": 128}, {"H": 32768, "d": 68}):
+        assert _fwd(lib, f5, **kw) == 2, kw
+        assert _bwd(lib, b10, **kw) == 2, kw
+        assert lib.attn_bwd_dkdv(*([FAKE] * 7), 1, kw["H"], 8, kw["d"], 1, 0.5,
+                                 kw.get("dtype", 0), NUL) == 2, kw
+    # row count B*H*N < 2^31 (so B*N*H*d < 2^39 with d <= 256)
+    assert _bwd(lib, b10, B=65535, H=16, N=2049, d=8) == 2      # 2^31 + 917,488 rows
+    assert _fwd(lib, f5, B=8192, H=16, N=16384, d=256, dtype=1) == 2   # exactly 2^31 rows
     # the stage entry points validate the same way
     assert lib.attn_bwd_preprocess(FAKE, NUL, FAKE, FAKE, 1, 1, 8, 8, 0, NUL) == 1
     assert lib.attn_bwd_preprocess(FAKE, FAKE, NUL, FAKE, 1, 1, 8, 8, 0, NUL) == 1

@@ -1,9 +1,10 @@
 """Backward of the backward: HIP path vs the fp64 oracle through the C ABI.
 
 Relative Frobenius error per output tensor (hQ, hK, hV, hdO) and for the two
-row scalars r and E the kernels leave in the workspace.  Two feeds of O and L
-as in the first backward's tests: the library's own forward, and the
-oracle's O and L cast to the device type.
+row scalars r and E the kernels leave in the workspace, gated per tensor, per
+(b, h) and per row as in the first backward's tests (``tests/gpu_check.py``).
+Two feeds of O and L: the library's own forward, and the oracle's O and L
+cast to the device type.
 """
 
 import math
@@ -14,10 +15,11 @@ import pytest
 
 from exact_softmax_attention_attn_amd import workloads
 from oracle import attn_oracle as orc
+from tests import gpu_check
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"f32": 1e-5, "bf16": 2e-2}
+TOL = gpu_check.TOL
 
 
 def _say(msg):
@@ -45,10 +47,6 @@ def _host(t):
     return t.float().cpu().numpy().astype(np.float64)
 
 
-def rel_fro(got, ref):
-    return float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30))
-
-
 CASES = [
     # B, H, N, d, dtype, causal
     (3, 2, 8, 4, "f32", True),
@@ -61,13 +59,36 @@ CASES = [
 ]
 
 
+# every score of a row lowered by scale * q_shift > 100 (L < -88; keys share
+# channel 0 = -1, queries have channel 0 = q_shift), ragged N: the padded keys
+# of the last tile must not reach the products
+SHIFTED = [
+    (1, 2, 1000, 64, "f32", False, 900.0),
+    (1, 2, 1000, 128, "bf16", False, 1296.0),
+    (1, 1, 1000, 128, "bf16", True, 1296.0),
+]
+
+
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "x".join(map(str, c)))
 def test_bwd_bwd_parity(B, case):
+    Bn, H, N, d, dtype, causal = case
+    x = workloads.make_random(Bn, H, N, d, dtype, seed=N + d,
+                              qkv_std=0.5 if dtype == "bf16" else 1.0)
+    _bob_case(B, x, case)
+
+
+@pytest.mark.parametrize("case", SHIFTED, ids=lambda c: "x".join(map(str, c)))
+def test_bwd_bwd_parity_shifted_scores(B, case):
+    from tests.test_gpu_parity import shifted_tol
+    Bn, H, N, d, dtype, causal, q_shift = case
+    x = workloads.make_shifted(Bn, H, N, d, dtype, seed=5 + d, q_shift=q_shift, k_shift=1.0)
+    _bob_case(B, x, case[:6], tol=shifted_tol(dtype, 1.0 / math.sqrt(d), q_shift, 1.0))
+
+
+def _bob_case(B, x, case, tol=None):
     import torch
     Bn, H, N, d, dtype, causal = case
     scale = 1.0 / math.sqrt(d)
-    x = workloads.make_random(Bn, H, N, d, dtype, seed=N + d,
-                              qkv_std=0.5 if dtype == "bf16" else 1.0)
     x.update(workloads.make_cotangents(Bn, H, N, d, dtype, seed=N))
     xs = {n: x[n].astype(np.float64) for n in x}
     O, L = orc.attn_fwd(xs["q"], xs["k"], xs["v"], scale, causal)
@@ -86,11 +107,10 @@ def test_bwd_bwd_parity(B, case):
                                          t["gk"], t["gv"], causal=causal, scale=scale,
                                          workspace=ws)
         torch.cuda.synchronize()
-        errs = {"hQ": rel_fro(_host(hq), ref["hQ"]), "hK": rel_fro(_host(hk), ref["hK"]),
-                "hV": rel_fro(_host(hv), ref["hV"]), "hdO": rel_fro(_host(hdo), ref["hdO"]),
-                "r": rel_fro(_host(ws[2]), ref["r"]), "E": rel_fro(_host(ws[3]), ref["E"])}
-        assert all(np.isfinite(v) for v in errs.values()), (case, feed, errs)
-        assert max(errs.values()) <= TOL[dtype], (case, feed, errs)
+        got = {"hQ": _host(hq), "hK": _host(hk), "hV": _host(hv), "hdO": _host(hdo),
+               "r": _host(ws[2]), "E": _host(ws[3])}
+        gpu_check.check(f"bob {case} feed={feed}", got, ref, dtype,
+                        names=("hQ", "hK", "hV", "hdO", "r", "E"), tol=tol)
 
 
 def test_c5_bob_full_size_sampled_against_oracle(B):
@@ -115,10 +135,12 @@ def test_c5_bob_full_size_sampled_against_oracle(B):
         _say(f"c5_bob oracle sample head {h}")
         s = orc.attn_bwd_bwd_sampled(x["q"], x["k"], x["v"], x["do"], x["gq"], x["gk"], x["gv"],
                                      w.scale, True, 0, h, rows, cols, row_block=1024)
-        errs = {"hQ": rel_fro(_host(hq[0, rows, h]), s["hQ"]),
-                "hdO": rel_fro(_host(hdo[0, rows, h]), s["hdO"]),
-                "hK": rel_fro(_host(hk[0, cols, h]), s["hK"]),
-                "hV": rel_fro(_host(hv[0, cols, h]), s["hV"]),
-                "r": rel_fro(_host(ws[2, 0, h]), s["r"]), "E": rel_fro(_host(ws[3, 0, h]), s["E"])}
-        print("c5_bob sampled errors", h, errs, flush=True)
-        assert max(errs.values()) <= TOL["bf16"], (h, errs)
+        got = {"hQ": _host(hq[0, rows, h]), "hdO": _host(hdo[0, rows, h]),
+               "hK": _host(hk[0, cols, h]), "hV": _host(hv[0, cols, h])}
+        # sampled rows as one (b, h) slice [1, rows, 1, d]; r and E [1, 1, N]
+        g = {n: v[None, :, None, :] for n, v in got.items()}
+        r = {n: s[n][None, :, None, :] for n in got}
+        for n, i in (("r", 2), ("E", 3)):
+            g[n], r[n] = _host(ws[i, 0, h])[None, None, :], s[n][None, None, :]
+        gpu_check.check(f"c5_bob sampled head {h}", g, r, "bf16",
+                        names=("hQ", "hK", "hV", "hdO", "r", "E"))

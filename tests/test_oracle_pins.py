@@ -145,7 +145,7 @@ def test_ds_rows_sum_to_zero_and_max_shift_gradient_cancels(causal):
     for b in range(2):
         for h in range(3):
             q, k, v, do = (x[n][b, :, h] for n in ("q", "k", "v", "do"))
-            _, _, _, _, _, p = orc.head_backward(q, k, v, do, scale, causal)
+            _, _, _, _, _, p, _, _ = orc.head_backward(q, k, v, do, scale, causal)
             dp = do @ v.T
             ds, _ = orc.softmax_backward(p, dp)
             bound = 1e-12 * np.abs(ds).sum(axis=1) + 1e-300
@@ -299,3 +299,19 @@ def test_sampled_evaluator_equals_full_oracle(causal):
     np.testing.assert_allclose(s["dV"], g["dV"][1, cols, 0], rtol=1e-11, atol=1e-13)
     np.testing.assert_allclose(s["L"], L[1, 0], rtol=1e-13, atol=1e-13)
     np.testing.assert_allclose(s["D"], g["D"][1, 0], rtol=1e-11, atol=1e-13)
+
+
+# ---------------------------------------------------------------- forward outputs of attn_bwd
+
+def test_attn_bwd_reports_the_forward_outputs_of_attn_fwd():
+    # attn_bwd hands back O and L as computed on its way to the gradient; they
+    # must be attn_fwd's values bit for bit (attn_fwd is pinned above by
+    # scipy's logsumexp, closed forms and torch), causal and full, with a
+    # block mask too.
+    x = _rand(2, 3, 150, 16, seed=11)
+    bm = workloads.make_block_mask(150, 0.6, seed=3, keep_diagonal=False, empty_rows=(1,))
+    for causal, mask in ((True, None), (False, None), (True, bm)):
+        O, L = orc.attn_fwd(x["q"], x["k"], x["v"], 0.25, causal, mask)
+        g = orc.attn_bwd(x["q"], x["k"], x["v"], x["do"], 0.25, causal, mask)
+        np.testing.assert_array_equal(g["O"], O)
+        np.testing.assert_array_equal(g["L"], L)
