@@ -40,6 +40,7 @@ _SIGNATURES = {
                                   _I, _I, _I, _I, _I, _F, _I, _P]),
     "attn_bwd_dq_masked": (_I, [_P, _P, _P, _P, _P, _P, _P, _I,
                                 _I, _I, _I, _I, _I, _F, _I, _P]),
+    "attn_bwd_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
     "attn_bwd_bwd_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "attn_bwd_bwd": (_I, [_P] * 14 + [_I, _I, _I, _I, _I, _F, _I, _P]),
     "attn_status_string": (ctypes.c_char_p, [_I]),
@@ -175,6 +176,21 @@ def attn_bwd(q, k, v, o, do, lse, causal: bool = True, scale: float | None = Non
     with torch.cuda.device(q.device):
         _call("attn_bwd", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
               _ptr(dk), _ptr(dv), _ptr(workspace), B, H, N, d, int(bool(causal)), scale,
+              _dtype_code(q), _stream(q.device))
+    return dq, dk, dv
+
+
+def attn_bwd_noalloc(q, k, v, o, do, lse, dq, dk, dv, causal: bool = True,
+                     scale: float | None = None):
+    """attn_bwd with the library's static per-GPU workspace (the C call
+    allocates nothing; outputs are the caller's): dQ, dK, dV."""
+    _check_bnhd(q, k, v, o, do, dq, dk, dv)
+    B, N, H, d = q.shape
+    _check_rows(lse, B, H, N, q.device)
+    scale = default_scale(d) if scale is None else float(scale)
+    with torch.cuda.device(q.device):
+        _call("attn_bwd_noalloc", _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse),
+              _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, int(bool(causal)), scale,
               _dtype_code(q), _stream(q.device))
     return dq, dk, dv
 

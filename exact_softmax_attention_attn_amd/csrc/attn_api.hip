@@ -2,7 +2,9 @@
 // check passes), dispatch to the kernel launchers, status reporting.
 #include <initializer_list>
 #include <math.h>
+#include <mutex>
 #include <stdint.h>
+#include <stdio.h>
 #include <string.h>
 
 #include "attn.h"
@@ -12,10 +14,52 @@ namespace {
 
 thread_local char g_last_error[256] = "";
 
+void set_error_text(const char* s) {
+  strncpy(g_last_error, s, sizeof(g_last_error) - 1);
+  g_last_error[sizeof(g_last_error) - 1] = '\0';
+}
+
 void set_hip_error(hipError_t e) {
   const char* s = hipGetErrorString(e);
-  strncpy(g_last_error, s ? s : "unknown HIP error", sizeof(g_last_error) - 1);
-  g_last_error[sizeof(g_last_error) - 1] = '\0';
+  set_error_text(s ? s : "unknown HIP error");
+}
+
+// Workspace of attn_bwd_noalloc: one array per GPU, in the library's own
+// device memory, held until the process ends.  Host code never uses the
+// array's name as an address: each device's address comes from
+// hipGetSymbolAddress (looked up once per device, with that device current)
+// and is what the kernels receive.
+constexpr size_t kScratchBytes = ATTN_NOALLOC_MAX_BYTES;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of the array (its address looked up on the
+// device's first call).
+int current_device_scratch(float** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    set_hip_error(e);
+    return ATTN_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    set_error_text("attn_bwd_noalloc: device index beyond the 64 the library tracks");
+    return ATTN_ERR_UNSUPPORTED;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) {
+      set_hip_error(e);
+      return ATTN_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = static_cast<float*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return ATTN_OK;
 }
 
 int finish(hipError_t e) {
@@ -160,6 +204,24 @@ int attn_bwd_dq(const void* Q, const void* K, const void* V, const void* dO,
   return finish(attn::launch_bwd_dq(a, static_cast<hipStream_t>(stream)));
 }
 
+}  // extern "C"
+
+namespace {
+// The three stages of attn_bwd on a validated call, with workspace ws.
+int run_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+            const float* L, void* dQ, void* dK, void* dV, float* ws, int B, int H, int N, int d,
+            int causal, float scale, int dtype, hipStream_t s) {
+  hipError_t e = attn::launch_bwd_preprocess(O, dO, L, ws, B, H, N, d, dtype, s);
+  if (e != hipSuccess) return finish(e);
+  const attn::BwdArgs a = make_bwd(Q, K, V, dO, ws, dQ, dK, dV, B, H, N, d, causal, scale, dtype);
+  e = attn::launch_bwd_dkdv(a, s);
+  if (e != hipSuccess) return finish(e);
+  return finish(attn::launch_bwd_dq(a, s));
+}
+}  // namespace
+
+extern "C" {
+
 int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
              const float* L, void* dQ, void* dK, void* dV, void* workspace, int B, int H, int N,
              int d, int causal, float scale, int dtype, void* stream) {
@@ -167,15 +229,31 @@ int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const v
   ATTN_TRY(check_sizes(B, H, N, d));
   ATTN_TRY(check_scale_causal(scale, causal));
   ATTN_TRY(check_dtype_dim(H, d, dtype));
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = attn::launch_bwd_preprocess(O, dO, L, static_cast<float*>(workspace), B, H, N,
-                                             d, dtype, s);
-  if (e != hipSuccess) return finish(e);
-  const attn::BwdArgs a =
-      make_bwd(Q, K, V, dO, workspace, dQ, dK, dV, B, H, N, d, causal, scale, dtype);
-  e = attn::launch_bwd_dkdv(a, s);
-  if (e != hipSuccess) return finish(e);
-  return finish(attn::launch_bwd_dq(a, s));
+  return run_bwd(Q, K, V, O, dO, L, dQ, dK, dV, static_cast<float*>(workspace), B, H, N, d,
+                 causal, scale, dtype, static_cast<hipStream_t>(stream));
+}
+
+int attn_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                     const float* L, void* dQ, void* dK, void* dV, int B, int H, int N, int d,
+                     int causal, float scale, int dtype, void* stream) {
+  ATTN_TRY(check_ptrs({Q, K, V, O, dO, L, dQ, dK, dV}));
+  ATTN_TRY(check_sizes(B, H, N, d));
+  ATTN_TRY(check_scale_causal(scale, causal));
+  ATTN_TRY(check_dtype_dim(H, d, dtype));
+  const size_t need = 2 * (size_t)B * (size_t)H * (size_t)N * sizeof(float);
+  if (need > kScratchBytes) {
+    char msg[160];
+    snprintf(msg, sizeof(msg),
+             "attn_bwd_noalloc: workspace of %zu bytes (2*B*H*N floats) exceeds the static "
+             "%zu-byte array; call attn_bwd with a workspace instead",
+             need, kScratchBytes);
+    set_error_text(msg);
+    return ATTN_ERR_UNSUPPORTED;
+  }
+  float* ws = nullptr;
+  ATTN_TRY(current_device_scratch(&ws));
+  return run_bwd(Q, K, V, O, dO, L, dQ, dK, dV, ws, B, H, N, d, causal, scale, dtype,
+                 static_cast<hipStream_t>(stream));
 }
 
 int attn_bwd_masked(const void* Q, const void* K, const void* V, const void* O, const void* dO,

@@ -36,11 +36,13 @@
  *    even) before they enter a product; outputs are rounded to bf16.
  *  - Pointers are device pointers (or host-coherent pointers the GPU can
  *    read), aligned to 16 bytes.  The caller owns every buffer; the library
- *    allocates nothing, frees nothing and keeps no pointer after returning.
+ *    allocates nothing, frees nothing and keeps no pointer after returning
+ *    (attn_bwd_noalloc's workspace is a static array of the library's own).
  *  - Outputs must not alias inputs or each other; they are overwritten.
  *  - stream is a hipStream_t (NULL = the null stream).  Calls only enqueue
  *    work and return; results are visible after the stream is synchronised.
- *    There is no global mutable state, so calls are thread-safe.
+ *    Apart from attn_bwd_noalloc's per-GPU workspace array, there is no
+ *    global mutable state, so calls are thread-safe.
  *  - Errors.  The return value is an attn_status_t.  On ATTN_ERR_INVALID or
  *    ATTN_ERR_UNSUPPORTED nothing was enqueued, no HIP call was made, and the
  *    outputs are untouched.  ATTN_ERR_HIP means a launch failed; the text of
@@ -103,6 +105,31 @@ size_t attn_bwd_workspace_bytes(int B, int H, int N, int d);
 int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
              const float* L, void* dQ, void* dK, void* dV, void* workspace,
              int B, int H, int N, int d, int causal, float scale, int dtype, void* stream);
+
+/*
+ * attn_bwd for callers that cannot allocate device memory -- code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc: the
+ * same three stages and kernels, with the workspace taken from an array the
+ * library holds in each GPU's memory (ATTN_NOALLOC_MAX_BYTES per GPU, from
+ * the first call on that GPU until the process ends) instead of an argument.
+ * The call allocates nothing.
+ *   in, out: as attn_bwd; results are bitwise those of attn_bwd.
+ *   Limit: the workspace attn_bwd would need, 2*B*H*N*sizeof(float), must not
+ *   exceed ATTN_NOALLOC_MAX_BYTES (B*H*N <= 2,097,152 rows); larger calls
+ *   return ATTN_ERR_UNSUPPORTED before any HIP call, with the reason in
+ *   attn_last_error().
+ *   Sharing: every call on one GPU uses that GPU's one array, which keeps the
+ *   last call's contents (nothing in it needs clearing: the first stage
+ *   overwrites all it later reads).  Calls that overlap on one GPU -- on
+ *   different streams, or from different threads without ordering -- race on
+ *   it; calls on different GPUs do not.  The current device must be the one
+ *   the pointers and the stream belong to.
+ */
+#define ATTN_NOALLOC_MAX_BYTES ((size_t)16 << 20)
+int attn_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                     const float* L, void* dQ, void* dK, void* dV,
+                     int B, int H, int N, int d, int causal, float scale, int dtype,
+                     void* stream);
 
 /*
  * Stage 1 of attn_bwd: D_i = sum_c dO_ic O_ic in float32 (the softmax-weighted
@@ -212,7 +239,8 @@ int attn_bwd_bwd(const void* Q, const void* K, const void* V, const void* O, con
 /* Static text for a status code ("ok", "invalid argument", ...). */
 const char* attn_status_string(int status);
 
-/* Text of the last ATTN_ERR_HIP on the calling thread ("" if none). */
+/* Text of the last ATTN_ERR_HIP on the calling thread, or of the last size
+ * rejection by attn_bwd_noalloc ("" if none). */
 const char* attn_last_error(void);
 
 #ifdef __cplusplus

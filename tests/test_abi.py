@@ -33,8 +33,8 @@ def test_header_declares_the_entry_points():
     assert _declared() == sorted([
         "attn_bwd", "attn_bwd_bwd", "attn_bwd_bwd_workspace_bytes", "attn_bwd_dkdv",
         "attn_bwd_dkdv_masked", "attn_bwd_dq", "attn_bwd_dq_masked", "attn_bwd_masked",
-        "attn_bwd_preprocess", "attn_bwd_workspace_bytes", "attn_fwd_lse", "attn_fwd_lse_masked",
-        "attn_last_error", "attn_status_string"])
+        "attn_bwd_noalloc", "attn_bwd_preprocess", "attn_bwd_workspace_bytes", "attn_fwd_lse",
+        "attn_fwd_lse_masked", "attn_last_error", "attn_status_string"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -213,3 +213,24 @@ def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
     monkeypatch.setattr(binding, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         binding.load(str(tmp_path / "libattn.so"))
+
+
+def test_noalloc_entry_point_validates_before_any_hip_call(lib):
+    p9 = [FAKE] * 9
+
+    def call(ptrs=p9, B=1, H=1, N=8, d=8, causal=1, scale=0.5, dtype=0):
+        return lib.attn_bwd_noalloc(*ptrs, B, H, N, d, causal, scale, dtype, NUL)
+
+    for i in range(9):
+        p = list(p9); p[i] = NUL
+        assert call(p) == 1
+        p[i] = MIS
+        assert call(p) == 1
+    assert call(N=0) == 1 and call(scale=0.0) == 1 and call(causal=2) == 1
+    assert call(d=136) == 2 and call(dtype=3) == 2
+    assert lib.attn_last_error() == b""
+    # the static workspace holds 2 * 2,097,152 floats: one row more is refused
+    assert call(B=1, H=1, N=2097153) == 2
+    assert b"exceeds" in lib.attn_last_error()
+    assert call(B=2, H=16, N=65537) == 2
+    # (last in this file: it leaves attn_last_error() set on this thread)
