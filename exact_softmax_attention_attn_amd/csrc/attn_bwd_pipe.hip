@@ -229,9 +229,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     const int qa = t * BQ;                       // first query row of the tile
     constexpr int E = 8 / L;                     // exps per product (half a sub-tile per chain)
     constexpr int M2 = 16 / L;                   // dS multiplies per product
+    // before product n of an even position, wait for operands n and n + 1
+    auto pair_wait = [&](int n) ATTN_INLINE {
+      if (n % 2 == 0) need_both(ring[n % AH], ring[(n + 1) % AH]);
+    };
     auto s_chain = [&](int c, f32x16& acc) ATTN_INLINE {
 #pragma unroll
       for (int i = 0; i < L; ++i) {
+        pair_wait(c * L + i);
         acc = M::mma(ring[(c * L + i) % AH], kf[i], acc);
         refill(c * L + i);
         slot(c, i);
@@ -245,6 +250,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     if constexpr (HP) {
 #pragma unroll
       for (int i = 0; i < L; ++i) {
+        pair_wait(C_DVP * L + i);
         mma_acc_agpr(dv_acc[i % MT], ring[(C_DVP * L + i) % AH], bpp[i / MT]);
         refill(C_DVP * L + i);
         slot(C_DVP, i);
@@ -258,6 +264,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < L; ++i) {
       if constexpr (HP) {
+        pair_wait(C_DKP * L + i);
         mma_acc_agpr(dk_acc[i % MT], ring[(C_DKP * L + i) % AH], bdsp[i / MT]);
         refill(C_DKP * L + i);
         slot(C_DKP, i);
@@ -270,6 +277,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     const f32x16 lb = row_scalars(B.l, 32);      // -L2 of S_b's rows
 #pragma unroll
     for (int i = 0; i < L; ++i) {
+      pair_wait(C_DPA * L + i);
       pa = M::mma(ring[(C_DPA * L + i) % AH], vf[i], pa);
       refill(C_DPA * L + i);
       slot(C_DPA, i);
@@ -286,6 +294,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     f32x16 sb = zero16();
 #pragma unroll
     for (int i = 0; i < L; ++i) {
+      pair_wait(C_SB * L + i);
       sb = M::mma(ring[(C_SB * L + i) % AH], kf[i], sb);
       refill(C_SB * L + i);
       slot(C_SB, i);
@@ -301,6 +310,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     // dV_a | exps of S_b, first half
 #pragma unroll
     for (int i = 0; i < L; ++i) {
+      pair_wait(C_DVA * L + i);
       mma_acc_agpr(dv_acc[i % MT], ring[(C_DVA * L + i) % AH], bpa[i / MT]);
       refill(C_DVA * L + i);
       slot(C_DVA, i);
@@ -311,6 +321,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     // dP_b | exps of S_b, second half
 #pragma unroll
     for (int i = 0; i < L; ++i) {
+      pair_wait(C_DPB * L + i);
       pb = M::mma(ring[(C_DPB * L + i) % AH], vf[i], pb);
       refill(C_DPB * L + i);
       slot(C_DPB, i);
@@ -327,6 +338,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     // dK_a | dS_b = P_b o dP'_b
 #pragma unroll
     for (int i = 0; i < L; ++i) {
+      pair_wait(C_DKA * L + i);
       mma_acc_agpr(dk_acc[i % MT], ring[(C_DKA * L + i) % AH], bdsa[i / MT]);
       refill(C_DKA * L + i);
       slot(C_DKA, i);

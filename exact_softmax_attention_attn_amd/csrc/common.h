@@ -70,6 +70,13 @@ template <typename V> __device__ __forceinline__ void pin_operand(V& x) {
   asm volatile("" : "+v"(x));
 }
 
+// Wait for two operand fragments at once: an empty statement that reads both
+// makes the compiler's wait before it cover the pair, so the second of two
+// back-to-back products needs no wait of its own.
+template <typename V> __device__ __forceinline__ void need_both(const V& a, const V& b) {
+  asm volatile("" : : "v"(a), "v"(b));
+}
+
 // A value every lane of the wave agrees on, moved to a scalar register (so
 // addresses built from it stay scalar).
 __device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
@@ -421,23 +428,22 @@ __device__ __forceinline__ void async_fill(const Tile<bf16, ROWS, D>& t, const b
 // cannot tell which LDS buffer a tracked copy writes and would drain every
 // copy before the next LDS read; it does not see these, so their users wait
 // explicitly (wait_async_fills*) before reading what they wrote.  M0 (the
-// LDS destination) is saved and restored around each copy.
+// LDS destination) is declared clobbered, so the compiler keeps nothing in it
+// across a copy and no save and restore is needed.
 __device__ __forceinline__ unsigned lds_address(const void* p) {
   return (unsigned)(unsigned long)((lds_void*)p);
 }
 __device__ __forceinline__ void lds_dma_b128(const void* sbase, unsigned voff, unsigned lds) {
-  unsigned saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\ts_nop 0\n\ts_mov_b32 m0, %0"
-      : "=&s"(saved) : "v"(voff), "s"(sbase), "s"(lds) : "memory");
+      "s_mov_b32 m0, %2\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      : : "v"(voff), "s"(sbase), "s"(lds) : "memory", "m0");
 }
 __device__ __forceinline__ void lds_dma_b32(const void* sbase, unsigned voff, unsigned lds) {
-  unsigned saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
-      "global_load_lds_dword %1, %2\n\ts_nop 0\n\ts_mov_b32 m0, %0"
-      : "=&s"(saved) : "v"(voff), "s"(sbase), "s"(lds) : "memory");
+      "s_mov_b32 m0, %2\n\ts_nop 0\n\t"
+      "global_load_lds_dword %0, %1"
+      : : "v"(voff), "s"(sbase), "s"(lds) : "memory", "m0");
 }
 
 // Copy instruction i of the plan (assembly form); tile_base wave-uniform.
