@@ -15,7 +15,9 @@ fp64 oracle on whole (batch, head) slices of the same workload on the host
 cores (a bounded sample of about CPU_BASELINE_SECONDS).
 
 Other workloads (--workload) time other steps the same way: the backward of
-the backward (op "bob", 44 * d FLOPs per kept pair, its one call as the
+the backward (op "bob", 24 * d algorithmic FLOPs per kept pair: S, dP, G as
+two, A, then hQ, hK and hdO as two each and hV; the 44 * d its three passes
+execute, recomputation included, is reported beside it; its one call as the
 roofline) and the forward alone (op "fwd", 4 * d per kept pair: S and P V,
 its one kernel as the roofline, the oracle's forward as the CPU baseline).
 
@@ -117,7 +119,7 @@ def cpu_baseline(w, x, bm=None, cot=None, op="bwd"):
         done += 1
         if spent >= CPU_BASELINE_SECONDS:
             break
-    per = 4 if op == "fwd" else (10 if cot is None else 44)
+    per = 4 if op == "fwd" else (10 if cot is None else 24)
     fn = "attn_fwd" if op == "fwd" else ("attn_bwd" if cot is None else "attn_bwd_bwd")
     flops = per * w.d * pairs(1, 1, w.N, w.causal, bm) * done
     return {"value": round(flops / spent / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
@@ -327,11 +329,12 @@ def main(argv=None):
     dqk = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
     ms = wall / args.steps * 1e3
     P = pairs(w.B, w.H, w.N, w.causal, bm)
-    # FLOPs per kept pair: the backward's five contractions (10 d); the
-    # backward of the backward's 22 products of 2 d each as scheduled (S, dP,
-    # G as two, A in each of its three passes, plus hK, hV, hQ, hdO: 44 d);
-    # the forward's two (S and P V: 4 d)
-    per_pair = {"bob": 44 * w.d, "fwd": 4 * w.d}.get(w.op, 10 * w.d)
+    # algorithmic FLOPs per kept pair, recomputation excluded: the backward's
+    # five contractions (10 d); the backward of the backward's twelve (S, dP,
+    # G as two, A, then hQ, hK, hdO as two each and hV: 24 d); the forward's
+    # two (S and P V: 4 d).  The backward of the backward's three passes
+    # execute 22 products (44 d), reported as executed work beside it.
+    per_pair = {"bob": 24 * w.d, "fwd": 4 * w.d}.get(w.op, 10 * w.d)
     flops = per_pair * P
     value = flops / (ms * 1e-3) / 1e12
     if w.op in ("bob", "fwd"):
@@ -402,6 +405,7 @@ def main(argv=None):
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
                    "causal": w.causal, "scale": w.scale, "layout": "[B,N,H,d]",
                    "parallelism": "single GPU", "op": w.op, "flops_per_pair": per_pair,
+                   **({"flops_per_pair_executed": 44 * w.d} if w.op == "bob" else {}),
                    **({"block_mask": w.mask, "kept_pairs": P} if bm is not None else {})},
         "pct_of_peak": round(100 * value / peak, 2),
         "stages_ms": ({"bwd_bwd": round(dqk, 4)} if w.op == "bob" else
@@ -417,7 +421,9 @@ def main(argv=None):
                                                  / denominators["copy_gbs"], 4)),
         "roofline": {"kernel": dkdv_kernel, "bound": "mfma", "achieved": round(achieved, 3),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": traffic_record() if w.name == "c5_long" else None},
+                     "traffic": traffic_record() if w.name == "c5_long" else None,
+                     **({"executed_tflops": round(44 * w.d * P / (dqk * 1e-3) / 1e12, 3)}
+                        if w.op == "bob" else {})},
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle, whole heads, bounded)", file=sys.stderr, flush=True)
