@@ -84,21 +84,27 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
   const int kv0 = kvb + wave * 32;
   const int kv = kv0 + l32;
   const LanePlan<D> plan(lane);
-  frag kf[KS], vf[KS];
-  load_row_frags<bf16, D>(kf, K + base, rs, kv, N, d, h);
-  load_row_frags<bf16, D>(vf, V + base, rs, kv, N, d, h);
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    pin_agpr(kf[ks]);
-    pin_agpr(vf[ks]);
+  using FS = AsyncFillShape<BQ, D>;
+  unsigned copy_off[FS::PER];
+  async_fill_plan<BQ, D>(copy_off, rs, wave, lane);
+  // The block's K and V rows go to LDS first, by whole-row copies (buf2 holds
+  // rows 0..63, buf3 rows 64..127; K in the q slot, V in the o slot; the
+  // sequence's ragged last block by the register path with zero rows).  They
+  // fly while the visit list is built and the walk's first two tiles are
+  // requested, and each wave then reads its 32 rows into registers.
+  if (kvb + BKV <= N) {
+    async_fill_untracked<BQ, D>(QT{buf2.q}, K + base + kvb * rs, copy_off, wave);
+    async_fill_untracked<BQ, D>(QT{buf2.o}, V + base + kvb * rs, copy_off, wave);
+    async_fill_untracked<BQ, D>(QT{buf3.q}, K + base + (kvb + BQ) * rs, copy_off, wave);
+    async_fill_untracked<BQ, D>(QT{buf3.o}, V + base + (kvb + BQ) * rs, copy_off, wave);
+  } else {
+    fill_sync(QT{buf2.q}, K + base, rs, kvb, N, d, tid);
+    fill_sync(QT{buf2.o}, V + base, rs, kvb, N, d, tid);
+    fill_sync(QT{buf3.q}, K + base, rs, kvb + BQ, N, d, tid);
+    fill_sync(QT{buf3.o}, V + base, rs, kvb + BQ, N, d, tid);
   }
-
+  frag kf[KS], vf[KS];                          // read from LDS before the walk
   f32x16 dv_acc[MT], dk_acc[MT];
-#pragma unroll
-  for (int i = 0; i < MT; ++i) {
-    dv_acc[i] = zero16(); pin_agpr(dv_acc[i]);
-    dk_acc[i] = zero16(); pin_agpr(dk_acc[i]);
-  }
 
   const int nqt = (N + BQ - 1) / BQ;
   const int qt0 = CAUSAL ? kvb / BQ : 0;
@@ -116,13 +122,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     });
   }
 
-  unsigned copy_off[AsyncFillShape<BQ, D>::PER];
-  async_fill_plan<BQ, D>(copy_off, rs, wave, lane);
   // A query tile (Q, dO rows and their two row scalars) into LDS.  Whole
   // tiles go by direct global->LDS copies: 2 * PER instructions per wave,
   // plus one for the row scalars on waves 0 and 1.  The walk's first tile may
   // be the sequence's ragged last one: register path with zero padding.
-  using FS = AsyncFillShape<BQ, D>;
   auto fill_whole = [&](Buf& B, int t) ATTN_INLINE {
     const int q0 = t * BQ;
     async_fill_untracked<BQ, D>(QT{B.q}, Q + base + q0 * rs, copy_off, wave);
@@ -407,6 +410,34 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
   if (ntiles > 0) {                             // a sparse walk may visit nothing
     fill(buf0, tile_of(0));
     if (ntiles > 1) fill_whole(buf1, tile_of(1));
+  }
+  // K and V have landed once at most the 2 PER copies of a tile issued after
+  // them are in flight (a ragged first tile went by the register path, whose
+  // loads were waited for in order after them); every wave's copies, then
+  // the reads
+  if (ntiles > 0) wait_async_fills_but<2 * FS::PER>();
+  else wait_async_fills();
+  lds_barrier();
+  {
+    const Buf& kvt = wave < 2 ? buf2 : buf3;
+    const int r0 = (wave & 1) * 32;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      kf[ks] = plan.cols(kvt.q, r0, ks);
+      vf[ks] = plan.cols(kvt.o, r0, ks);
+      pin_agpr(kf[ks]);
+      pin_agpr(vf[ks]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    dv_acc[i] = zero16(); pin_agpr(dv_acc[i]);
+    dk_acc[i] = zero16(); pin_agpr(dk_acc[i]);
+  }
+
+  if (ntiles > 0) {
+    // the first step's barrier also frees buf2 (its copies of tile 2 land
+    // there) from the K, V reads above
     step(bool_c<false>{}, 0, buf0, buf3, buf2);
     int k = 1;
     for (; k + 6 <= ntiles; k += 4) {
@@ -428,11 +459,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
   mma_acc_drain(dv_acc);
 #pragma unroll
   for (int i = 0; i < MT; ++i) asm volatile("" : "+a"(dk_acc[i]));
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    store_acc_transposed<bf16>(dv_acc[mt], dV + base, rs, kv0, mt * 32, N, d, 1.f, lane);
-    store_acc_transposed<bf16>(dk_acc[mt], dK + base, rs, kv0, mt * 32, N, d, scale, lane);
-  }
+  // every wave is done with the ring: rows out through buf0 (waves 0, 1) and
+  // buf1 (waves 2, 3), whole rows per store
+  static_assert(2 * RowStage<D>::BYTES <= sizeof(Buf), "staging area");
+  lds_barrier();
+  bf16* stage = reinterpret_cast<bf16*>(wave < 2 ? &buf0 : &buf1) + (wave & 1) * (RowStage<D>::BYTES / 2);
+  store_rows_via_lds<D>(dv_acc, dV + base, rs, kv0, N, 1.f, stage, lane);
+  store_rows_via_lds<D>(dk_acc, dK + base, rs, kv0, N, scale, stage, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -492,23 +525,8 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
   float nl2[NH];                               // -L log2 e of the lane's query, per half
   const bf16 one = (bf16)1.f, zero = (bf16)0.f;
   ones = h == 0 ? frag{one, one, zero, zero, zero, zero, zero, zero} : frag{};
-#pragma unroll
-  for (int c = 0; c < NH; ++c) {
-    const int q = qw + 32 * c + l32;
-    load_row_frags<bf16, D>(qf[c], Q + base, rs, q, N, d, h);
-    load_row_frags<bf16, D>(of[c], dO + base, rs, q, N, d, h);
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      pin_agpr(qf[c][kk]);
-      pin_agpr(of[c][kk]);
-    }
-    // padded rows (q >= N) and rows with no kept key (stored -inf): P = 0
-    nl2[c] = q < N ? Lh[q] : -__builtin_inff();
-    const float dq = q < N ? Dh[q] : 0.f;
-    const bf16 dhi = (bf16)dq;
-    const bf16 dlo = (bf16)(dq - (float)dhi);
-    bd[c] = h == 0 ? frag{dhi, dlo, zero, zero, zero, zero, zero, zero} : frag{};
-  }
+  // (Q, dO and the row scalars of the wave's rows are read once the walk's
+  // first two key tiles are on their way, below)
 
   f32x16 acc[NH][MT];
 #pragma unroll
@@ -740,6 +758,24 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
   bds1[0] = bds1[1] = frag{};
   if (ntiles > 0) fill(buf0, tile_at(0));       // a sparse walk may visit nothing
   if (ntiles > 1) fill(buf1, tile_at(1));
+  // the wave's own rows, while those copies fly
+#pragma unroll
+  for (int c = 0; c < NH; ++c) {
+    const int q = qw + 32 * c + l32;
+    load_row_frags<bf16, D>(qf[c], Q + base, rs, q, N, d, h);
+    load_row_frags<bf16, D>(of[c], dO + base, rs, q, N, d, h);
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      pin_agpr(qf[c][kk]);
+      pin_agpr(of[c][kk]);
+    }
+    // padded rows (q >= N) and rows with no kept key (stored -inf): P = 0
+    nl2[c] = q < N ? Lh[q] : -__builtin_inff();
+    const float dq = q < N ? Dh[q] : 0.f;
+    const bf16 dhi = (bf16)dq;
+    const bf16 dlo = (bf16)(dq - (float)dhi);
+    bd[c] = h == 0 ? frag{dhi, dlo, zero, zero, zero, zero, zero, zero} : frag{};
+  }
   int kt = 0;
   for (; kt + 3 <= inner_end; kt += 3) {
     step_inner(kt, buf0, buf2);
@@ -761,12 +797,14 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
   }
 
   mma_acc_drain(acc);
+  // every wave is done with the key tiles: rows out through buf0 (waves 0, 1)
+  // and buf1 (waves 2, 3), whole rows per store
+  static_assert(NW == 4 && 2 * RowStage<D>::BYTES <= sizeof(Buf), "staging area");
+  lds_barrier();
+  bf16* stage = reinterpret_cast<bf16*>(wave < 2 ? &buf0 : &buf1) + (wave & 1) * (RowStage<D>::BYTES / 2);
 #pragma unroll
   for (int c = 0; c < NH; ++c)
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-      store_acc_transposed<bf16>(acc[c][mt], dQ + base, rs, qw + 32 * c, mt * 32, N, d, scale,
-                                 lane);
+    store_rows_via_lds<D>(acc[c], dQ + base, rs, qw + 32 * c, N, scale, stage, lane);
 }
 
 // ---------------------------------------------------------------------------

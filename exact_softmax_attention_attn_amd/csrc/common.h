@@ -576,4 +576,46 @@ __device__ __forceinline__ void store_acc_transposed(const f32x16& acc, T* g, lo
   }
 }
 
+// Store a wave's 32 positions x D head-dim columns, held as D / 32 accumulators
+// of X^T in the layout store_acc_transposed takes (accumulator mt: columns
+// 32 mt .. 32 mt + 31 by positions n0 .. n0 + 31), into a global
+// [pos, row_stride] bf16 matrix, times `mul`, by way of a wave-private LDS
+// area of 32 rows x RowStage<D>::PITCH = D + 8 elements (the 16-byte pad keeps
+// the reads aligned and spreads the writes of one column over the banks).  The
+// lanes first put their 4-column pieces there, then read back 16-byte pieces
+// of whole rows: each store instruction then writes 64 / (D / 8) complete
+// rows instead of one 16-byte piece of each of 32 rows.  Positions >= nrows
+// are not stored.  No other wave may use the area meanwhile.
+template <int D> struct RowStage {
+  static constexpr int PITCH = D + 8;
+  static constexpr int BYTES = 32 * PITCH * 2;
+};
+template <int D>
+__device__ __forceinline__ void store_rows_via_lds(const f32x16 (&acc)[D / 32], bf16* g,
+                                                   long row_stride, int n0, int nrows, float mul,
+                                                   bf16* stage, int lane) {
+  constexpr int PITCH = RowStage<D>::PITCH;
+  const int h = lane >> 5, r = lane & 31;
+#pragma unroll
+  for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+    for (int grp = 0; grp < 4; ++grp) {
+      const bf16x4 v{(bf16)(acc[mt][4 * grp + 0] * mul), (bf16)(acc[mt][4 * grp + 1] * mul),
+                     (bf16)(acc[mt][4 * grp + 2] * mul), (bf16)(acc[mt][4 * grp + 3] * mul)};
+      *reinterpret_cast<bf16x4*>(stage + r * PITCH + mt * 32 + 8 * grp + 4 * h) = v;
+    }
+  // the wave's LDS writes land before its reads below
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  constexpr int CPR = D / 8;                   // 16-byte pieces per row
+  constexpr int RPI = 64 / CPR;                // rows per instruction
+#pragma unroll
+  for (int j = 0; j < 32 / RPI; ++j) {
+    const int rr = j * RPI + lane / CPR, c = (lane % CPR) * 8;
+    const bf16x8 v = *reinterpret_cast<const bf16x8*>(stage + rr * PITCH + c);
+    if (n0 + rr < nrows) *reinterpret_cast<bf16x8*>(g + (long)(n0 + rr) * row_stride + c) = v;
+  }
+  // the reads are done before the area is written again
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
 }  // namespace attn
