@@ -2,15 +2,18 @@
 """Benchmark of the exact causal attention backward (attn_bwd) on one MI355X.
 
 One step = one attn_bwd over the whole workload: the preprocess (D), the
-dK/dV kernel and the dQ kernel, launched through the C ABI stage entry
-points on torch's current stream.  Inputs, O and L (from attn_fwd_lse) are
-resident in HBM before the timed region starts.
+dK/dV kernel and the dQ kernel, launched back to back by the C ABI entry
+point on torch's current stream.  Inputs, O and L (from attn_fwd_lse) are
+resident in HBM before the timed region starts.  A second timed region runs
+the same steps through the three stage entry points with HIP events between
+the kernels, for the per-stage times and the roofline.
 
 Prints one JSON line.  `value` is attn_bwd TFLOP/s with FLOPs counted as
-10 * d * (kept pairs), kept pairs = B*H*N(N+1)/2 causal.  `roofline` covers
-the dominant kernel (dK/dV): its algorithmic FLOPs (8 * d * pairs: S, dP,
-dV, dK) over its mean duration from HIP events recorded around it on the
-launch stream, against the bf16 dense MFMA peak.  `cpu_baseline` times the
+10 * d * (kept pairs), kept pairs = B*H*N(N+1)/2 causal, over the first
+region's wall time.  `roofline` covers the dominant kernel (dK/dV): its
+algorithmic FLOPs (8 * d * pairs: S, dP, dV, dK) over its mean duration from
+the HIP events recorded around it on the launch stream in the second region,
+against the bf16 dense MFMA peak.  `cpu_baseline` times the
 fp64 oracle on whole (batch, head) slices of the same workload on the host
 cores (a bounded sample of about CPU_BASELINE_SECONDS).
 
@@ -310,19 +313,43 @@ def main(argv=None):
         if ev is not None:
             ev[3].record()
 
+    def call():
+        # one step as a user makes it: the operation's own entry point (the
+        # backward's three kernels go out back to back from one C call)
+        if w.op == "bob":
+            return step_bob()
+        if w.op == "fwd":
+            return forward()
+        if mask is None:
+            binding.attn_bwd(q, k, v, o, do, lse, causal=w.causal, scale=w.scale, dq=dq, dk=dk,
+                             dv=dv, workspace=ws)
+        else:
+            binding.attn_bwd_masked(q, k, v, o, do, lse, mask, causal=w.causal, scale=w.scale,
+                                    dq=dq, dk=dk, dv=dv, workspace=ws)
+
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
-        step()
+        call()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # timed region 1 (value, ms_per_step): K steps of the entry point
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for _ in range(args.steps):
+        call()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    # timed region 2 (stages, roofline): the same K steps through the stage
+    # entry points, HIP events between the kernels on the launch stream
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
 
     pre = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     dkdv = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))

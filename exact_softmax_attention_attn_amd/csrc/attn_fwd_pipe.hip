@@ -7,11 +7,11 @@
 // ddx issue #243 (item 2) keeps for the backward: L = m + log z, natural log of
 // the row's normaliser of the scaled scores.
 //
-// Workgroup = 4 waves = 256 query rows of one (b, h); wave w owns query rows
-// qw + [0, 64) as two halves of 32.  Q is the B operand of S^T = K Q^T and
-// stays in AGPRs, so each lane owns one query row of each half, and the O^T
-// accumulators stay in AGPRs.  Each K and V operand read from LDS feeds both
-// halves.
+// Workgroup = 256 query rows of one (b, h): NW = 4 waves of 64 rows (two
+// halves of 32, NH = 2) or 8 waves of 32 rows (NH = 1, two waves per SIMD).
+// Q is the B operand of S^T = K Q^T and stays in AGPRs, so each lane owns one
+// query row of each half, and the O^T accumulators stay in AGPRs.  With two
+// halves each K and V operand read from LDS feeds both.
 //
 // Online softmax in log2 units, kept per query: m (running max of c s, c =
 // scale log2 e) and l (running sum of exp2(c s - m)); the scale is applied in
@@ -25,7 +25,9 @@
 //                                             row sums of P_j
 //   B: O^T_c += V^T P_j^T (c = 0, 1)        | mask, row max, rescale decision
 //                                             and half-0 exps of S_{j+1}
-// so every VALU stage reads a chain that finished one chain earlier.  Row sums
+// so every VALU stage reads a chain that finished one chain earlier (with one
+// half, chain A only packs and sums, and the other wave on the SIMD fills the
+// gaps).  Row sums
 // are taken on the bf16 P that enters the products (pairs summed by
 // v_dot2_f32_bf16), so O and l are normalised consistently.  The two lanes
 // that share a query exchange their halves of a key sub-tile with
@@ -79,14 +81,15 @@ __device__ __forceinline__ float frag_sum(const bf16x8& f, float acc) {
 
 }  // namespace
 
-template <int D, bool CAUSAL, bool SPARSE>
-__global__ __launch_bounds__(256, 1) void fwd_bf16_pipe_kernel(
+template <int D, bool CAUSAL, bool SPARSE, int NH, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_pipe_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     bf16* __restrict__ O, float* __restrict__ Lout, int H, int N, int d, float scale_log2,
     const unsigned char* __restrict__ mask, int mask_heads) {
   using M = Mma<bf16>;
   using frag = bf16x8;
-  constexpr int NH = 2, WQ = 64, NW = 4, BQ = NW * WQ, BKV = 64;
+  constexpr int WQ = 32 * NH, BQ = NW * WQ, BKV = 64;
+  static_assert(BQ == 256, "256 query rows per workgroup");
   constexpr int KS = D / 16, MT = D / 32, L = KS, AH = 4, NT = NW * 64;
   static_assert(L == 2 * MT, "chain length");
   using KT = Tile<bf16, BKV, D>;
@@ -127,7 +130,7 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_pipe_kernel(
   // rows, in order (entry = tile | which mask rows keep it << 14)
   __shared__ unsigned short vis[SPARSE ? kMaxVisit : 1];
   __shared__ int nvis;
-  static_assert(!SPARSE || (BQ == 2 * kMaskBlock && WQ * 2 == kMaskBlock),
+  static_assert(!SPARSE || (BQ == 2 * kMaskBlock && kMaskBlock % WQ == 0),
                 "mask rows per block and per wave");
   const int nb = (N + kMaskBlock - 1) / kMaskBlock;
   const int ntiles = !SPARSE ? ntiles_all : build_visits(vis, &nvis, ntiles_all,
@@ -278,9 +281,13 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_pipe_kernel(
     // A: S_{j+1} | exps of S_j half 1, pack P_j and its row sums
     constexpr int EH = 16 / (L / 2);             // half-1 exps per product pair
     auto valu_a = [&](int i) ATTN_INLINE {
-      if (i < L / 2) exps(sc, 1, i * EH, (i + 1) * EH);
+      if constexpr (NH > 1) {
+        if (i < L / 2) exps(sc, 1, i * EH, (i + 1) * EH);
+      }
       if (i == L / 2) pack_and_sum(0);
-      if (i == L / 2 + 1) pack_and_sum(1);
+      if constexpr (NH > 1) {
+        if (i == L / 2 + 1) pack_and_sum(1);
+      }
     };
     if (has_next) {
       s_chain(Bn, j + 1, sn, valu_a);
@@ -297,10 +304,13 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_pipe_kernel(
       if (i == 1) {
         float mx[NH];
         row_max(sn, mx);
-        bool upd[NH];
+        bool upd[NH], any = false;
 #pragma unroll
-        for (int c = 0; c < NH; ++c) upd[c] = mx[c] > m[c] + 8.f;
-        resc = __builtin_amdgcn_ballot_w64(upd[0] || upd[1]) != 0;
+        for (int c = 0; c < NH; ++c) {
+          upd[c] = mx[c] > m[c] + 8.f;
+          any = any || upd[c];
+        }
+        resc = __builtin_amdgcn_ballot_w64(any) != 0;
         if (resc) {
 #pragma unroll
           for (int c = 0; c < NH; ++c) {
@@ -397,10 +407,15 @@ __global__ __launch_bounds__(256, 1) void fwd_bf16_pipe_kernel(
   }
 }
 
+// Waves per workgroup: 8 of 32 query rows each (two waves per SIMD, which
+// hide each other's softmax work at the price of twice the LDS operand reads
+// per product), where a wave fits in 256 registers; otherwise 4 of 64 rows
+// (the non-causal d = 128 form, whose edge checks need more registers).
 template <int D, bool C, bool S>
 static hipError_t fwd_pipe_run(const FwdArgs& a, hipStream_t stream) {
+  constexpr int NW = (D == 128 && !C) ? 4 : 8, NH = 8 / NW;
   dim3 grid((a.N + 255) / 256, a.H, a.B);
-  hipLaunchKernelGGL((fwd_bf16_pipe_kernel<D, C, S>), grid, dim3(256), 0, stream,
+  hipLaunchKernelGGL((fwd_bf16_pipe_kernel<D, C, S, NH, NW>), grid, dim3(NW * 64), 0, stream,
                      static_cast<const bf16*>(a.Q), static_cast<const bf16*>(a.K),
                      static_cast<const bf16*>(a.V), static_cast<bf16*>(a.O), a.L, a.H, a.N,
                      a.d, a.scale * kLog2e, a.mask, a.mask_heads);
