@@ -218,6 +218,21 @@ int run_bwd(const void* Q, const void* K, const void* V, const void* O, const vo
   if (e != hipSuccess) return finish(e);
   return finish(attn::launch_bwd_dq(a, s));
 }
+
+int run_bob(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+            const float* L, const void* gQ, const void* gK, const void* gV, void* hQ, void* hK,
+            void* hV, void* hdO, void* workspace, const unsigned char* mask, int mask_heads,
+            int B, int H, int N, int d, int causal, float scale, int dtype, void* stream) {
+  attn::BobArgs a;
+  a.Q = Q; a.K = K; a.V = V; a.O = O; a.dO = dO; a.L = L;
+  a.gQ = gQ; a.gK = gK; a.gV = gV;
+  a.hQ = hQ; a.hK = hK; a.hV = hV; a.hdO = hdO;
+  a.ws = static_cast<float*>(workspace);
+  a.B = B; a.H = H; a.N = N; a.d = d;
+  a.causal = causal; a.scale = scale; a.dtype = dtype;
+  a.mask = mask; a.mask_heads = mask_heads;
+  return finish(attn::launch_bwd_bwd(a, static_cast<hipStream_t>(stream)));
+}
 }  // namespace
 
 extern "C" {
@@ -324,14 +339,23 @@ int attn_bwd_bwd(const void* Q, const void* K, const void* V, const void* O, con
   ATTN_TRY(check_scale_causal(scale, causal));
   ATTN_TRY(check_dtype_dim(H, d, dtype));
   if (d > (dtype == ATTN_BF16 ? 128 : 64)) return ATTN_ERR_UNSUPPORTED;
-  attn::BobArgs a;
-  a.Q = Q; a.K = K; a.V = V; a.O = O; a.dO = dO; a.L = L;
-  a.gQ = gQ; a.gK = gK; a.gV = gV;
-  a.hQ = hQ; a.hK = hK; a.hV = hV; a.hdO = hdO;
-  a.ws = static_cast<float*>(workspace);
-  a.B = B; a.H = H; a.N = N; a.d = d;
-  a.causal = causal; a.scale = scale; a.dtype = dtype;
-  return finish(attn::launch_bwd_bwd(a, static_cast<hipStream_t>(stream)));
+  return run_bob(Q, K, V, O, dO, L, gQ, gK, gV, hQ, hK, hV, hdO, workspace, nullptr, 1, B, H, N,
+                 d, causal, scale, dtype, stream);
+}
+
+int attn_bwd_bwd_masked(const void* Q, const void* K, const void* V, const void* O,
+                        const void* dO, const float* L, const void* gQ, const void* gK,
+                        const void* gV, void* hQ, void* hK, void* hV, void* hdO, void* workspace,
+                        const unsigned char* mask, int mask_heads, int B, int H, int N, int d,
+                        int causal, float scale, int dtype, void* stream) {
+  ATTN_TRY(check_ptrs({Q, K, V, O, dO, L, gQ, gK, gV, hQ, hK, hV, hdO, workspace}));
+  ATTN_TRY(check_sizes(B, H, N, d));
+  ATTN_TRY(check_scale_causal(scale, causal));
+  ATTN_TRY(check_dtype_dim(H, d, dtype));
+  ATTN_TRY(check_mask(mask, mask_heads, B, H, N));
+  if (d > (dtype == ATTN_BF16 ? 128 : 64)) return ATTN_ERR_UNSUPPORTED;
+  return run_bob(Q, K, V, O, dO, L, gQ, gK, gV, hQ, hK, hV, hdO, workspace, mask, mask_heads, B,
+                 H, N, d, causal, scale, dtype, stream);
 }
 
 const char* attn_status_string(int status) {

@@ -20,7 +20,9 @@
 //
 // The kernels follow the generic forward / backward kernels' tiling: 4 waves,
 // 32 rows per wave, 64-row streamed tiles double-buffered in LDS, the wave's
-// own rows as the B operands of 32x32 matrix products.
+// own rows as the B operands of 32x32 matrix products.  With a block mask
+// (optional) each workgroup, whose 128 rows are one mask row or column,
+// walks a visit list of the kept tiles instead of the whole range.
 #include <type_traits>
 
 #include "common.h"
@@ -43,7 +45,8 @@ __global__ __launch_bounds__(256, 1) void bob_q_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ dO, const T* __restrict__ gQ, const T* __restrict__ gK,
     const T* __restrict__ gV, float* __restrict__ ws, T* __restrict__ hQ, T* __restrict__ hdO,
-    int H, int N, int d, float scale_log2, float scale) {
+    int H, int N, int d, float scale_log2, float scale, const unsigned char* __restrict__ mask,
+    int mask_heads) {
   using M = Mma<T>;
   using frag = typename M::frag;
   constexpr int BQ = 128, BKV = 64, KS = D / M::K, MT = D / 32, RS = 32 / M::K;
@@ -90,6 +93,23 @@ __global__ __launch_bounds__(256, 1) void bob_q_kernel(
 
   const int kv_end = CAUSAL ? min(N, qb + BQ) : N;
   const int nkt = (kv_end + BKV - 1) / BKV;
+  // the walk: key tiles 0 .. nkt - 1, or (block mask) the ones whose mask
+  // block (row ib: the workgroup's 128 query rows are one mask row, column of
+  // the tile) is kept
+  static_assert(BQ == kMaskBlock, "one mask row per workgroup");
+  __shared__ unsigned short vis[kMaxVisit];
+  __shared__ int nvis;
+  int ntiles = nkt;
+  if (mask) {
+    const int nb = (N + kMaskBlock - 1) / kMaskBlock;
+    const unsigned char* mk = head_mask(mask, mask_heads, b, head, H, nb);
+    ntiles = build_visits(vis, &nvis, nkt, [&](int t) ATTN_INLINE -> unsigned {
+      return mk[ib * nb + t * BKV / kMaskBlock] ? (1u << 14) | (unsigned)t : 0u;
+    });
+  }
+  auto tile_at = [&](int p) ATTN_INLINE -> int {
+    return mask ? (int)(visit_entry(vis, p) & kVisitTile) : p;
+  };
 
   auto fill = [&](Buf& B, int kt) ATTN_INLINE {
     const int k0 = kt * BKV;
@@ -203,20 +223,23 @@ __global__ __launch_bounds__(256, 1) void bob_q_kernel(
     }
   };
 
-  auto step = [&](const Buf& cur, Buf& nxt, int kt) ATTN_INLINE {
-    if (kt + 1 < nkt) fill(nxt, kt + 1);
-    const int k0 = kt * BKV;
+  // step p: tile tile_at(p) in cur while tile tile_at(p + 1) is copied to nxt
+  auto step = [&](const Buf& cur, Buf& nxt, int p) ATTN_INLINE {
+    const int k0 = tile_at(p) * BKV;
+    if (p + 1 < ntiles) fill(nxt, tile_at(p + 1));
     body(cur, k0, (CAUSAL && k0 + BKV - 1 > qb) || k0 + BKV > N);
     wait_async_fills();
     __syncthreads();
   };
 
-  fill(bufA, 0);
-  wait_async_fills();
-  __syncthreads();
-  for (int kt = 0; kt < nkt; kt += 2) {
-    step(bufA, bufB, kt);
-    if (kt + 1 < nkt) step(bufB, bufA, kt + 1);
+  if (ntiles > 0) {                               // a masked walk may visit nothing
+    fill(bufA, tile_at(0));
+    wait_async_fills();
+    __syncthreads();
+  }
+  for (int p = 0; p < ntiles; p += 2) {
+    step(bufA, bufB, p);
+    if (p + 1 < ntiles) step(bufB, bufA, p + 1);
   }
 
   if constexpr (PASS == 1) {
@@ -247,7 +270,8 @@ __global__ __launch_bounds__(256, 1) void bob_kv_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ dO, const T* __restrict__ gQ, const T* __restrict__ gK,
     const T* __restrict__ gV, const float* __restrict__ ws, T* __restrict__ hK,
-    T* __restrict__ hV, int H, int N, int d, float scale_log2, float scale) {
+    T* __restrict__ hV, int H, int N, int d, float scale_log2, float scale,
+    const unsigned char* __restrict__ mask, int mask_heads) {
   using M = Mma<T>;
   using frag = typename M::frag;
   constexpr int BKV = 128, BQ = 64, KS = D / M::K, MT = D / 32, RS = 32 / M::K;
@@ -290,6 +314,24 @@ __global__ __launch_bounds__(256, 1) void bob_kv_kernel(
 
   const int nqt = (N + BQ - 1) / BQ;
   const int qt0 = CAUSAL ? kvb / BQ : 0;
+  // the walk: query tiles qt0 .. nqt - 1, or (block mask) the ones whose mask
+  // block (row of the tile, column jb: the workgroup's 128 keys are one mask
+  // column) is kept
+  static_assert(BKV == kMaskBlock, "one mask column per workgroup");
+  __shared__ unsigned short vis[kMaxVisit];
+  __shared__ int nvis;
+  int ntiles = nqt - qt0;
+  if (mask) {
+    const int nb = (N + kMaskBlock - 1) / kMaskBlock;
+    const unsigned char* mk = head_mask(mask, mask_heads, b, head, H, nb);
+    ntiles = build_visits(vis, &nvis, ntiles, [&](int i) ATTN_INLINE -> unsigned {
+      const int t = qt0 + i;
+      return mk[(t * BQ / kMaskBlock) * nb + jb] ? (1u << 14) | (unsigned)t : 0u;
+    });
+  }
+  auto tile_at = [&](int p) ATTN_INLINE -> int {
+    return mask ? (int)(visit_entry(vis, p) & kVisitTile) : qt0 + p;
+  };
 
   auto fill = [&](Buf& B, int qt) ATTN_INLINE {
     const int q0 = qt * BQ;
@@ -401,20 +443,23 @@ __global__ __launch_bounds__(256, 1) void bob_kv_kernel(
     }
   };
 
-  auto step = [&](const Buf& cur, Buf& nxt, int qt) ATTN_INLINE {
-    if (qt + 1 < nqt) fill(nxt, qt + 1);
-    const int q0 = qt * BQ;
+  // step p: tile tile_at(p) in cur while tile tile_at(p + 1) is copied to nxt
+  auto step = [&](const Buf& cur, Buf& nxt, int p) ATTN_INLINE {
+    const int q0 = tile_at(p) * BQ;
+    if (p + 1 < ntiles) fill(nxt, tile_at(p + 1));
     body(cur, q0, CAUSAL && q0 < kvb + BKV);
     wait_async_fills();
     __syncthreads();
   };
 
-  fill(bufA, qt0);
-  wait_async_fills();
-  __syncthreads();
-  for (int qt = qt0; qt < nqt; qt += 2) {
-    step(bufA, bufB, qt);
-    if (qt + 1 < nqt) step(bufB, bufA, qt + 1);
+  if (ntiles > 0) {                               // a masked walk may visit nothing
+    fill(bufA, tile_at(0));
+    wait_async_fills();
+    __syncthreads();
+  }
+  for (int p = 0; p < ntiles; p += 2) {
+    step(bufA, bufB, p);
+    if (p + 1 < ntiles) step(bufB, bufA, p + 1);
   }
 
 #pragma unroll
@@ -437,7 +482,8 @@ static hipError_t bob_go(const BobArgs& a, hipStream_t stream) {
                      static_cast<const T*>(a.V), static_cast<const T*>(a.dO),
                      static_cast<const T*>(a.gQ), static_cast<const T*>(a.gK),
                      static_cast<const T*>(a.gV), a.ws, static_cast<T*>(a.hQ),
-                     static_cast<T*>(a.hdO), a.H, a.N, a.d, sl2, a.scale);
+                     static_cast<T*>(a.hdO), a.H, a.N, a.d, sl2, a.scale, a.mask,
+                     a.mask_heads);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bob_kv_kernel<T, D, C>), gq, dim3(256), 0, stream,
@@ -445,7 +491,8 @@ static hipError_t bob_go(const BobArgs& a, hipStream_t stream) {
                      static_cast<const T*>(a.V), static_cast<const T*>(a.dO),
                      static_cast<const T*>(a.gQ), static_cast<const T*>(a.gK),
                      static_cast<const T*>(a.gV), a.ws, static_cast<T*>(a.hK),
-                     static_cast<T*>(a.hV), a.H, a.N, a.d, sl2, a.scale);
+                     static_cast<T*>(a.hV), a.H, a.N, a.d, sl2, a.scale, a.mask,
+                     a.mask_heads);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bob_q_kernel<T, D, C, 2>), gq, dim3(256), 0, stream,
@@ -453,7 +500,8 @@ static hipError_t bob_go(const BobArgs& a, hipStream_t stream) {
                      static_cast<const T*>(a.V), static_cast<const T*>(a.dO),
                      static_cast<const T*>(a.gQ), static_cast<const T*>(a.gK),
                      static_cast<const T*>(a.gV), a.ws, static_cast<T*>(a.hQ),
-                     static_cast<T*>(a.hdO), a.H, a.N, a.d, sl2, a.scale);
+                     static_cast<T*>(a.hdO), a.H, a.N, a.d, sl2, a.scale, a.mask,
+                     a.mask_heads);
   return hipGetLastError();
 }
 

@@ -57,6 +57,8 @@ struct BobArgs {
   int causal;
   float scale;
   int dtype;
+  const unsigned char* mask = nullptr;   // optional block mask (as BwdArgs)
+  int mask_heads = 1;
 };
 
 // Head dims are served by kernels compiled for 32, 64, 128 or (bf16) 256

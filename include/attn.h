@@ -236,6 +236,18 @@ int attn_bwd_bwd(const void* Q, const void* K, const void* V, const void* O, con
                  void* hQ, void* hK, void* hV, void* hdO, void* workspace,
                  int B, int H, int N, int d, int causal, float scale, int dtype, void* stream);
 
+/* attn_bwd_bwd restricted to the pairs a block mask keeps (mask and
+ * mask_heads as in the block-sparse section above; L from attn_fwd_lse_masked
+ * with the same mask).  Every pass walks only kept tiles; a query row that
+ * keeps no key gets r = E = 0 and hQ = hdO = 0, and adds nothing to hK, hV.
+ * Validation and limits are those of attn_bwd_bwd plus the mask's. */
+int attn_bwd_bwd_masked(const void* Q, const void* K, const void* V, const void* O,
+                        const void* dO, const float* L, const void* gQ, const void* gK,
+                        const void* gV, void* hQ, void* hK, void* hV, void* hdO, void* workspace,
+                        const unsigned char* mask, int mask_heads,
+                        int B, int H, int N, int d, int causal, float scale, int dtype,
+                        void* stream);
+
 /* Static text for a status code ("ok", "invalid argument", ...). */
 const char* attn_status_string(int status);
 

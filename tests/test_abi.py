@@ -31,7 +31,8 @@ def _declared():
 
 def test_header_declares_the_entry_points():
     assert _declared() == sorted([
-        "attn_bwd", "attn_bwd_bwd", "attn_bwd_bwd_workspace_bytes", "attn_bwd_dkdv",
+        "attn_bwd", "attn_bwd_bwd", "attn_bwd_bwd_masked", "attn_bwd_bwd_workspace_bytes",
+        "attn_bwd_dkdv",
         "attn_bwd_dkdv_masked", "attn_bwd_dq", "attn_bwd_dq_masked", "attn_bwd_masked",
         "attn_bwd_noalloc", "attn_bwd_preprocess", "attn_bwd_workspace_bytes", "attn_fwd_lse",
         "attn_fwd_lse_masked", "attn_last_error", "attn_status_string"])
@@ -188,6 +189,24 @@ def test_bwd_bwd_entry_point_validates(lib):
     assert call(dtype=5) == 2
     assert lib.attn_bwd_bwd_workspace_bytes(2, 3, 10, 64) == 4 * 60 * 4
     assert lib.attn_bwd_bwd_workspace_bytes(0, 3, 10, 64) == 0
+    assert lib.attn_last_error() == b""
+
+
+def test_masked_bwd_bwd_entry_point_validates(lib):
+    p14 = [FAKE] * 14
+
+    def call(mask=FAKE, heads=1, ptrs=p14, B=1, H=1, N=8, d=8, causal=1, scale=0.5, dtype=0):
+        return lib.attn_bwd_bwd_masked(*ptrs, mask, heads, B, H, N, d, causal, scale, dtype, NUL)
+
+    for i in range(14):
+        p = list(p14); p[i] = NUL
+        assert call(ptrs=p) == 1
+    assert call(mask=NUL) == 1                  # no mask
+    assert call(heads=0) == 1                   # mask_heads not 1 or B * H
+    assert call(heads=3, B=2, H=2) == 1
+    assert call(N=65537) == 2                   # longer walks than the visit lists hold
+    assert call(d=68) == 2 and call(d=136, dtype=1) == 2
+    assert call(scale=0.0) == 1 and call(causal=3) == 1
     assert lib.attn_last_error() == b""
 
 

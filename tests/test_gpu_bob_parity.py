@@ -4,7 +4,9 @@ Relative Frobenius error per output tensor (hQ, hK, hV, hdO) and for the two
 row scalars r and E the kernels leave in the workspace, gated per tensor, per
 (b, h) and per row as in the first backward's tests (``tests/gpu_check.py``).
 Two feeds of O and L: the library's own forward, and the oracle's O and L
-cast to the device type.
+cast to the device type.  The block-masked form is checked the same way
+against the oracle with the mask, plus two exact checks: an all-ones mask
+reproduces the unmasked call bit for bit, and an all-zeros mask gives zeros.
 """
 
 import math
@@ -144,3 +146,93 @@ def test_c5_bob_full_size_sampled_against_oracle(B):
             g[n], r[n] = _host(ws[i, 0, h])[None, None, :], s[n][None, None, :]
         gpu_check.check(f"c5_bob sampled head {h}", g, r, "bf16",
                         names=("hQ", "hK", "hV", "hdO", "r", "E"))
+
+
+# block masks: B, H, N, d, dtype, causal, mask recipe (tests/test_gpu_mask_parity.py)
+MASKED = [
+    (1, 2, 300, 64, "f32", True, "random_heads"),
+    (2, 1, 260, 32, "f32", False, "random_empty"),      # rows keeping no key
+    (1, 2, 1000, 128, "bf16", True, "random"),
+    (1, 2, 700, 128, "bf16", False, "random_empty"),
+    (1, 1, 1100, 128, "bf16", True, "window"),           # local window + sink blocks
+    (1, 2, 513, 64, "bf16", True, "random_empty"),       # ragged last tile
+]
+
+
+@pytest.mark.parametrize("case", MASKED, ids=lambda c: "x".join(map(str, c)))
+def test_masked_bwd_bwd_parity(B, case):
+    import torch
+    from tests.test_gpu_mask_parity import _mask
+    Bn, H, N, d, dtype, causal, recipe = case
+    scale = 1.0 / math.sqrt(d)
+    x = workloads.make_random(Bn, H, N, d, dtype, seed=N + d + 1,
+                              qkv_std=0.5 if dtype == "bf16" else 1.0)
+    x.update(workloads.make_cotangents(Bn, H, N, d, dtype, seed=N + 1))
+    m = _mask(recipe, Bn, H, N, seed=N + 2)
+    xs = {n: x[n].astype(np.float64) for n in x}
+    O, L = orc.attn_fwd(xs["q"], xs["k"], xs["v"], scale, causal, m)
+    ref = orc.attn_bwd_bwd(xs["q"], xs["k"], xs["v"], xs["do"], xs["gq"], xs["gk"], xs["gv"],
+                           scale, causal, m)
+    t = {n: _dev(x[n], dtype) for n in x}
+    mask = torch.from_numpy(m).cuda()
+    empty = np.isneginf(L)                                         # rows keeping no key
+    for feed in ("own", "oracle"):
+        _say(f"masked {case} feed={feed}")
+        if feed == "own":
+            o, lse = B.attn_fwd_lse_masked(t["q"], t["k"], t["v"], mask, causal=causal,
+                                           scale=scale)
+        else:
+            o = _dev(O, dtype)
+            lse = torch.from_numpy(np.ascontiguousarray(L, dtype=np.float32)).cuda()
+        ws = torch.empty((4, Bn, H, N), dtype=torch.float32, device="cuda")
+        hq, hk, hv, hdo = B.attn_bwd_bwd_masked(t["q"], t["k"], t["v"], o, t["do"], lse, t["gq"],
+                                                t["gk"], t["gv"], mask, causal=causal,
+                                                scale=scale, workspace=ws)
+        torch.cuda.synchronize()
+        got = {"hQ": _host(hq), "hK": _host(hk), "hV": _host(hv), "hdO": _host(hdo),
+               "r": _host(ws[2]), "E": _host(ws[3])}
+        for n, a in got.items():
+            assert np.isfinite(a).all(), (case, feed, n)
+        gpu_check.check(f"masked bob {case} feed={feed}", got, ref, dtype,
+                        names=("hQ", "hK", "hV", "hdO", "r", "E"))
+        if empty.any():
+            for n in ("hQ", "hdO"):
+                assert np.all(np.transpose(got[n], (0, 2, 1, 3))[empty] == 0.0), (case, feed, n)
+            assert np.all(got["r"][empty] == 0.0) and np.all(got["E"][empty] == 0.0)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_masked_bwd_bwd_all_ones_equals_unmasked_bitwise(B, causal):
+    import torch
+    n, d = 700, 128
+    _say(f"bob all-ones mask causal={causal}")
+    x = workloads.make_random(1, 2, n, d, "bf16", seed=11, qkv_std=0.5)
+    x.update(workloads.make_cotangents(1, 2, n, d, "bf16", seed=12))
+    t = {k: _dev(v, "bf16") for k, v in x.items()}
+    ones = torch.ones(((n + 127) // 128,) * 2, dtype=torch.uint8, device="cuda")
+    o, lse = B.attn_fwd_lse(t["q"], t["k"], t["v"], causal=causal)
+    args = (t["q"], t["k"], t["v"], o, t["do"], lse, t["gq"], t["gk"], t["gv"])
+    ws0 = torch.empty((4, 1, 2, n), dtype=torch.float32, device="cuda")
+    ws1 = torch.empty_like(ws0)
+    g0 = B.attn_bwd_bwd(*args, causal=causal, workspace=ws0)
+    g1 = B.attn_bwd_bwd_masked(*args, ones, causal=causal, workspace=ws1)
+    torch.cuda.synchronize()
+    for a, b in zip(g0, g1):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert torch.equal(ws0, ws1)
+
+
+def test_masked_bwd_bwd_all_zeros_gives_zeros(B):
+    import torch
+    n, d = 384, 64
+    _say("bob all-zeros mask")
+    x = workloads.make_random(1, 2, n, d, "bf16", seed=13, qkv_std=0.5)
+    x.update(workloads.make_cotangents(1, 2, n, d, "bf16", seed=14))
+    t = {k: _dev(v, "bf16") for k, v in x.items()}
+    zeros = torch.zeros((3, 3), dtype=torch.uint8, device="cuda")
+    o, lse = B.attn_fwd_lse_masked(t["q"], t["k"], t["v"], zeros)
+    out = B.attn_bwd_bwd_masked(t["q"], t["k"], t["v"], o, t["do"], lse, t["gq"], t["gk"],
+                                t["gv"], zeros)
+    torch.cuda.synchronize()
+    for a in out:
+        assert torch.all(a == 0)
