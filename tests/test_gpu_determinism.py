@@ -5,7 +5,7 @@ accumulation is owned by one workgroup, so the same call on the same inputs
 must give the same bits.  The unmasked pipelined path is covered in
 test_gpu_parity.py; this covers the block-masked path, the generic kernels
 (float32, and bf16 head dim 256 with its column split), the forward, and the
-backward of the backward.  Each case runs three times and compares bits.
+backward of the backward (dense and block-masked).  Each case runs three times and compares bits.
 """
 
 import math
@@ -89,23 +89,34 @@ def test_forward_and_backward_repeat_bitwise(B, case):
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("case", [(1, 2, 600, 128, "bf16", True), (1, 2, 200, 64, "f32", False)],
+@pytest.mark.parametrize("case", [(1, 2, 600, 128, "bf16", True, False),
+                                  (1, 2, 200, 64, "f32", False, False),
+                                  (1, 2, 600, 128, "bf16", True, True)],
                          ids=lambda c: "x".join(map(str, c)))
 def test_backward_of_backward_repeats_bitwise(B, case):
     import torch
-    Bn, H, N, d, dtype, causal = case
+    Bn, H, N, d, dtype, causal, masked = case
     _say(f"bob {case}")
     x = workloads.make_random(Bn, H, N, d, dtype, seed=N + d,
                               qkv_std=0.5 if dtype == "bf16" else 1.0)
     x.update(workloads.make_cotangents(Bn, H, N, d, dtype, seed=N))
     t = {n: _dev(x[n], dtype) for n in x}
     scale = 1.0 / math.sqrt(d)
-    o, lse = B.attn_fwd_lse(t["q"], t["k"], t["v"], causal=causal, scale=scale)
+    mask = None
+    if masked:
+        mask = torch.from_numpy(workloads.make_block_mask(N, 0.6, N, heads=(Bn, H),
+                                                          empty_rows=(1,))).cuda()
+        o, lse = B.attn_fwd_lse_masked(t["q"], t["k"], t["v"], mask, causal=causal, scale=scale)
+    else:
+        o, lse = B.attn_fwd_lse(t["q"], t["k"], t["v"], causal=causal, scale=scale)
 
     def run():
         ws = torch.empty((4, Bn, H, N), dtype=torch.float32, device="cuda")
-        out = B.attn_bwd_bwd(t["q"], t["k"], t["v"], o, t["do"], lse, t["gq"], t["gk"],
-                             t["gv"], causal=causal, scale=scale, workspace=ws)
+        args = (t["q"], t["k"], t["v"], o, t["do"], lse, t["gq"], t["gk"], t["gv"])
+        if masked:
+            out = B.attn_bwd_bwd_masked(*args, mask, causal=causal, scale=scale, workspace=ws)
+        else:
+            out = B.attn_bwd_bwd(*args, causal=causal, scale=scale, workspace=ws)
         return tuple(out) + (ws[2], ws[3])
 
     first = run()
