@@ -525,14 +525,44 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
   float nl2[NH];                               // -L log2 e of the lane's query, per half
   const bf16 one = (bf16)1.f, zero = (bf16)0.f;
   ones = h == 0 ? frag{one, one, zero, zero, zero, zero, zero, zero} : frag{};
-  // (Q, dO and the row scalars of the wave's rows are read once the walk's
-  // first two key tiles are on their way, below)
 
   f32x16 acc[NH][MT];
 #pragma unroll
   for (int c = 0; c < NH; ++c)
 #pragma unroll
     for (int i = 0; i < MT; ++i) { acc[c][i] = zero16(); pin_agpr(acc[c][i]); }
+
+  using FS = AsyncFillShape<BKV, D, NW>;
+  unsigned copy_off[FS::PER];
+  async_fill_plan<BKV, D, NW>(copy_off, rs, wave, lane);
+  // 64 of the block's own rows (of Q or dO, from row r0) into an LDS tile,
+  // the same way
+  auto fill_rows = [&](bf16* t, const bf16* src, int r0) ATTN_INLINE {
+    if (r0 + BKV <= N) async_fill_untracked<BKV, D, NW>(KT{t}, src + base + r0 * rs, copy_off, wave);
+    else fill_sync<bf16, BKV, D, NT>(KT{t}, src + base, rs, r0, N, d, tid);
+  };
+  // The block's Q and dO rows reach the waves' registers through LDS, by
+  // whole-row copies (a lane loading its own row would touch 32 rows per
+  // instruction), in two rounds since the three tile buffers hold 384 rows:
+  // first Q (buf0, buf1) and dO rows 0..127 (buf2), then dO rows 128..255
+  // (buf2) beside the walk's first two key tiles (buf0, buf1).  Each buffer
+  // holds 128 rows as its k and v tiles; wave w's 64 rows are tile w % 2 of
+  // buffer w / 2 (Q) and of buf2 (dO, round w / 2 + 1).
+  static_assert(NW == 4 && WQ == BKV, "two waves' rows per buffer");
+  fill_rows(buf0.k, Q, qb);
+  fill_rows(buf0.v, Q, qb + 64);
+  fill_rows(buf1.k, Q, qb + 128);
+  fill_rows(buf1.v, Q, qb + 192);
+  fill_rows(buf2.k, dO, qb);
+  fill_rows(buf2.v, dO, qb + 64);
+  float dq[NH];
+#pragma unroll
+  for (int c = 0; c < NH; ++c) {
+    const int q = qw + 32 * c + l32;
+    // padded rows (q >= N) and rows with no kept key (stored -inf): P = 0
+    nl2[c] = q < N ? Lh[q] : -__builtin_inff();
+    dq[c] = q < N ? Dh[q] : 0.f;
+  }
 
   const int kv_end = CAUSAL ? min(N, qb + BQ) : N;
   const int ntiles_all = (kv_end + BKV - 1) / BKV;
@@ -571,9 +601,6 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
   // A key tile (K and V rows) into LDS: whole tiles by direct copies (2 * PER
   // instructions per wave), the sequence's ragged last tile by the register
   // path with zero padding.
-  using FS = AsyncFillShape<BKV, D, NW>;
-  unsigned copy_off[FS::PER];
-  async_fill_plan<BKV, D, NW>(copy_off, rs, wave, lane);
   auto fill = [&](Buf& B, int kt) ATTN_INLINE {
     const int k0 = kt * BKV;
     if (k0 + BKV <= N) {
@@ -756,24 +783,52 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
 #pragma unroll
   for (int i = 0; i < 2 * MT; ++i) tf[i] = frag{};
   bds1[0] = bds1[1] = frag{};
+  // round 1 landed (every wave's copies): Q for all waves, dO for waves 0, 1
+  wait_async_fills();
+  lds_barrier();
+  {
+    const Buf& qb_buf = wave < 2 ? buf0 : buf1;
+    const bf16* qt = (wave & 1) ? qb_buf.v : qb_buf.k;
+    const bf16* ot = (wave & 1) ? buf2.v : buf2.k;
+#pragma unroll
+    for (int c = 0; c < NH; ++c)
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        qf[c][kk] = plan.cols(qt, 32 * c, kk);
+        if (wave < 2) of[c][kk] = plan.cols(ot, 32 * c, kk);
+      }
+  }
+  lds_barrier();                               // buf0..2 free again
+  // round 2: dO rows 128..255, then the walk's first two tiles
+  fill_rows(buf2.k, dO, qb + 128);
+  fill_rows(buf2.v, dO, qb + 192);
   if (ntiles > 0) fill(buf0, tile_at(0));       // a sparse walk may visit nothing
   if (ntiles > 1) fill(buf1, tile_at(1));
-  // the wave's own rows, while those copies fly
+  // dO has landed once at most the 2 PER copies of a tile issued after it are
+  // in flight (a ragged first tile went by the register path, whose loads
+  // were waited for in order after it)
+  if (ntiles > 0) wait_async_fills_but<2 * FS::PER>();
+  else wait_async_fills();
+  lds_barrier();
+  {
+    const bf16* ot = (wave & 1) ? buf2.v : buf2.k;
+#pragma unroll
+    for (int c = 0; c < NH; ++c)
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk)
+        if (wave >= 2) of[c][kk] = plan.cols(ot, 32 * c, kk);
+  }
+  // (the first step's barrier frees buf2, which its copies of tile 2 fill,
+  // from these reads)
 #pragma unroll
   for (int c = 0; c < NH; ++c) {
-    const int q = qw + 32 * c + l32;
-    load_row_frags<bf16, D>(qf[c], Q + base, rs, q, N, d, h);
-    load_row_frags<bf16, D>(of[c], dO + base, rs, q, N, d, h);
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       pin_agpr(qf[c][kk]);
       pin_agpr(of[c][kk]);
     }
-    // padded rows (q >= N) and rows with no kept key (stored -inf): P = 0
-    nl2[c] = q < N ? Lh[q] : -__builtin_inff();
-    const float dq = q < N ? Dh[q] : 0.f;
-    const bf16 dhi = (bf16)dq;
-    const bf16 dlo = (bf16)(dq - (float)dhi);
+    const bf16 dhi = (bf16)dq[c];
+    const bf16 dlo = (bf16)(dq[c] - (float)dhi);
     bd[c] = h == 0 ? frag{dhi, dlo, zero, zero, zero, zero, zero, zero} : frag{};
   }
   int kt = 0;
