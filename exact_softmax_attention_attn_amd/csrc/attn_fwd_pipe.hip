@@ -111,13 +111,7 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_pipe_kernel(
   const int qb = ib * BQ;
   const int qw = qb + wave * WQ;               // this wave's first query row
   const LanePlan<D> plan(lane);
-  frag qf[NH][KS];
-#pragma unroll
-  for (int c = 0; c < NH; ++c) {
-    load_row_frags<bf16, D>(qf[c], Q + base, rs, qw + 32 * c + l32, N, d, h);
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) pin_agpr(qf[c][kk]);
-  }
+  frag qf[NH][KS];                             // read from LDS in the prologue
   f32x16 acc[NH][MT];
 #pragma unroll
   for (int c = 0; c < NH; ++c)
@@ -248,18 +242,44 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_pipe_kernel(
     lsum[c] += sum_pair(frag_sum(bp[c][1], frag_sum(bp[c][0], 0.f)));
   };
 
-  // ---- prologue: tiles 0 and 1 in flight; S_0, m = its row max (at least
-  // -1e30, so a row whose first keys are all masked stays finite)
+  // ---- prologue.  The block's 256 Q rows reach the waves' registers
+  // through LDS by whole-row copies (a lane loading its own row would touch
+  // 32 rows per instruction): rows 0..127 into buf1, 128..255 into buf2 (each
+  // buffer's k and v tiles hold 64 rows), beside tile 0 into buf0; tile 1
+  // goes to buf1 once the waves have read their rows.  Then S_0, m = its row
+  // max (at least -1e30, so a row whose first keys are all masked stays
+  // finite).
 #pragma unroll
   for (int c = 0; c < NH; ++c) { m[c] = -1e30f; lsum[c] = 0.f; }
-  if (ntiles > 0) {                             // a sparse walk may visit nothing
+  {
+    auto fill_rows = [&](bf16* t, int r0) ATTN_INLINE {
+      if (r0 + BKV <= N) async_fill_untracked<BKV, D, NW>(KT{t}, Q + base + r0 * rs, copy_off, wave);
+      else fill_sync<bf16, BKV, D, NT>(KT{t}, Q + base, rs, r0, N, d, tid);
+    };
+    fill_rows(buf1.k, qb);
+    fill_rows(buf1.v, qb + 64);
+    fill_rows(buf2.k, qb + 128);
+    fill_rows(buf2.v, qb + 192);
+    if (ntiles > 0) fill(buf0, tile_at(0));     // a sparse walk may visit nothing
+    wait_async_fills();
+    lds_barrier();
+#pragma unroll
+    for (int c = 0; c < NH; ++c) {
+      const int r = wave * WQ + 32 * c;         // the half's first row in the block
+      const Buf& qbuf = r < 128 ? buf1 : buf2;
+      const bf16* qt = (r & 64) ? qbuf.v : qbuf.k;
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) qf[c][kk] = plan.cols(qt, r & 63, kk);
+    }
+#pragma unroll
+    for (int c = 0; c < NH; ++c)
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) pin_agpr(qf[c][kk]);
+    lds_barrier();                              // buf1 and buf2 free again
+  }
+  if (ntiles > 0) {
     const int t0 = tile_at(0);
-    const int t1 = ntiles > 1 ? tile_at(1) : 0;
-    fill(buf0, t0);
-    if (ntiles > 1) fill(buf1, t1);
-    if (ntiles > 1 && (t1 + 1) * BKV <= N) wait_async_fills_but<2 * FS::PER>();   // tile 1 may fly
-    else wait_async_fills();
-    __syncthreads();
+    if (ntiles > 1) fill(buf1, tile_at(1));     // lands during sub-tile 0
     s_chain(buf0, 0, sc, [&](int) ATTN_INLINE {});
     const bool kill0 = kill_at(0);
     if (needs_mask(t0 * BKV, kill0)) mask_sub(sc, t0 * BKV, kill0);
@@ -394,12 +414,16 @@ __global__ __launch_bounds__(NW * 64, 1) void fwd_bf16_pipe_kernel(
   if (t + 1 < ntiles) tile(t + 1, buf1, buf2, buf0);
 
   mma_acc_drain(acc);
+  // every wave is done with the key tiles: O leaves through LDS, whole rows
+  // per store, three waves' staging areas per buffer
+  static_assert(3 * RowStage<D>::BYTES <= sizeof(Buf) && NW <= 9, "staging area");
+  lds_barrier();
+  bf16* stage = reinterpret_cast<bf16*>(wave < 3 ? &buf0 : wave < 6 ? &buf1 : &buf2) +
+                (wave % 3) * (RowStage<D>::BYTES / 2);
 #pragma unroll
   for (int c = 0; c < NH; ++c) {
     const float inv = lsum[c] > 0.f ? 1.f / lsum[c] : 0.f;   // no kept key: O = 0
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-      store_acc_transposed<bf16>(acc[c][mt], O + base, rs, qw + 32 * c, mt * 32, N, d, inv, lane);
+    store_rows_via_lds<D>(acc[c], O + base, rs, qw + 32 * c, N, inv, stage, lane);
     const int q = qw + 32 * c + l32;
     if (h == 0 && q < N)
       Lout[((long)b * H + head) * N + q] =

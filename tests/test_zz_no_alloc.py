@@ -85,3 +85,29 @@ def test_noalloc_rejects_a_workspace_beyond_its_array(B):
     st = lib.attn_bwd_noalloc(*p, 1, 1, 2097153, 8, 1, 0.5, 0, ctypes.c_void_p(0))
     assert st == B.ATTN_ERR_UNSUPPORTED
     assert b"exceeds" in lib.attn_last_error()
+
+
+def test_noalloc_replays_under_graph_capture(B):
+    """The callers it is for: a HIP graph captures the allocation-free call
+    once and replays it; each replay, with eager work and synchronisation in
+    between, must give attn_bwd's dQ, dK, dV bit for bit."""
+    import torch
+    shape = (1, 4, 700, 128, "bf16", True)
+    _say(f"graph capture {shape}")
+    (q, k, v, o, do, lse, scale), ref, outs = _case(B, *shape)
+    # the first call on a device finds the array's address; it runs outside the capture
+    B.attn_bwd_noalloc(q, k, v, o, do, lse, *outs, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        B.attn_bwd_noalloc(q, k, v, o, do, lse, *outs, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    for i in range(3):
+        for t in outs:
+            t.fill_(float("nan"))                  # eager work between the replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, a, r in zip(("dQ", "dK", "dV"), outs, ref):
+            assert torch.equal(a.view(torch.int16), r.view(torch.int16)), (i, name)
+    del g
