@@ -294,3 +294,49 @@ def test_c5_variants_sampled_against_oracle(B, name):
     sdk = dk.double().sum(dim=1).cpu().numpy()
     adk = dk.double().abs().sum(dim=1).cpu().numpy()
     assert np.all(np.abs(sdk) <= TOL["bf16"] * adk + 1e-6)
+
+
+@pytest.mark.parametrize("recipe", ["causal", "window"])
+def test_longest_sequence_sampled_against_oracle(B, recipe):
+    """N = 65,536 (the longest a block-masked call takes: 1,024 tiles of 64
+    rows per visit list), one head of d = 64, bf16: sampled rows and columns
+    against the oracle, plus the sum rules.  Under the window mask (16 blocks
+    and the first block) key block 0 is kept by every query block, so its dK/dV
+    walk fills the visit list to exactly its 1,024 entries."""
+    import torch
+    N, d = 65536, 64
+    scale = 1.0 / math.sqrt(d)
+    _say(f"N={N} {recipe} inputs")
+    x = workloads.make_random(1, 1, N, d, "bf16", seed=17, qkv_std=0.5)
+    q, k, v, do = (_dev(x[n], "bf16") for n in ("q", "k", "v", "do"))
+    bm = workloads.window_block_mask(N, 16, 1) if recipe == "window" else None
+    _say(f"N={N} {recipe} forward + backward on the GPU")
+    if bm is None:
+        o, lse = B.attn_fwd_lse(q, k, v, causal=True, scale=scale)
+        dq, dk, dv = B.attn_bwd(q, k, v, o, do, lse, causal=True, scale=scale)
+    else:
+        assert int(bm[:, 0].sum()) * 2 == 1024          # key block 0's walk: 1,024 tiles
+        mask = torch.from_numpy(bm).cuda()
+        o, lse = B.attn_fwd_lse_masked(q, k, v, mask, causal=True, scale=scale)
+        dq, dk, dv = B.attn_bwd_masked(q, k, v, o, do, lse, mask, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(9)
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 32767, 32768, N - 2, N - 1],
+                                     rng.integers(0, N, 24)]))
+    cols = np.unique(np.concatenate([[0, 1, 127, 128, 32767, 65407, N - 1],
+                                     rng.integers(0, N, 24)]))
+    _say(f"N={N} {recipe} oracle sample")
+    s = orc.attn_bwd_sampled(x["q"], x["k"], x["v"], x["do"], scale, True, 0, 0, rows, cols,
+                             row_block=1024, block_mask=bm)
+    got = {"dQ": dq[0, rows, 0].float().cpu().numpy(), "O": o[0, rows, 0].float().cpu().numpy(),
+           "dK": dk[0, cols, 0].float().cpu().numpy(), "dV": dv[0, cols, 0].float().cpu().numpy()}
+    g = {n: a[None, :, None, :] for n, a in got.items()}
+    r = {n: s[n][None, :, None, :] for n in got}
+    g["L"], r["L"] = lse[0, 0].cpu().numpy()[None, None, :], s["L"][None, None, :]
+    gpu_check.check(f"N={N} {recipe} sampled", g, r, "bf16")
+    sdv = dv.double().sum(dim=1).cpu().numpy()
+    sdo = do.double().sum(dim=1).cpu().numpy()
+    assert rel_fro(sdv, sdo) <= TOL["bf16"]
+    sdk = dk.double().sum(dim=1).cpu().numpy()
+    adk = dk.double().abs().sum(dim=1).cpu().numpy()
+    assert np.all(np.abs(sdk) <= TOL["bf16"] * adk + 1e-6)
