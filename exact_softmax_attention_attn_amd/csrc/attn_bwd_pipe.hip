@@ -535,8 +535,9 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
   using FS = AsyncFillShape<BKV, D, NW>;
   unsigned copy_off[FS::PER];
   async_fill_plan<BKV, D, NW>(copy_off, rs, wave, lane);
-  // 64 of the block's own rows (of Q or dO, from row r0) into an LDS tile,
-  // the same way
+  // 64 of the block's own rows (of Q or dO, from row r0) into an LDS tile:
+  // direct copies (PER instructions per wave), or, for the sequence's ragged
+  // end, the register path with zero rows
   auto fill_rows = [&](bf16* t, const bf16* src, int r0) ATTN_INLINE {
     if (r0 + BKV <= N) async_fill_untracked<BKV, D, NW>(KT{t}, src + base + r0 * rs, copy_off, wave);
     else fill_sync<bf16, BKV, D, NT>(KT{t}, src + base, rs, r0, N, d, tid);
