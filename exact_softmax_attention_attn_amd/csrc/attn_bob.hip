@@ -40,8 +40,19 @@ template <bool B> using bool_c = std::integral_constant<bool, B>;
 // registers as B operands, so S^T, dP^T, G^T, A^T come out with key rows along
 // the registers and one query per lane (two lanes, l and l + 32, per query).
 // ---------------------------------------------------------------------------
+// Key rows per streamed tile: pass 1 at D = 128 (bf16) takes 32, so that its
+// two 4-operand buffers (64 KB) leave LDS for a second workgroup on the CU,
+// whose products and VALU work overlap this one's (pass 1 reduces into two
+// scalars per row and fits two waves per SIMD); elsewhere 64.
+template <typename T, int D, int PASS> constexpr int bob_q_tile_rows() {
+  return (PASS == 1 && D == 128 && sizeof(T) == 2) ? 32 : 64;
+}
+template <typename T, int D, int PASS> constexpr int bob_q_min_blocks() {
+  return bob_q_tile_rows<T, D, PASS>() == 32 ? 2 : 1;
+}
+
 template <typename T, int D, bool CAUSAL, int PASS>
-__global__ __launch_bounds__(256, 1) void bob_q_kernel(
+__global__ __launch_bounds__(256, (bob_q_min_blocks<T, D, PASS>())) void bob_q_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ dO, const T* __restrict__ gQ, const T* __restrict__ gK,
     const T* __restrict__ gV, float* __restrict__ ws, T* __restrict__ hQ, T* __restrict__ hdO,
@@ -49,7 +60,9 @@ __global__ __launch_bounds__(256, 1) void bob_q_kernel(
     int mask_heads) {
   using M = Mma<T>;
   using frag = typename M::frag;
-  constexpr int BQ = 128, BKV = 64, KS = D / M::K, MT = D / 32, RS = 32 / M::K;
+  constexpr int BQ = 128, BKV = bob_q_tile_rows<T, D, PASS>(), KS = D / M::K, MT = D / 32,
+                RS = 32 / M::K;
+  constexpr int VT = 64, SUB = VT / BKV;     // visit-list tiles: 64 rows, SUB walk tiles each
   using KT = Tile<T, BKV, D>;
   struct __align__(16) Buf {
     T k[KT::ELEMS];
@@ -92,23 +105,25 @@ __global__ __launch_bounds__(256, 1) void bob_q_kernel(
   for (int i = 0; i < (PASS == 2 ? MT : 1); ++i) { acc_q[i] = zero16(); acc_o[i] = zero16(); }
 
   const int kv_end = CAUSAL ? min(N, qb + BQ) : N;
-  const int nkt = (kv_end + BKV - 1) / BKV;
-  // the walk: key tiles 0 .. nkt - 1, or (block mask) the ones whose mask
-  // block (row ib: the workgroup's 128 query rows are one mask row, column of
-  // the tile) is kept
+  // the walk: key tiles 0 .. ceil(kv_end / BKV) - 1, or (block mask) those in
+  // the kept 64-row tiles, a 64-row tile being kept when its mask block (row
+  // ib: the workgroup's 128 query rows are one mask row) is
   static_assert(BQ == kMaskBlock, "one mask row per workgroup");
   __shared__ unsigned short vis[kMaxVisit];
   __shared__ int nvis;
-  int ntiles = nkt;
+  int ntiles = (kv_end + BKV - 1) / BKV;
   if (mask) {
     const int nb = (N + kMaskBlock - 1) / kMaskBlock;
     const unsigned char* mk = head_mask(mask, mask_heads, b, head, H, nb);
-    ntiles = build_visits(vis, &nvis, nkt, [&](int t) ATTN_INLINE -> unsigned {
-      return mk[ib * nb + t * BKV / kMaskBlock] ? (1u << 14) | (unsigned)t : 0u;
+    const int nvt = (kv_end + VT - 1) / VT;
+    ntiles = SUB * build_visits(vis, &nvis, nvt, [&](int t) ATTN_INLINE -> unsigned {
+      return mk[ib * nb + t * VT / kMaskBlock] ? (1u << 14) | (unsigned)t : 0u;
     });
   }
+  // (masked, SUB = 2: the second half of a kept tile may lie past kv_end; its
+  // rows read as zeros and every pair in it is masked, so it adds nothing)
   auto tile_at = [&](int p) ATTN_INLINE -> int {
-    return mask ? (int)(visit_entry(vis, p) & kVisitTile) : p;
+    return mask ? SUB * (int)(visit_entry(vis, p / SUB) & kVisitTile) + p % SUB : p;
   };
 
   auto fill = [&](Buf& B, int kt) ATTN_INLINE {
@@ -134,6 +149,9 @@ __global__ __launch_bounds__(256, 1) void bob_q_kernel(
   // products (0 * inf)
   const int klim = CAUSAL ? q : N - 1;              // last kept key of the lane's query
   const int wlim = CAUSAL ? qw + 31 : N - 1;        // ... of any query of the wave
+  // LDS operands are read ahead of the products that take them: two K steps
+  // ahead in the first chain, one fenced group ahead after it, so each
+  // group's reads are in flight while the previous group's products run.
   auto body = [&](const Buf& B, int k0, bool masked) ATTN_INLINE {
     const KT kt_{const_cast<T*>(B.k)}, vt_{const_cast<T*>(B.v)};
     const KT gkt_{const_cast<T*>(B.gk)}, gvt_{const_cast<T*>(B.gv)};
@@ -141,23 +159,50 @@ __global__ __launch_bounds__(256, 1) void bob_q_kernel(
     for (int st = 0; st < BKV / 32; ++st) {
       const int ka = k0 + st * 32;
       if (masked && ka > wlim) continue;             // every pair masked
-      f32x16 s = zero16(), dp = zero16(), g = zero16(), a = zero16();
+      const int rr = st * 32 + l32;
+      // the hQ / hdO products of group i = (K step i / MT, columns i % MT)
+      struct Ops { frag k, gk, gv, v; };
+      auto rd = [&](int i) ATTN_INLINE -> Ops {
+        const int ss = i / MT, c = (i % MT) * 32 + l32;
+        return {kt_.along_rows(c, st * 32, ss, h), gkt_.along_rows(c, st * 32, ss, h),
+                gvt_.along_rows(c, st * 32, ss, h), vt_.along_rows(c, st * 32, ss, h)};
+      };
+      Ops nx;
+      // every register of a lane holds the lane's query, so its row scalars
+      // start the accumulators: dP - D, and (pass 2) A - E
+      f32x16 s = zero16(), g = zero16();
+      f32x16 dp = PASS == 2 ? splat16(Dq) : zero16(), a = PASS == 2 ? splat16(-eq) : zero16();
+      frag kc[KS], ngk, nv, ngv;
+      kc[0] = kt_.along_cols(rr, 0, h);
+      if constexpr (KS > 1) kc[1] = kt_.along_cols(rr, 1, h);
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
-        const frag kc = kt_.along_cols(st * 32 + l32, kk, h);
-        s = M::mma(kc, qf[kk], s);
-        g = M::mma(kc, gqf[kk], g);
+        if (kk + 2 < KS) kc[kk + 2] = kt_.along_cols(rr, kk + 2, h);
+        if (kk == KS - 1) {
+          ngk = gkt_.along_cols(rr, 0, h);
+          nv = vt_.along_cols(rr, 0, h);
+          ngv = gvt_.along_cols(rr, 0, h);
+        }
+        s = M::mma(kc[kk], qf[kk], s);
+        g = M::mma(kc[kk], gqf[kk], g);
+        __builtin_amdgcn_sched_barrier(0);
       }
       // register r = key row ka + acc_row(r, h), column = query row q.  S is
       // complete here: P = exp2(S scale log2 e - L2) is formed beside the G,
       // dP and A products (scheduling fences keep the interleave).
-      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
-        g = M::mma(gkt_.along_cols(st * 32 + l32, kk, h), qf[kk], g);
-        const frag vc = vt_.along_cols(st * 32 + l32, kk, h);
-        dp = M::mma(vc, of[kk], dp);
-        a = M::mma(gvt_.along_cols(st * 32 + l32, kk, h), of[kk], a);
+        const frag cgk = ngk, cv = nv, cgv = ngv;
+        if (kk + 1 < KS) {
+          ngk = gkt_.along_cols(rr, kk + 1, h);
+          nv = vt_.along_cols(rr, kk + 1, h);
+          ngv = gvt_.along_cols(rr, kk + 1, h);
+        } else if constexpr (PASS == 2) {
+          nx = rd(0);
+        }
+        g = M::mma(cgk, qf[kk], g);
+        dp = M::mma(cv, of[kk], dp);
+        a = M::mma(cgv, of[kk], a);
 #pragma unroll
         for (int r = 16 * kk / KS; r < 16 * (kk + 1) / KS; ++r) {
           float p = fast_exp2(__builtin_fmaf(s[r], scale_log2, Lq));
@@ -168,17 +213,17 @@ __global__ __launch_bounds__(256, 1) void bob_q_kernel(
       }
       auto elem = [&](int r) ATTN_INLINE {
         const float p = s[r];
-        const float dpd = dp[r] + Dq;                 // dP - D
-        const float gg = g[r] * scale;                // G
+        const float dpd = PASS == 2 ? dp[r] : dp[r] + Dq;   // dP - D
         if constexpr (PASS == 1) {
-          racc += p * gg;
-          eacc += p * a[r] + p * dpd * gg;
+          const float gg = g[r] * scale;              // G
+          racc = __builtin_fmaf(p, gg, racc);
+          eacc = __builtin_fmaf(p, __builtin_fmaf(dpd, gg, a[r]), eacc);
         } else {
-          const float w = p * (gg - rq);
-          s[r] = p;                                     // P
-          dp[r] = p * dpd;                              // dS
-          g[r] = p * (a[r] + dpd * (gg - rq) - eq);     // dS2
-          a[r] = w;                                     // W
+          const float t = __builtin_fmaf(g[r], scale, -rq);   // G - r
+          s[r] = p;                                           // P
+          dp[r] = p * dpd;                                    // dS
+          g[r] = p * __builtin_fmaf(dpd, t, a[r]);            // dS2 (a = A - E)
+          a[r] = p * t;                                       // W
         }
       };
       if constexpr (PASS == 1) {
@@ -196,11 +241,14 @@ __global__ __launch_bounds__(256, 1) void bob_q_kernel(
           bw[ss] = M::pack(a, ss);
         };
         // hQ^T += K^T dS2^T + gK^T dS^T;  hdO^T += gV^T P^T + V^T W^T
-        auto prods = [&](int ss, int mt) ATTN_INLINE {
-          acc_q[mt] = M::mma(kt_.along_rows(mt * 32 + l32, st * 32, ss, h), bds2[ss], acc_q[mt]);
-          acc_q[mt] = M::mma(gkt_.along_rows(mt * 32 + l32, st * 32, ss, h), bds[ss], acc_q[mt]);
-          acc_o[mt] = M::mma(gvt_.along_rows(mt * 32 + l32, st * 32, ss, h), bp[ss], acc_o[mt]);
-          acc_o[mt] = M::mma(vt_.along_rows(mt * 32 + l32, st * 32, ss, h), bw[ss], acc_o[mt]);
+        auto prods = [&](int i) ATTN_INLINE {
+          const Ops o = nx;
+          if (i + 1 < 2 * NG) nx = rd(i + 1);
+          const int ss = i / MT, mt = i % MT;
+          acc_q[mt] = M::mma(o.k, bds2[ss], acc_q[mt]);
+          acc_q[mt] = M::mma(o.gk, bds[ss], acc_q[mt]);
+          acc_o[mt] = M::mma(o.gv, bp[ss], acc_o[mt]);
+          acc_o[mt] = M::mma(o.v, bw[ss], acc_o[mt]);
         };
 #pragma unroll
         for (int r = 0; r < 8; ++r) elem(r);
@@ -209,7 +257,7 @@ __global__ __launch_bounds__(256, 1) void bob_q_kernel(
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < NG; ++i) {
-          prods(i / MT, i % MT);
+          prods(i);
 #pragma unroll
           for (int r = 8 + 8 * i / NG; r < 8 + 8 * (i + 1) / NG; ++r) elem(r);
           __builtin_amdgcn_sched_barrier(0);
@@ -218,7 +266,10 @@ __global__ __launch_bounds__(256, 1) void bob_q_kernel(
         for (int ss = HS; ss < RS; ++ss) pack(ss);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < NG; ++i) prods(HS + i / MT, i % MT);
+        for (int i = NG; i < 2 * NG; ++i) {
+          prods(i);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
   };
@@ -365,7 +416,7 @@ __global__ __launch_bounds__(256, 1) void bob_kv_kernel(
     for (int st = 0; st < BQ / 32; ++st) {
       const int qa = q0 + st * 32;
       if (masked && qa + 31 < kv0) continue;       // every pair above the diagonal
-      f32x16 s = zero16(), dp = zero16(), g = zero16(), a = zero16();
+      f32x16 s = zero16(), g = zero16(), a = zero16();
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const frag qc = qt_.along_cols(st * 32 + l32, ks, h);
@@ -383,6 +434,9 @@ __global__ __launch_bounds__(256, 1) void bob_kv_kernel(
         rg[gi] = *reinterpret_cast<const f32x4*>(&B.r[i0]);
         eg[gi] = *reinterpret_cast<const f32x4*>(&B.e[i0]);
       }
+      f32x16 dp;                                    // starts at -D: dP - D
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dp[r] = dg[r / 4][r % 4];
       // S is complete here: P is formed beside the G, dP and A products
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -402,11 +456,11 @@ __global__ __launch_bounds__(256, 1) void bob_kv_kernel(
       auto elem = [&](int r) ATTN_INLINE {
         const int gi = r / 4, i = r % 4;
         const float p = s[r];
-        const float dpd = dp[r] + dg[gi][i];        // dP - D
-        const float gg = g[r] * scale;              // G
-        dp[r] = p * dpd;                            // dS
-        s[r] = p * (a[r] + dpd * (gg - rg[gi][i]) - eg[gi][i]);   // dS2
-        a[r] = p * (gg - rg[gi][i]);                // W
+        const float dpd = dp[r];                                  // dP - D
+        const float t = __builtin_fmaf(g[r], scale, -rg[gi][i]);  // G - r
+        dp[r] = p * dpd;                                          // dS
+        s[r] = p * (__builtin_fmaf(dpd, t, a[r]) - eg[gi][i]);    // dS2
+        a[r] = p * t;                                             // W
       };
       // The first half of the registers (K steps 0 .. RS/2 - 1) is packed
       // first; its products run while the VALU works on the second half.
