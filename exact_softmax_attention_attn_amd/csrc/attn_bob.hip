@@ -32,6 +32,13 @@ namespace attn {
 
 namespace {
 template <bool B> using bool_c = std::integral_constant<bool, B>;
+
+__device__ __forceinline__ f32x16 splat16(float v) {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = v;
+  return z;
+}
 }
 
 // ---------------------------------------------------------------------------

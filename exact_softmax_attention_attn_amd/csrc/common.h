@@ -41,13 +41,6 @@ __device__ __forceinline__ f32x16 zero16() {
   return z;
 }
 
-__device__ __forceinline__ f32x16 splat16(float v) {
-  f32x16 z;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) z[i] = v;
-  return z;
-}
-
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Keep a matrix-core operand that lives for the whole kernel in the
