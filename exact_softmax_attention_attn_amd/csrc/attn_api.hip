@@ -207,13 +207,28 @@ int attn_bwd_dq(const void* Q, const void* K, const void* V, const void* dO,
 }  // extern "C"
 
 namespace {
-// The three stages of attn_bwd on a validated call, with workspace ws.
+// The stages of attn_bwd on a validated call, with workspace ws (a block mask
+// optional).  Where the dQ kernel can do the preprocess for its own rows
+// (bf16, d 64 or 128), it runs first and fills ws, then dK/dV: two launches.
+// Otherwise preprocess, dK/dV, dQ.  Both orders leave the same bits in dQ,
+// dK, dV and ws.
 int run_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
             const float* L, void* dQ, void* dK, void* dV, float* ws, int B, int H, int N, int d,
-            int causal, float scale, int dtype, hipStream_t s) {
+            int causal, float scale, int dtype, hipStream_t s,
+            const unsigned char* mask = nullptr, int mask_heads = 1) {
+  attn::BwdArgs a = make_bwd(Q, K, V, dO, ws, dQ, dK, dV, B, H, N, d, causal, scale, dtype);
+  a.mask = mask;
+  a.mask_heads = mask_heads;
+  if (attn::bwd_dq_fuses_preprocess(a)) {
+    a.O = O;
+    a.L = L;
+    a.ws_out = ws;
+    hipError_t e = attn::launch_bwd_dq_fused(a, s);
+    if (e != hipSuccess) return finish(e);
+    return finish(attn::launch_bwd_dkdv(a, s));
+  }
   hipError_t e = attn::launch_bwd_preprocess(O, dO, L, ws, B, H, N, d, dtype, s);
   if (e != hipSuccess) return finish(e);
-  const attn::BwdArgs a = make_bwd(Q, K, V, dO, ws, dQ, dK, dV, B, H, N, d, causal, scale, dtype);
   e = attn::launch_bwd_dkdv(a, s);
   if (e != hipSuccess) return finish(e);
   return finish(attn::launch_bwd_dq(a, s));
@@ -280,17 +295,8 @@ int attn_bwd_masked(const void* Q, const void* K, const void* V, const void* O, 
   ATTN_TRY(check_scale_causal(scale, causal));
   ATTN_TRY(check_dtype_dim(H, d, dtype));
   ATTN_TRY(check_mask(mask, mask_heads, B, H, N));
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = attn::launch_bwd_preprocess(O, dO, L, static_cast<float*>(workspace), B, H, N,
-                                             d, dtype, s);
-  if (e != hipSuccess) return finish(e);
-  attn::BwdArgs a =
-      make_bwd(Q, K, V, dO, workspace, dQ, dK, dV, B, H, N, d, causal, scale, dtype);
-  a.mask = mask;
-  a.mask_heads = mask_heads;
-  e = attn::launch_bwd_dkdv(a, s);
-  if (e != hipSuccess) return finish(e);
-  return finish(attn::launch_bwd_dq(a, s));
+  return run_bwd(Q, K, V, O, dO, L, dQ, dK, dV, static_cast<float*>(workspace), B, H, N, d,
+                 causal, scale, dtype, static_cast<hipStream_t>(stream), mask, mask_heads);
 }
 
 int attn_bwd_dkdv_masked(const void* Q, const void* K, const void* V, const void* dO,

@@ -484,4 +484,10 @@ hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream) {
   ATTN_DISPATCH(dq_go, a, stream);
 }
 
+bool bwd_dq_fuses_preprocess(const BwdArgs& a) { return use_pipe(a); }
+hipError_t launch_bwd_dq_fused(const BwdArgs& a, hipStream_t stream) {
+  if (!use_pipe(a) || !a.O || !a.L || !a.ws_out) return hipErrorInvalidValue;
+  return launch_bwd_dq_fused_bf16_pipe(a, stream);
+}
+
 }  // namespace attn

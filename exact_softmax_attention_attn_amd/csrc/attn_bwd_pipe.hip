@@ -485,13 +485,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
 // one after the other, so each VALU stage sits beside a chain it does not feed.
 // Key tiles are copied two steps ahead into a ring of three separately named
 // LDS buffers.  No atomics.
+//
+// FUSE: the kernel also does the preprocess for its own rows -- D = rowsum(dO
+// o O) with the preprocess kernel's lanes and summation order (so the same
+// bits), and -L log2 e from the forward's L -- and writes both to the
+// workspace (ws: -D [B, H, N], then -L log2 e), where the dK/dV kernel that
+// runs after it reads them.  nL2 and nD are then unused; otherwise O, L and
+// ws are.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL, int WQ, int NW, bool SPARSE>
+template <int D, bool CAUSAL, int WQ, int NW, bool SPARSE, bool FUSE>
 __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ nL2, const float* __restrict__ nD,
     bf16* __restrict__ dQ, int H, int N, int d, float scale_log2, float scale,
-    const unsigned char* __restrict__ mask, int mask_heads) {
+    const unsigned char* __restrict__ mask, int mask_heads, const bf16* __restrict__ O,
+    const float* __restrict__ L, float* __restrict__ ws) {
   using M = Mma<bf16>;
   using frag = bf16x8;
   constexpr int NH = WQ / 32;                  // 32-row halves per wave
@@ -512,8 +520,9 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
   const int head = bo.head, b = bo.b;
   const long rs = (long)H * d;
   const long base = ((long)b * N * H + head) * d;
-  const float* Lh = nL2 + ((long)b * H + head) * N;   // -L * log2(e)
-  const float* Dh = nD + ((long)b * H + head) * N;    // -D
+  const long rbase = ((long)b * H + head) * N;        // the (b, h) slice of [B, H, N]
+  const float* Lh = FUSE ? L + rbase : nL2 + rbase;   // L (FUSE) or -L * log2(e)
+  const float* Dh = nD + rbase;                       // -D (unless FUSE)
 
   const int qb = ib * BQ;
   const int qw = qb + wave * WQ;               // this wave's first query row
@@ -556,13 +565,57 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
   fill_rows(buf1.v, Q, qb + 192);
   fill_rows(buf2.k, dO, qb);
   fill_rows(buf2.v, dO, qb + 64);
+  // -L log2 e as the preprocess forms it (a row with no kept key, L = -inf,
+  // gives -inf, so every P of it is 0)
+  auto neg_l2 = [](float l) ATTN_INLINE -> float {
+    return l == -__builtin_inff() ? -__builtin_inff() : -l * kLog2e;
+  };
+  // FUSE: -D and -L log2 e of the block's rows, kept here until the end,
+  // where they go to the workspace as two whole-block stores
+  __shared__ float sD[FUSE ? BQ : 1], sL2[FUSE ? BQ : 1];
+  if constexpr (FUSE) {
+    // the preprocess for rows qb .. qb + BQ - 1: 16 lanes per row, 16 rows per
+    // pass (the round-1 copies above are in flight meanwhile)
+    static_assert(NT == 256 && BQ % 16 == 0, "16 rows of 16 lanes per pass");
+    // (d = D <= 128: the preprocess's column loop is one chunk per lane)
+    static_assert(D <= 16 * 8, "one 8-column chunk per lane");
+    constexpr int NP = BQ / 16;
+    const int sub = tid & 15;
+    // every pass's loads first, from clamped (in-bounds) addresses, so they
+    // are in flight together; lanes past the row or the head dim count 0
+    bf16x8 xo[NP], xg[NP];
+    float lr[NP];
+#pragma unroll
+    for (int pass = 0; pass < NP; ++pass) {
+      const int n = min(qb + pass * 16 + (tid >> 4), N - 1);
+      const long at = base + (long)n * rs + min(sub * 8, D - 8);
+      xo[pass] = *reinterpret_cast<const bf16x8*>(O + at);
+      xg[pass] = *reinterpret_cast<const bf16x8*>(dO + at);
+      lr[pass] = Lh[n];
+    }
+#pragma unroll
+    for (int pass = 0; pass < NP; ++pass) {
+      const int rl = pass * 16 + (tid >> 4), n = qb + rl;
+      float acc = 0.f;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) acc += (float)xo[pass][t] * (float)xg[pass][t];
+      if (!(n < N && sub * 8 < D)) acc = 0.f;
+#pragma unroll
+      for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);
+      if (sub == 0) {
+        sD[rl] = n < N ? -acc : 0.f;
+        sL2[rl] = neg_l2(lr[pass]);
+      }
+    }
+  }
   float dq[NH];
 #pragma unroll
   for (int c = 0; c < NH; ++c) {
     const int q = qw + 32 * c + l32;
     // padded rows (q >= N) and rows with no kept key (stored -inf): P = 0
-    nl2[c] = q < N ? Lh[q] : -__builtin_inff();
-    dq[c] = q < N ? Dh[q] : 0.f;
+    if constexpr (FUSE) nl2[c] = q < N ? neg_l2(Lh[q]) : -__builtin_inff();
+    else nl2[c] = q < N ? Lh[q] : -__builtin_inff();
+    dq[c] = (!FUSE && q < N) ? Dh[q] : 0.f;    // FUSE: from sD once it is published
   }
 
   const int kv_end = CAUSAL ? min(N, qb + BQ) : N;
@@ -785,8 +838,13 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
   for (int i = 0; i < 2 * MT; ++i) tf[i] = frag{};
   bds1[0] = bds1[1] = frag{};
   // round 1 landed (every wave's copies): Q for all waves, dO for waves 0, 1
+  // (and, FUSE, every row's -D is in sD)
   wait_async_fills();
   lds_barrier();
+  if constexpr (FUSE) {
+#pragma unroll
+    for (int c = 0; c < NH; ++c) dq[c] = sD[wave * WQ + 32 * c + l32];
+  }
   {
     const Buf& qb_buf = wave < 2 ? buf0 : buf1;
     const bf16* qt = (wave & 1) ? qb_buf.v : qb_buf.k;
@@ -861,6 +919,12 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
 #pragma unroll
   for (int c = 0; c < NH; ++c)
     store_rows_via_lds<D>(acc[c], dQ + base, rs, qw + 32 * c, N, scale, stage, lane);
+  if constexpr (FUSE) {
+    if (tid < BQ && qb + tid < N) {
+      ws[rbase + qb + tid] = sD[tid];
+      ws[(long)gridDim.z * H * N + rbase + qb + tid] = sL2[tid];
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -888,20 +952,28 @@ static hipError_t dkdv_pipe_go(const BwdArgs& a, hipStream_t stream) {
 #ifndef ATTN_DQ_NW
 #define ATTN_DQ_NW 4
 #endif
-template <int D, bool C, bool S>
+template <int D, bool C, bool S, bool F>
 static hipError_t dq_pipe_run(const BwdArgs& a, hipStream_t stream) {
   constexpr int NW = ATTN_DQ_NW, WQ = 256 / NW;
   dim3 grid((a.N + 255) / 256, a.H, a.B);
-  hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, C, WQ, NW, S>), grid, dim3(NW * 64), 0, stream,
+  hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, C, WQ, NW, S, F>), grid, dim3(NW * 64), 0, stream,
                      static_cast<const bf16*>(a.Q), static_cast<const bf16*>(a.K),
                      static_cast<const bf16*>(a.V), static_cast<const bf16*>(a.dO),
-                     a.Dws + rows_of(a), a.Dws, static_cast<bf16*>(a.dQ), a.H, a.N, a.d,
-                     a.scale * kLog2e, a.scale, a.mask, a.mask_heads);
+                     F ? nullptr : a.Dws + rows_of(a), F ? nullptr : a.Dws,
+                     static_cast<bf16*>(a.dQ), a.H, a.N, a.d, a.scale * kLog2e, a.scale, a.mask,
+                     a.mask_heads, F ? static_cast<const bf16*>(a.O) : nullptr,
+                     F ? a.L : nullptr, F ? a.ws_out : nullptr);
   return hipGetLastError();
 }
 template <int D, bool C>
 static hipError_t dq_pipe_go(const BwdArgs& a, hipStream_t stream) {
-  return a.mask ? dq_pipe_run<D, C, true>(a, stream) : dq_pipe_run<D, C, false>(a, stream);
+  return a.mask ? dq_pipe_run<D, C, true, false>(a, stream)
+                : dq_pipe_run<D, C, false, false>(a, stream);
+}
+template <int D, bool C>
+static hipError_t dq_fused_pipe_go(const BwdArgs& a, hipStream_t stream) {
+  return a.mask ? dq_pipe_run<D, C, true, true>(a, stream)
+                : dq_pipe_run<D, C, false, true>(a, stream);
 }
 
 #define ATTN_PIPE_DISPATCH(FN, a, stream)                                  \
@@ -920,6 +992,9 @@ hipError_t launch_bwd_dkdv_bf16_pipe(const BwdArgs& a, hipStream_t stream) {
 }
 hipError_t launch_bwd_dq_bf16_pipe(const BwdArgs& a, hipStream_t stream) {
   ATTN_PIPE_DISPATCH(dq_pipe_go, a, stream);
+}
+hipError_t launch_bwd_dq_fused_bf16_pipe(const BwdArgs& a, hipStream_t stream) {
+  ATTN_PIPE_DISPATCH(dq_fused_pipe_go, a, stream);
 }
 
 }  // namespace attn

@@ -20,6 +20,11 @@ struct BwdArgs {
   int dtype;  // 0 = f32, 1 = bf16
   const unsigned char* mask = nullptr;   // block-sparse mask, or nullptr (every block kept)
   int mask_heads = 1;
+  // dQ with the preprocess fused in (launch_bwd_dq_fused) only: the forward's
+  // O and L, and the workspace (Dws) writable, which it fills
+  const void* O = nullptr;
+  const float* L = nullptr;
+  float* ws_out = nullptr;
 };
 
 struct FwdArgs {
@@ -88,6 +93,12 @@ hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_lse(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dkdv_bf16_pipe(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dq_bf16_pipe(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_dq_fused_bf16_pipe(const BwdArgs& a, hipStream_t stream);
+// Whether launch_bwd_dq_fused serves these arguments (bf16, d 64 or 128); if
+// so, it does the preprocess for dQ's own rows and writes the workspace, and
+// launch_bwd_dkdv may follow it with no preprocess launch.
+bool bwd_dq_fuses_preprocess(const BwdArgs& a);
+hipError_t launch_bwd_dq_fused(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_lse_bf16_pipe(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_bwd(const BobArgs& a, hipStream_t stream);
 

@@ -91,8 +91,11 @@ int attn_fwd_lse(const void* Q, const void* K, const void* V, void* O, float* L,
 size_t attn_bwd_workspace_bytes(int B, int H, int N, int d);
 
 /*
- * Backward pass by score recomputation: the three stages below, in order, on
- * one stream.
+ * Backward pass by score recomputation, on one stream: the three stages below
+ * in order (preprocess, dK/dV, dQ), or, for bf16 with d = 64 or 128, two
+ * launches -- dQ first, doing the preprocess's arithmetic for its own rows and
+ * writing -D and -L * log2(e) to the workspace, then dK/dV.  Both orders give
+ * the same bits in dQ, dK, dV and the workspace.
  *   in : Q, K, V, O, dO [B, N, H, d] (dtype); L [B, H, N] float32 as written
  *        by attn_fwd_lse (or any L_i = log sum_j exp(S_ij) of the same kept set)
  *   out: dQ, dK, dV     [B, N, H, d] (dtype)
@@ -109,7 +112,7 @@ int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const v
 /*
  * attn_bwd for callers that cannot allocate device memory -- code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc: the
- * same three stages and kernels, with the workspace taken from an array the
+ * same launches and kernels, with the workspace taken from an array the
  * library holds in each GPU's memory (ATTN_NOALLOC_MAX_BYTES per GPU, from
  * the first call on that GPU until the process ends) instead of an argument.
  * The call allocates nothing.
@@ -119,8 +122,8 @@ int attn_bwd(const void* Q, const void* K, const void* V, const void* O, const v
  *   return ATTN_ERR_UNSUPPORTED before any HIP call, with the reason in
  *   attn_last_error().
  *   Sharing: every call on one GPU uses that GPU's one array, which keeps the
- *   last call's contents (nothing in it needs clearing: the first stage
- *   overwrites all it later reads).  Calls that overlap on one GPU -- on
+ *   last call's contents (nothing in it needs clearing: the first launch
+ *   overwrites all that the later ones read).  Calls that overlap on one GPU -- on
  *   different streams, or from different threads without ordering -- race on
  *   it; calls on different GPUs do not.  The current device must be the one
  *   the pointers and the stream belong to.
@@ -187,7 +190,7 @@ int attn_fwd_lse_masked(const void* Q, const void* K, const void* V, void* O, fl
                         int B, int H, int N, int d, int causal, float scale, int dtype,
                         void* stream);
 
-/* attn_bwd restricted to the pairs a block mask keeps (same three stages;
+/* attn_bwd restricted to the pairs a block mask keeps (the same launches;
  * the preprocess is the same, dK/dV and dQ walk only kept tiles). */
 int attn_bwd_masked(const void* Q, const void* K, const void* V, const void* O, const void* dO,
                     const float* L, void* dQ, void* dK, void* dV, void* workspace,
