@@ -46,10 +46,8 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(const T* __restrict
     const T* g = dO + row * d;
     for (int c = sub * VEC; c < d; c += 16 * VEC) {
       if constexpr (sizeof(T) == 2) {
-        bf16x8 a = *reinterpret_cast<const bf16x8*>(o + c);
-        bf16x8 b = *reinterpret_cast<const bf16x8*>(g + c);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) acc += (float)a[t] * (float)b[t];
+        acc = dot8_bf16(*reinterpret_cast<const bf16x8*>(o + c),
+                        *reinterpret_cast<const bf16x8*>(g + c), acc);
       } else {
         f32x4 a = *reinterpret_cast<const f32x4*>(o + c);
         f32x4 b = *reinterpret_cast<const f32x4*>(g + c);

@@ -596,9 +596,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
 #pragma unroll
     for (int pass = 0; pass < NP; ++pass) {
       const int rl = pass * 16 + (tid >> 4), n = qb + rl;
-      float acc = 0.f;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) acc += (float)xo[pass][t] * (float)xg[pass][t];
+      float acc = dot8_bf16(xo[pass], xg[pass], 0.f);
       if (!(n < N && sub * 8 < D)) acc = 0.f;
 #pragma unroll
       for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);

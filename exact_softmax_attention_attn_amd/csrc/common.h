@@ -43,6 +43,19 @@ __device__ __forceinline__ f32x16 zero16() {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// acc + sum_t x[t] y[t] over one 8-element bf16 chunk, as four two-element
+// dot products (the products are exact in float32).  The preprocess kernel
+// and the dQ kernel's folded preprocess both form D with it, so they leave
+// the same bits.
+typedef __bf16 bf16pair __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot8_bf16(const bf16x8& x, const bf16x8& y, float acc) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    acc = __builtin_amdgcn_fdot2_f32_bf16(bf16pair{x[2 * i], x[2 * i + 1]},
+                                          bf16pair{y[2 * i], y[2 * i + 1]}, acc, false);
+  return acc;
+}
+
 // Keep a matrix-core operand that lives for the whole kernel in the
 // accumulation register file: the MFMA reads A/B operands from AGPRs directly,
 // and the architectural VGPRs stay free for the per-tile working set.
