@@ -139,14 +139,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     return mask ? (int)(visit_entry(vis, p) & kVisitTile) : qt0 + p;
   };
 
+  // bf16 whole tiles: direct copies by a plan built once per workgroup (the
+  // tile base in scalar registers, a 32-bit offset per lane and copy), waited
+  // for at the end of each step
+  using FS = AsyncFillShape<BQ, D>;
+  unsigned copy_off[FS::PER];
+  const int wu = wave_uniform(wave);
+  if constexpr (sizeof(T) == 2) async_fill_plan<BQ, D>(copy_off, rs, wu, lane);
   auto fill = [&](Buf& B, int qt) ATTN_INLINE {
     const int q0 = qt * BQ;
     if constexpr (sizeof(T) == 2) {
       if (q0 + BQ <= N && d == D) {
-        fill_async(QT{B.q}, Q + base, rs, q0, wave, lane);
-        fill_async(QT{B.o}, dO + base, rs, q0, wave, lane);
-        if (wave == 0) fill_async_row64(B.l, Lh + q0);
-        if (wave == 1) fill_async_row64(B.dd, Dh + q0);
+        const long at = base + (long)q0 * rs;
+        async_fill_untracked<BQ, D>(QT{B.q}, Q + at, copy_off, wu);
+        async_fill_untracked<BQ, D>(QT{B.o}, dO + at, copy_off, wu);
+        if (wu == 0) fill_row64_untracked(B.l, Lh + q0, lane);
+        if (wu == 1) fill_row64_untracked(B.dd, Dh + q0, lane);
         return;
       }
     }
@@ -317,12 +325,18 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
     return mask ? (int)(visit_entry(vis, p) & kVisitTile) : p;
   };
 
+  // bf16 whole tiles: direct copies by a plan built once per workgroup
+  using FS = AsyncFillShape<BKV, D>;
+  unsigned copy_off[FS::PER];
+  const int wu = wave_uniform(wave);
+  if constexpr (sizeof(T) == 2) async_fill_plan<BKV, D>(copy_off, rs, wu, lane);
   auto fill = [&](Buf& B, int kt) ATTN_INLINE {
     const int k0 = kt * BKV;
     if constexpr (sizeof(T) == 2) {
       if (k0 + BKV <= N && d == D) {
-        fill_async(KT{B.k}, K + base, rs, k0, wave, lane);
-        fill_async(KT{B.v}, V + base, rs, k0, wave, lane);
+        const long at = base + (long)k0 * rs;
+        async_fill_untracked<BKV, D>(KT{B.k}, K + at, copy_off, wu);
+        async_fill_untracked<BKV, D>(KT{B.v}, V + at, copy_off, wu);
         return;
       }
     }

@@ -79,12 +79,20 @@ __global__ __launch_bounds__(256, 1) void fwd_lse_kernel(const T* __restrict__ Q
     return mask ? (int)(visit_entry(vis, p) & kVisitTile) : p;
   };
 
+  // bf16 whole tiles: direct copies by a plan built once per workgroup (the
+  // tile base in scalar registers, a 32-bit offset per lane and copy), waited
+  // for at the end of each step
+  using FS = AsyncFillShape<BKV, D>;
+  unsigned copy_off[FS::PER];
+  const int wu = wave_uniform(wave);
+  if constexpr (sizeof(T) == 2) async_fill_plan<BKV, D>(copy_off, rs, wu, lane);
   auto fill = [&](Buf& B, int kt) ATTN_INLINE {
     const int k0 = kt * BKV;
     if constexpr (sizeof(T) == 2) {
       if (k0 + BKV <= N && d == D) {
-        fill_async(KT{B.k}, K + base, rs, k0, wave, lane);
-        fill_async(KT{B.v}, V + base, rs, k0, wave, lane);
+        const long at = base + (long)k0 * rs;
+        async_fill_untracked<BKV, D>(KT{B.k}, K + at, copy_off, wu);
+        async_fill_untracked<BKV, D>(KT{B.v}, V + at, copy_off, wu);
         return;
       }
     }
@@ -95,7 +103,9 @@ __global__ __launch_bounds__(256, 1) void fwd_lse_kernel(const T* __restrict__ Q
   auto body = [&](const Buf& B, int k0, auto masked_c) ATTN_INLINE {
     constexpr bool MASKED = decltype(masked_c)::value;
     const KT kt_{const_cast<T*>(B.k)}, vt_{const_cast<T*>(B.v)};
-#pragma unroll
+    // (not unrolled: two sub-tiles in flight at once overflow the registers
+    // at the widest head dims)
+#pragma unroll 1
     for (int st = 0; st < BKV / 32; ++st) {
       const int ka = k0 + st * 32;
       if (MASKED && CAUSAL && ka > qw + 31) continue;
