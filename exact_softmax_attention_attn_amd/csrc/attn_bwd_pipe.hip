@@ -573,37 +573,26 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
   // FUSE: -D and -L log2 e of the block's rows, kept here until the end,
   // where they go to the workspace as two whole-block stores
   __shared__ float sD[FUSE ? BQ : 1], sL2[FUSE ? BQ : 1];
+  // The preprocess for rows qb .. qb + BQ - 1: 16 lanes per row, 16 rows per
+  // pass.  Every pass's loads go out here, from clamped (in-bounds) addresses,
+  // beside the round-1 copies (and a block mask's reads below); the sums are
+  // formed once the visit list is built.  Lanes past the row or the head dim
+  // count 0.
+  static_assert(!FUSE || (NT == 256 && BQ % 16 == 0), "16 rows of 16 lanes per pass");
+  // (d = D <= 128: the preprocess's column loop is one chunk per lane)
+  static_assert(!FUSE || D <= 16 * 8, "one 8-column chunk per lane");
+  constexpr int NP = FUSE ? BQ / 16 : 1;
+  const int pl = tid & 15;                     // the lane's 8-column chunk of its row
+  bf16x8 xo[NP], xg[NP];
+  float lr[NP];
   if constexpr (FUSE) {
-    // the preprocess for rows qb .. qb + BQ - 1: 16 lanes per row, 16 rows per
-    // pass (the round-1 copies above are in flight meanwhile)
-    static_assert(NT == 256 && BQ % 16 == 0, "16 rows of 16 lanes per pass");
-    // (d = D <= 128: the preprocess's column loop is one chunk per lane)
-    static_assert(D <= 16 * 8, "one 8-column chunk per lane");
-    constexpr int NP = BQ / 16;
-    const int sub = tid & 15;
-    // every pass's loads first, from clamped (in-bounds) addresses, so they
-    // are in flight together; lanes past the row or the head dim count 0
-    bf16x8 xo[NP], xg[NP];
-    float lr[NP];
 #pragma unroll
     for (int pass = 0; pass < NP; ++pass) {
       const int n = min(qb + pass * 16 + (tid >> 4), N - 1);
-      const long at = base + (long)n * rs + min(sub * 8, D - 8);
+      const long at = base + (long)n * rs + min(pl * 8, D - 8);
       xo[pass] = *reinterpret_cast<const bf16x8*>(O + at);
       xg[pass] = *reinterpret_cast<const bf16x8*>(dO + at);
       lr[pass] = Lh[n];
-    }
-#pragma unroll
-    for (int pass = 0; pass < NP; ++pass) {
-      const int rl = pass * 16 + (tid >> 4), n = qb + rl;
-      float acc = dot8_bf16(xo[pass], xg[pass], 0.f);
-      if (!(n < N && sub * 8 < D)) acc = 0.f;
-#pragma unroll
-      for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);
-      if (sub == 0) {
-        sD[rl] = n < N ? -acc : 0.f;
-        sL2[rl] = neg_l2(lr[pass]);
-      }
     }
   }
   float dq[NH];
@@ -636,6 +625,20 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
                               (r0 + 1 < nb && mk[(r0 + 1) * nb + c] ? 2u : 0u);
         return code ? (code << 14) | (unsigned)t : 0u;
       });
+  if constexpr (FUSE) {
+#pragma unroll
+    for (int pass = 0; pass < NP; ++pass) {
+      const int rl = pass * 16 + (tid >> 4), n = qb + rl;
+      float acc = dot8_bf16(xo[pass], xg[pass], 0.f);
+      if (!(n < N && pl * 8 < D)) acc = 0.f;
+#pragma unroll
+      for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);
+      if (pl == 0) {
+        sD[rl] = n < N ? -acc : 0.f;
+        sL2[rl] = neg_l2(lr[pass]);
+      }
+    }
+  }
   // walk positions below inner_end need no checks (unmasked, next two tiles
   // whole); a sparse walk takes every step through the checked form (one loop
   // keeps the register assignment the same all along the walk)
