@@ -570,6 +570,7 @@ static hipError_t bob_go(const BobArgs& a, hipStream_t stream) {
                      a.mask_heads);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (bob_q2_pipe_serves(a)) return launch_bob_q2_pipe(a, stream);
   hipLaunchKernelGGL((bob_q_kernel<T, D, C, 2>), gq, dim3(256), 0, stream,
                      static_cast<const T*>(a.Q), static_cast<const T*>(a.K),
                      static_cast<const T*>(a.V), static_cast<const T*>(a.dO),

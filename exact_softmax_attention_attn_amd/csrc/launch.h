@@ -93,6 +93,10 @@ hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_lse(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dkdv_bf16_pipe(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dq_bf16_pipe(const BwdArgs& a, hipStream_t stream);
+// Backward of the backward, pass 2 query-block outer (hQ, hdO), pipelined:
+// serves bf16 at d = 64 and 128.
+bool bob_q2_pipe_serves(const BobArgs& a);
+hipError_t launch_bob_q2_pipe(const BobArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dq_fused_bf16_pipe(const BwdArgs& a, hipStream_t stream);
 // Whether launch_bwd_dq_fused serves these arguments (bf16, d 64 or 128); if
 // so, it does the preprocess for dQ's own rows and writes the workspace, and

@@ -1,4 +1,4 @@
-"""Static check of the pipelined backward kernels' device assembly (CPU only).
+"""Static check of the pipelined kernels' device assembly (CPU only).
 
 The pipelined kernels accumulate dK, dV and dQ with matrix instructions
 written in inline assembly, so the compiler does not know their latency.  If
@@ -237,7 +237,8 @@ def test_checker_follows_branches_not_text_order():
 @pytest.mark.skipif(shutil.which(build_lib.HIPCC) is None and not os.path.exists(build_lib.HIPCC),
                     reason="hipcc not available")
 @pytest.mark.parametrize("src,kinds", [("attn_bwd_pipe.hip", ("dkdv", "dq")),
-                                       ("attn_fwd_pipe.hip", ("fwd",))])
+                                       ("attn_fwd_pipe.hip", ("fwd",)),
+                                       ("attn_bob_pipe.hip", ("bob_q2",))])
 def test_pipelined_kernels_never_touch_in_flight_accumulators(tmp_path, src, kinds):
     out = tmp_path / "pipe.s"
     flags = [f for f in build_lib.COMMON_FLAGS if f != "-fPIC"]
