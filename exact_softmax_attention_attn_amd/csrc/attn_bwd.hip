@@ -56,8 +56,7 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(const T* __restrict
       }
     }
   }
-#pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);
+  acc = sum16_lanes(acc);
   if (n < N && sub == 0) {
     const long i = bh * N + n;
     Dout[i] = -acc;

@@ -631,8 +631,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
       const int rl = pass * 16 + (tid >> 4), n = qb + rl;
       float acc = dot8_bf16(xo[pass], xg[pass], 0.f);
       if (!(n < N && pl * 8 < D)) acc = 0.f;
-#pragma unroll
-      for (int off = 8; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 16);
+      acc = sum16_lanes(acc);
       if (pl == 0) {
         sD[rl] = n < N ? -acc : 0.f;
         sL2[rl] = neg_l2(lr[pass]);

@@ -47,6 +47,24 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // dot products (the products are exact in float32).  The preprocess kernel
 // and the dQ kernel's folded preprocess both form D with it, so they leave
 // the same bits.
+// Sum over each aligned group of 16 lanes, returned in all 16, by DPP moves
+// (no LDS round trips): lane pairs (quad_perm 1,0,3,2), pairs of pairs
+// (quad_perm 2,3,0,1), then the half-row and row mirrors pair quads and
+// eights.  Every lane adds the same two values at each stage, so all 16 get
+// the same bits.  The preprocess kernel and the dQ kernel's folded
+// preprocess both reduce D with it.
+template <int CTRL> __device__ __forceinline__ float dpp_add(float x) {
+  return x + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL,
+                                                                  0xF, 0xF, false));
+}
+__device__ __forceinline__ float sum16_lanes(float x) {
+  x = dpp_add<0xB1>(x);    // quad_perm [1, 0, 3, 2]
+  x = dpp_add<0x4E>(x);    // quad_perm [2, 3, 0, 1]
+  x = dpp_add<0x141>(x);   // row_half_mirror
+  x = dpp_add<0x140>(x);   // row_mirror
+  return x;
+}
+
 typedef __bf16 bf16pair __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float dot8_bf16(const bf16x8& x, const bf16x8& y, float acc) {
 #pragma unroll
