@@ -478,10 +478,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
 //   dS = P o dP',  dQ^T += K^T dS^T.
 // The scores are scaled in float32 (one FMA with the lane's -L2 per element,
 // the query rows run along the lanes), so they are the forward's scores to
-// float32 rounding.  -D cannot enter as a per-register C input either; each dP
-// chain starts with one extra product of a constant "ones" fragment and a
-// fragment carrying -D split into two bf16 parts (hi + lo, exact to about
-// 2^-16 relative), which adds it to every element.  The two halves' chains run
+// float32 rounding.  -D enters as the C input of each dP chain's first
+// product: every register of a lane belongs to the lane's query, so a tile
+// holding the lane's -D in all 16 registers (fixed for the whole walk) adds
+// it to every element, in float32.  The two halves' chains run
 // one after the other, so each VALU stage sits beside a chain it does not feed.
 // Key tiles are copied two steps ahead into a ring of three separately named
 // LDS buffers.  No atomics.
@@ -528,12 +528,10 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
   const int qw = qb + wave * WQ;               // this wave's first query row
   LanePlan<D> plan(lane);
   frag qf[NH][KS], of[NH][KS];
-  // bias operands: ones[k] = 1 for k in {0, 1}; bd[k] = (hi, lo) of the lane's
-  // -D for k in {0, 1}; zero elsewhere (K slots 8h .. 8h + 7)
-  frag ones, bd[NH];
+  // -D of the lane's query in every register, per half: the C input of each
+  // dP chain's first product
+  f32x16 ndt[NH];
   float nl2[NH];                               // -L log2 e of the lane's query, per half
-  const bf16 one = (bf16)1.f, zero = (bf16)0.f;
-  ones = h == 0 ? frag{one, one, zero, zero, zero, zero, zero, zero} : frag{};
 
   f32x16 acc[NH][MT];
 #pragma unroll
@@ -668,8 +666,8 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
 
   // Operands of the 32 key rows at r0 of a tile: K along the head dim (S, in
   // kf), V along the head dim (dP, in vf), K across positions (dQ, in tf).
-  // Per sub-tile the products run in chains (S and dP chains open with the
-  // row-scalar bias product):
+  // Per sub-tile the products run in chains (each dP chain starts from the
+  // -D tile):
   //   S_0 | S_1 | dP_0 | dP_1 | dQ_0 | dQ_1        (index = query half)
   // and every VALU stage reads a chain that finished at least one product
   // earlier: exps of S_0 beside S_1, exps of S_1 beside dP_0, dS_0 beside
@@ -739,11 +737,9 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
     }
     if (masked || kill) mask_half(sc[0], 0, ka, kill);
     // dP'_0 | P_1 = exp2(c S_1 - L2); second half of V read
-    pc[0] = M::mma(ones, bd[0], zero16());
-    fence();
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
-      pc[0] = M::mma(vf[kk], of[0][kk], pc[0]);
+      pc[0] = M::mma(vf[kk], of[0][kk], kk == 0 ? ndt[0] : pc[0]);
       if (kk < KS / 2) vf[KS / 2 + kk] = plan.cols(B.v, r0, KS / 2 + kk);
 #pragma unroll
       for (int e = 0; e < E; ++e)
@@ -752,12 +748,10 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
     }
     if (masked || kill) mask_half(sc[1], 1, ka, kill);
     // dP'_1 | dS_0 = P_0 o dP'_0, packed; first half of K^T read
-    pc[1] = M::mma(ones, bd[1], zero16());
-    fence();
     frag bds0[2];
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
-      pc[1] = M::mma(vf[kk], of[1][kk], pc[1]);
+      pc[1] = M::mma(vf[kk], of[1][kk], kk == 0 ? ndt[1] : pc[1]);
       if (kk >= KS / 2) tf[kk - KS / 2] = plan.rows(B.k, r0, 0, kk - KS / 2);
 #pragma unroll
       for (int e = 0; e < E; ++e) pc[0][kk * E + e] = sc[0][kk * E + e] * pc[0][kk * E + e];
@@ -886,9 +880,8 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
       pin_agpr(qf[c][kk]);
       pin_agpr(of[c][kk]);
     }
-    const bf16 dhi = (bf16)dq[c];
-    const bf16 dlo = (bf16)(dq[c] - (float)dhi);
-    bd[c] = h == 0 ? frag{dhi, dlo, zero, zero, zero, zero, zero, zero} : frag{};
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ndt[c][r] = dq[c];
   }
   int kt = 0;
   for (; kt + 3 <= inner_end; kt += 3) {
