@@ -57,7 +57,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ nL2, const float* __restrict__ nD,
     bf16* __restrict__ dK, bf16* __restrict__ dV, int H, int N, int d, float scale_log2,
-    float scale, const unsigned char* __restrict__ mask, int mask_heads) {
+    float scale, const unsigned char* __restrict__ mask, int mask_heads, int pair_cus) {
   using M = Mma<bf16>;
   using frag = bf16x8;
   constexpr int BKV = 128, BQ = 64, KS = D / 16, MT = D / 32, AH = 4;
@@ -73,7 +73,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
   const int wave = wave_uniform(tid >> 6);
-  const BlockOrder bo = block_order();
+  // (head dim 64: two workgroups per CU)
+  const BlockOrder bo = block_order_paired(D == 64 ? pair_cus : 0);
   const int jb = bo.rank, head = bo.head, b = bo.b;   // rank 0 = longest walk
   const long rs = (long)H * d;
   const long base = ((long)b * N * H + head) * d;
@@ -494,12 +495,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
 // ws are.
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL, int WQ, int NW, bool SPARSE, bool FUSE>
-__global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
+__global__ __launch_bounds__(NW * 64, WQ == 32 ? 2 : 1) void bwd_dq_bf16_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ nL2, const float* __restrict__ nD,
     bf16* __restrict__ dQ, int H, int N, int d, float scale_log2, float scale,
     const unsigned char* __restrict__ mask, int mask_heads, const bf16* __restrict__ O,
-    const float* __restrict__ L, float* __restrict__ ws) {
+    const float* __restrict__ L, float* __restrict__ ws, int pair_cus) {
   using M = Mma<bf16>;
   using frag = bf16x8;
   constexpr int NH = WQ / 32;                  // 32-row halves per wave
@@ -515,7 +516,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
   const int wave = wave_uniform(tid >> 6);
   const int nqb = gridDim.x;
-  const BlockOrder bo = block_order();
+  const BlockOrder bo = block_order_paired(NH == 1 ? pair_cus : 0);
   const int ib = CAUSAL ? (nqb - 1 - bo.rank) : bo.rank;   // longest first
   const int head = bo.head, b = bo.b;
   const long rs = (long)H * d;
@@ -537,7 +538,10 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
 #pragma unroll
   for (int c = 0; c < NH; ++c)
 #pragma unroll
-    for (int i = 0; i < MT; ++i) { acc[c][i] = zero16(); pin_agpr(acc[c][i]); }
+    for (int i = 0; i < MT; ++i) {
+      acc[c][i] = zero16();
+      if constexpr (NH == 2) pin_agpr(acc[c][i]);
+    }
 
   using FS = AsyncFillShape<BKV, D, NW>;
   unsigned copy_off[FS::PER];
@@ -556,13 +560,22 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
   // (buf2) beside the walk's first two key tiles (buf0, buf1).  Each buffer
   // holds 128 rows as its k and v tiles; wave w's 64 rows are tile w % 2 of
   // buffer w / 2 (Q) and of buf2 (dO, round w / 2 + 1).
-  static_assert(NW == 4 && WQ == BKV, "two waves' rows per buffer");
-  fill_rows(buf0.k, Q, qb);
-  fill_rows(buf0.v, Q, qb + 64);
-  fill_rows(buf1.k, Q, qb + 128);
-  fill_rows(buf1.v, Q, qb + 192);
-  fill_rows(buf2.k, dO, qb);
-  fill_rows(buf2.v, dO, qb + 64);
+  // One-half form (WQ = 32, 128 rows per block): Q in buf0 and dO in buf1,
+  // one round; wave w's 32 rows are rows 32 (w % 2) of tile w / 2.
+  static_assert(NW == 4 && (WQ == BKV || WQ == 32), "wave rows per buffer");
+  if constexpr (NH == 2) {
+    fill_rows(buf0.k, Q, qb);
+    fill_rows(buf0.v, Q, qb + 64);
+    fill_rows(buf1.k, Q, qb + 128);
+    fill_rows(buf1.v, Q, qb + 192);
+    fill_rows(buf2.k, dO, qb);
+    fill_rows(buf2.v, dO, qb + 64);
+  } else {
+    fill_rows(buf0.k, Q, qb);
+    fill_rows(buf0.v, Q, qb + 64);
+    fill_rows(buf1.k, dO, qb);
+    fill_rows(buf1.v, dO, qb + 64);
+  }
   // -L log2 e as the preprocess forms it (a row with no kept key, L = -inf,
   // gives -inf, so every P of it is 0)
   auto neg_l2 = [](float l) ATTN_INLINE -> float {
@@ -612,7 +625,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
   // (64 rows, one mask row) zeroes P on the tiles its own row drops.
   __shared__ unsigned short vis[SPARSE ? kMaxVisit : 1];
   __shared__ int nvis;
-  static_assert(!SPARSE || (BQ == 2 * kMaskBlock && WQ * 2 == kMaskBlock),
+  static_assert(!SPARSE || ((BQ == 2 * kMaskBlock || BQ == kMaskBlock) && WQ * 2 <= kMaskBlock),
                 "mask rows per block and per wave");
   const int nb = (N + kMaskBlock - 1) / kMaskBlock;
   const int ntiles = !SPARSE ? ntiles_all : build_visits(vis, &nvis, ntiles_all,
@@ -620,7 +633,7 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
         const unsigned char* mk = head_mask(mask, mask_heads, b, head, H, nb);
         const int r0 = qb / kMaskBlock, c = t * BKV / kMaskBlock;
         const unsigned code = (mk[r0 * nb + c] ? 1u : 0u) |
-                              (r0 + 1 < nb && mk[(r0 + 1) * nb + c] ? 2u : 0u);
+                              (BQ > kMaskBlock && r0 + 1 < nb && mk[(r0 + 1) * nb + c] ? 2u : 0u);
         return code ? (code << 14) | (unsigned)t : 0u;
       });
   if constexpr (FUSE) {
@@ -680,18 +693,20 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
   constexpr int NSLOT = 2 * FS::PER, SPS = NSLOT / 2;     // copy slots per tile, per sub-tile
   static_assert(KS % SPS == 0, "copy slots per sub-tile");
   static_assert(KS == 2 * MT, "one K fragment read per dQ_1 product");
-  static_assert(NH == 2, "two query halves per wave");
   auto copy_slot = [&](Buf& A, int k0, int j) ATTN_INLINE {
     if (j < FS::PER) async_fill_one_untracked<BKV, D, NW>(KT{A.k}, K + base + k0 * rs, copy_off, wave, j);
     else async_fill_one_untracked<BKV, D, NW>(KT{A.v}, V + base + k0 * rs, copy_off, wave, j - FS::PER);
   };
-  frag kf[KS], vf[KS], tf[2 * MT], bds1[2];
+  // (two-half form: kf, vf, tf, bds1; one-half form: kf, vf, tf for the
+  // pending sub-tile's K^T, tfn, pp, dpp)
+  frag kf[KS], vf[KS], tf[2 * MT], tfn[2 * MT], bds1[2];
+  f32x16 pp, dpp;
   // dQ_1 of the pending sub-tile (K^T in tf, dS_1 packed in bds1), reading the
   // K fragments of the sub-tile at r0 of B beside it
   auto dq_half1 = [&](const Buf& B, int r0) ATTN_INLINE {
 #pragma unroll
     for (int i = 0; i < 2 * MT; ++i) {
-      mma_acc_agpr(acc[1][i % MT], tf[i], bds1[i / MT]);
+      mma_acc_agpr(acc[NH - 1][i % MT], tf[i], bds1[i / MT]);
       kf[i] = plan.cols(B.k, r0, i);
       fence();
     }
@@ -786,14 +801,94 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
     pin_operand(bds1[1]);
     fence();
   };
-  // One key tile: the pending dQ_1 of the previous tile while this tile's
-  // first K fragments are read, then both sub-tiles.  Before the first tile
-  // the pending products add zero (dS = 0), which keeps every step alike.
+  // One-half form (WQ = 32): the wave's 32 query rows are one half, and two
+  // workgroups share a CU, so each SIMD runs two waves.  Per sub-tile j the
+  // chains run
+  //   S_j | dQ_{j-1} | dP_j
+  // with dS_{j-1} = P_{j-1} o dP'_{j-1} (multiplies and packs) beside S_j,
+  // P_j's exps beside dQ_{j-1} and dP_j, V_j read during S_j, K^T_j during
+  // dQ_{j-1} and the tile's second K during dP_j; a tile's first K is read
+  // after its barrier.  P_j, dP'_j and K^T_j stay pending (pp, dpp, tf).
+  // Everything, the dQ^T accumulators included, lives in VGPRs with builtin
+  // products: at two waves per SIMD a wave has 256 registers, and the
+  // compiler would split them evenly between VGPRs and AGPRs if any AGPR
+  // were pinned.
+  auto sub1 = [&](const Buf& B, int st, int ka, bool masked, bool kill, auto&& copy) ATTN_INLINE {
+    const int r0 = st * 32;
+    constexpr int EM = 16 / KS;                 // dS multiplies per S product
+    constexpr int EX = 16 / (2 * MT + KS);      // exps per dQ or dP product
+    static_assert(EM * KS == 16 && EX * (2 * MT + KS) == 16 && EM <= 8, "elements per product");
+    frag bd[2];
+    // S_j^T = K Q^T | dS_{j-1}, packed; V_j read
+    f32x16 sc = M::mma(kf[0], qf[0][0], zero16());
+    copy(st * SPS);
+#pragma unroll
+    for (int e = 0; e < EM; ++e) dpp[e] = pp[e] * dpp[e];
+    vf[0] = plan.cols(B.v, r0, 0);
+    fence();
+#pragma unroll
+    for (int kk = 1; kk < KS; ++kk) {
+      sc = M::mma(kf[kk], qf[0][kk], sc);
+      if (kk % (KS / SPS) == 0) copy(st * SPS + kk / (KS / SPS));
+#pragma unroll
+      for (int e = 0; e < EM; ++e) dpp[kk * EM + e] = pp[kk * EM + e] * dpp[kk * EM + e];
+      if (kk * EM + EM == 8) {
+        bd[0] = M::pack(dpp, 0);
+        pin_operand(bd[0]);
+      }
+      vf[kk] = plan.cols(B.v, r0, kk);
+      fence();
+    }
+    bd[1] = M::pack(dpp, 1);                    // first read MT products into dQ_{j-1}
+    pin_operand(bd[1]);
+    fence();
+    // dQ_{j-1}^T += K^T dS_{j-1}^T | P_j = exp2(c S_j - L2), first part; K^T_j read
+#pragma unroll
+    for (int i = 0; i < 2 * MT; ++i) {
+      acc[0][i % MT] = M::mma(tf[i], bd[i / MT], acc[0][i % MT]);
+      tfn[i] = plan.rows(B.k, r0, i / MT, i % MT);
+#pragma unroll
+      for (int e = 0; e < EX; ++e)
+        sc[i * EX + e] = fast_exp2(__builtin_fmaf(sc[i * EX + e], scale_log2, nl2[0]));
+      fence();
+    }
+    // dP'_j^T = V dO^T - D (the -D tile as C input) | the rest of P_j; the
+    // tile's second K read
+    f32x16 pc;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      pc = M::mma(vf[kk], of[0][kk], kk == 0 ? ndt[0] : pc);
+      if (st == 0) kf[kk] = plan.cols(B.k, 32, kk);
+#pragma unroll
+      for (int e = 0; e < EX; ++e) {
+        const int r = 2 * MT * EX + kk * EX + e;
+        sc[r] = fast_exp2(__builtin_fmaf(sc[r], scale_log2, nl2[0]));
+      }
+      fence();
+    }
+    if (masked || kill) mask_half(sc, 0, ka, kill);
+    pp = sc;
+    dpp = pc;
+#pragma unroll
+    for (int i = 0; i < 2 * MT; ++i) tf[i] = tfn[i];
+  };
+  // One key tile.  Two-half form: the pending dQ_1 of the previous tile while
+  // this tile's first K fragments are read, then both sub-tiles.  One-half
+  // form: this tile's first K fragments, then both sub-tiles.  Before the
+  // first tile the pending products add zero (dS = 0), which keeps every
+  // step alike.
   auto tile_body = [&](int kt, const Buf& B, bool masked, bool kill, auto&& copy) ATTN_INLINE {
-    dq_half1(B, 0);
-    sub(B, 0, kt * BKV, masked, kill, copy);
-    dq_half1(B, 32);
-    sub(B, 1, kt * BKV + 32, masked, kill, copy);
+    if constexpr (NH == 2) {
+      dq_half1(B, 0);
+      sub(B, 0, kt * BKV, masked, kill, copy);
+      dq_half1(B, 32);
+      sub(B, 1, kt * BKV + 32, masked, kill, copy);
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) kf[kk] = plan.cols(B.k, 0, kk);
+      sub1(B, 0, kt * BKV, masked, kill, copy);
+      sub1(B, 1, kt * BKV + 32, masked, kill, copy);
+    }
   };
 
   // Key tiles are copied two steps ahead into a ring of three separately
@@ -831,14 +926,28 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
 #pragma unroll
   for (int i = 0; i < 2 * MT; ++i) tf[i] = frag{};
   bds1[0] = bds1[1] = frag{};
+  pp = zero16();
+  dpp = zero16();
   // round 1 landed (every wave's copies): Q for all waves, dO for waves 0, 1
-  // (and, FUSE, every row's -D is in sD)
+  // (one-half form: dO for all waves) (and, FUSE, every row's -D is in sD)
   wait_async_fills();
   lds_barrier();
   if constexpr (FUSE) {
 #pragma unroll
     for (int c = 0; c < NH; ++c) dq[c] = sD[wave * WQ + 32 * c + l32];
   }
+  if constexpr (NH == 1) {
+    const bf16* qt = wave < 2 ? buf0.k : buf0.v;
+    const bf16* ot = wave < 2 ? buf1.k : buf1.v;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      qf[0][kk] = plan.cols(qt, 32 * (wave & 1), kk);
+      of[0][kk] = plan.cols(ot, 32 * (wave & 1), kk);
+    }
+    lds_barrier();                             // buf0, buf1 free again
+    if (ntiles > 0) fill(buf0, tile_at(0));     // a sparse walk may visit nothing
+    if (ntiles > 1) fill(buf1, tile_at(1));
+  } else {
   {
     const Buf& qb_buf = wave < 2 ? buf0 : buf1;
     const bf16* qt = (wave & 1) ? qb_buf.v : qb_buf.k;
@@ -871,14 +980,17 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
       for (int kk = 0; kk < KS; ++kk)
         if (wave >= 2) of[c][kk] = plan.cols(ot, 32 * c, kk);
   }
+  }
   // (the first step's barrier frees buf2, which its copies of tile 2 fill,
   // from these reads)
 #pragma unroll
   for (int c = 0; c < NH; ++c) {
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
-      pin_agpr(qf[c][kk]);
-      pin_agpr(of[c][kk]);
+      if constexpr (NH == 2) {
+        pin_agpr(qf[c][kk]);
+        pin_agpr(of[c][kk]);
+      }
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) ndt[c][r] = dq[c];
@@ -896,14 +1008,25 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
   }
   if (kt < ntiles) step(kt, buf0, buf2);
   if (kt + 1 < ntiles) step(kt + 1, buf1, buf0);
-  // the last sub-tile's dQ_1
+  if constexpr (NH == 2) {
+    // the last sub-tile's dQ_1
 #pragma unroll
-  for (int i = 0; i < 2 * MT; ++i) {
-    mma_acc_agpr(acc[1][i % MT], tf[i], bds1[i / MT]);
-    fence();
+    for (int i = 0; i < 2 * MT; ++i) {
+      mma_acc_agpr(acc[NH - 1][i % MT], tf[i], bds1[i / MT]);
+      fence();
+    }
+  } else {
+    // the last sub-tile's dS and dQ
+    frag bd[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dpp[r] = pp[r] * dpp[r];
+    bd[0] = M::pack(dpp, 0);
+    bd[1] = M::pack(dpp, 1);
+#pragma unroll
+    for (int i = 0; i < 2 * MT; ++i) acc[0][i % MT] = M::mma(tf[i], bd[i / MT], acc[0][i % MT]);
   }
 
-  mma_acc_drain(acc);
+  if constexpr (NH == 2) mma_acc_drain(acc);
   // every wave is done with the key tiles: rows out through buf0 (waves 0, 1)
   // and buf1 (waves 2, 3), whole rows per store
   static_assert(NW == 4 && 2 * RowStage<D>::BYTES <= sizeof(Buf), "staging area");
@@ -925,6 +1048,19 @@ __global__ __launch_bounds__(NW * 64, 1) void bwd_dq_bf16_kernel(
 // ---------------------------------------------------------------------------
 static inline long rows_of(const BwdArgs& a) { return (long)a.B * a.H * a.N; }
 
+// Compute units of the current device (0 if the query fails), once per device.
+static int device_cus() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+      cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 template <int D, bool C, bool S>
 static hipError_t dkdv_pipe_run(const BwdArgs& a, hipStream_t stream) {
   dim3 grid((a.N + 127) / 128, a.H, a.B);
@@ -933,7 +1069,7 @@ static hipError_t dkdv_pipe_run(const BwdArgs& a, hipStream_t stream) {
                      static_cast<const bf16*>(a.V), static_cast<const bf16*>(a.dO),
                      a.Dws + rows_of(a), a.Dws, static_cast<bf16*>(a.dK),
                      static_cast<bf16*>(a.dV), a.H, a.N, a.d, a.scale * kLog2e, a.scale,
-                     a.mask, a.mask_heads);
+                     a.mask, a.mask_heads, D == 64 ? device_cus() : 0);
   return hipGetLastError();
 }
 template <int D, bool C>
@@ -945,17 +1081,20 @@ static hipError_t dkdv_pipe_go(const BwdArgs& a, hipStream_t stream) {
 #ifndef ATTN_DQ_NW
 #define ATTN_DQ_NW 4
 #endif
+// (causal, head dim 64: the one-half form, 128 query rows per workgroup as
+// four waves of 32, two workgroups per CU, so that the SIMDs whose waves walk
+// the long rows near the sequence's end also take short ones)
 template <int D, bool C, bool S, bool F>
 static hipError_t dq_pipe_run(const BwdArgs& a, hipStream_t stream) {
-  constexpr int NW = ATTN_DQ_NW, WQ = 256 / NW;
-  dim3 grid((a.N + 255) / 256, a.H, a.B);
+  constexpr int NW = ATTN_DQ_NW, WQ = D == 64 && C ? 32 : 256 / NW, BQ = NW * WQ;
+  dim3 grid((a.N + BQ - 1) / BQ, a.H, a.B);
   hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, C, WQ, NW, S, F>), grid, dim3(NW * 64), 0, stream,
                      static_cast<const bf16*>(a.Q), static_cast<const bf16*>(a.K),
                      static_cast<const bf16*>(a.V), static_cast<const bf16*>(a.dO),
                      F ? nullptr : a.Dws + rows_of(a), F ? nullptr : a.Dws,
                      static_cast<bf16*>(a.dQ), a.H, a.N, a.d, a.scale * kLog2e, a.scale, a.mask,
                      a.mask_heads, F ? static_cast<const bf16*>(a.O) : nullptr,
-                     F ? a.L : nullptr, F ? a.ws_out : nullptr);
+                     F ? a.L : nullptr, F ? a.ws_out : nullptr, WQ == 32 ? device_cus() : 0);
   return hipGetLastError();
 }
 template <int D, bool C>

@@ -128,6 +128,24 @@ __device__ __forceinline__ BlockOrder block_order() {
   const int bh = lin % nbh;
   return {lin / nbh, bh % (int)gridDim.y, bh / (int)gridDim.y};
 }
+// The same for kernels that run two workgroups per CU, when the whole grid
+// fits the chip at once (cus < blocks <= 2 cus): the dispatcher gives the
+// first cus workgroups one CU each and the rest the CUs' second places in the
+// same order, so the second wave is numbered shortest-first (per XCD lane,
+// which keeps a head's blocks on one XCD): the CU that runs the longest block
+// also runs the shortest.  cus = 0 keeps block_order().
+__device__ __forceinline__ BlockOrder block_order_paired(int cus) {
+  const int nbh = gridDim.y * gridDim.z;
+  int lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  const int total = gridDim.x * nbh;
+  if (cus > 0 && cus % 8 == 0 && total > cus && total <= 2 * cus && (total - cus) % 8 == 0 &&
+      lin >= cus) {
+    const int m = (total - cus) / 8, j = (lin - cus) / 8, x = lin % 8;
+    lin = cus + 8 * (m - 1 - j) + x;
+  }
+  const int bh = lin % nbh;
+  return {lin / nbh, bh % (int)gridDim.y, bh / (int)gridDim.y};
+}
 
 // ---------------------------------------------------------------------------
 // Block-sparse masks.  A mask keeps or drops whole blocks of kMaskBlock query

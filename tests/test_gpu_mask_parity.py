@@ -53,6 +53,7 @@ CASES = [
     (1, 2, 1000, 128, "bf16", True, "random"),          # pipelined kernels, d = 128
     (1, 2, 1000, 128, "bf16", False, "random_heads"),
     (2, 2, 700, 64, "bf16", False, "random_empty"),     # d = 64, rows keeping no key
+    (2, 2, 700, 64, "bf16", True, "random_empty"),      # d = 64 causal (one-half dQ form)
     (1, 2, 513, 128, "bf16", True, "random_empty"),     # ragged last tile
     (1, 1, 1100, 128, "bf16", True, "window"),           # local window + sink blocks
     (1, 2, 300, 64, "f32", True, "random_heads"),        # generic kernels, float32
