@@ -750,6 +750,9 @@ __global__ __launch_bounds__(NW * 64, WQ == 32 ? 2 : 1) void bwd_dq_bf16_kernel(
         sc[0][kk * E + e] = fast_exp2(__builtin_fmaf(sc[0][kk * E + e], scale_log2, nl2[0]));
       fence();
     }
+    // (a use here keeps the exps beside the chain; otherwise the compiler
+    // bunches some of them next to their first use, with no product beside)
+    pin_operand(sc[0]);
     if (masked || kill) mask_half(sc[0], 0, ka, kill);
     // dP'_0 | P_1 = exp2(c S_1 - L2); second half of V read
 #pragma unroll
@@ -761,6 +764,7 @@ __global__ __launch_bounds__(NW * 64, WQ == 32 ? 2 : 1) void bwd_dq_bf16_kernel(
         sc[1][kk * E + e] = fast_exp2(__builtin_fmaf(sc[1][kk * E + e], scale_log2, nl2[1]));
       fence();
     }
+    pin_operand(sc[1]);
     if (masked || kill) mask_half(sc[1], 1, ka, kill);
     // dP'_1 | dS_0 = P_0 o dP'_0, packed; first half of K^T read
     frag bds0[2];
@@ -852,6 +856,7 @@ __global__ __launch_bounds__(NW * 64, WQ == 32 ? 2 : 1) void bwd_dq_bf16_kernel(
         sc[i * EX + e] = fast_exp2(__builtin_fmaf(sc[i * EX + e], scale_log2, nl2[0]));
       fence();
     }
+    pin_operand(sc);                            // keeps these exps beside the chain
     // dP'_j^T = V dO^T - D (the -D tile as C input) | the rest of P_j; the
     // tile's second K read
     f32x16 pc;
@@ -862,10 +867,13 @@ __global__ __launch_bounds__(NW * 64, WQ == 32 ? 2 : 1) void bwd_dq_bf16_kernel(
 #pragma unroll
       for (int e = 0; e < EX; ++e) {
         const int r = 2 * MT * EX + kk * EX + e;
-        sc[r] = fast_exp2(__builtin_fmaf(sc[r], scale_log2, nl2[0]));
+        float p = fast_exp2(__builtin_fmaf(sc[r], scale_log2, nl2[0]));
+        asm volatile("" : "+v"(p));             // here, not bunched at the chain's end
+        sc[r] = p;
       }
       fence();
     }
+    pin_operand(sc);
     if (masked || kill) mask_half(sc, 0, ka, kill);
     pp = sc;
     dpp = pc;
