@@ -347,7 +347,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_bf16_kernel(
       refill(C_DKA * L + i);
       slot(C_DKA, i);
 #pragma unroll
-      for (int e = 0; e < M2; ++e) pb[i * M2 + e] = sb[i * M2 + e] * pb[i * M2 + e];
+      for (int e = 0; e < M2; ++e) {
+        float x = sb[i * M2 + e] * pb[i * M2 + e];
+        asm volatile("" : "+v"(x));             // here, not bunched before the packs
+        pb[i * M2 + e] = x;
+      }
       fence();
     }
     bdsp[0] = M::pack(pb, 0);
