@@ -458,12 +458,18 @@ __global__ __launch_bounds__(256, 1) void bob_kv_kernel(
       f32x16 dp;                                    // starts at -D: dP - D
 #pragma unroll
       for (int r = 0; r < 16; ++r) dp[r] = dg[r / 4][r % 4];
-      // S is complete here: P is formed beside the G, dP and A products
+      // S is complete here: P is formed beside the G, dP and A products.
+      // Their gQ and dO fragments are read one K step ahead of use.
+      frag gqn = gqt_.along_cols(st * 32 + l32, 0, h), ocn = ot_.along_cols(st * 32 + l32, 0, h);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        g = M::mma(gqt_.along_cols(st * 32 + l32, ks, h), kf[ks], g);
-        const frag oc = ot_.along_cols(st * 32 + l32, ks, h);
+        const frag gqc = gqn, oc = ocn;
+        if (ks + 1 < KS) {
+          gqn = gqt_.along_cols(st * 32 + l32, ks + 1, h);
+          ocn = ot_.along_cols(st * 32 + l32, ks + 1, h);
+        }
+        g = M::mma(gqc, kf[ks], g);
         dp = M::mma(oc, vf[ks], dp);
         a = M::mma(oc, gvf[ks], a);
 #pragma unroll
@@ -492,12 +498,24 @@ __global__ __launch_bounds__(256, 1) void bob_kv_kernel(
         bds2[ss] = M::pack(s, ss);
         bw[ss] = M::pack(a, ss);
       };
-      // hV^T += dO^T W;  hK^T += Q^T dS2 + gQ^T dS
-      auto prods = [&](int ss, int mt) ATTN_INLINE {
-        acc_v[mt] = M::mma(ot_.along_rows(mt * 32 + l32, st * 32, ss, h), bw[ss], acc_v[mt]);
-        acc_k[mt] = M::mma(qt_.along_rows(mt * 32 + l32, st * 32, ss, h), bds2[ss], acc_k[mt]);
-        acc_k[mt] = M::mma(gqt_.along_rows(mt * 32 + l32, st * 32, ss, h), bds[ss], acc_k[mt]);
+      // hV^T += dO^T W;  hK^T += Q^T dS2 + gQ^T dS.  Group i = (ss, mt) of
+      // the NG * 2 groups; its three fragments are read one group ahead.
+      frag ro[3];
+      auto read_group = [&](int i) ATTN_INLINE {
+        const int ss = i / MT, mt = i % MT;
+        ro[0] = ot_.along_rows(mt * 32 + l32, st * 32, ss, h);
+        ro[1] = qt_.along_rows(mt * 32 + l32, st * 32, ss, h);
+        ro[2] = gqt_.along_rows(mt * 32 + l32, st * 32, ss, h);
       };
+      auto prods = [&](int ss, int mt) ATTN_INLINE {
+        const frag o0 = ro[0], o1 = ro[1], o2 = ro[2];
+        const int i = ss * MT + mt;
+        if (i + 1 < RS * MT) read_group(i + 1);
+        acc_v[mt] = M::mma(o0, bw[ss], acc_v[mt]);
+        acc_k[mt] = M::mma(o1, bds2[ss], acc_k[mt]);
+        acc_k[mt] = M::mma(o2, bds[ss], acc_k[mt]);
+      };
+      read_group(0);
 #pragma unroll
       for (int r = 0; r < 8; ++r) elem(r);
 #pragma unroll
