@@ -349,6 +349,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
   // products (0 * inf)
   const int klim = CAUSAL ? q : N - 1;              // last kept key of the lane's query
   const int wlim = CAUSAL ? qw + 31 : N - 1;        // ... of any query of the wave
+  // (bf16 head dim 256: the operands of one sub-tile's S, dP and dQ products
+  // are read in one sequence, RA fragments ahead of their products through a
+  // ring, with the order held by scheduling fences; read all at once they
+  // would take 128 registers and leave every product waiting on its read)
+  constexpr bool RING = sizeof(T) == 2 && D > 128;
+  constexpr int RA = 3;
   auto body = [&](const Buf& B, int k0, auto masked_c) ATTN_INLINE {
     constexpr bool MASKED = decltype(masked_c)::value;
     const KT kt_{const_cast<T*>(B.k)}, vt_{const_cast<T*>(B.v)};
@@ -356,12 +362,52 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
     for (int st = 0; st < BKV / 32; ++st) {
       const int ka = k0 + st * 32;
       if (MASKED && ka > wlim) continue;           // every pair masked
+      f32x16 s = zero16(), dp = zero16();
+      if constexpr (RING) {
+        // operand n of the sub-tile: K along the head dim (n < KS), V along
+        // the head dim (KS <= n < 2 KS), K across positions (then)
+        constexpr int NOP = 2 * KS + RS * MA;
+        auto opnd = [&](int n) ATTN_INLINE -> frag {
+          if (n < KS) return kt_.along_cols(st * 32 + l32, n, h);
+          if (n < 2 * KS) return vt_.along_cols(st * 32 + l32, n - KS, h);
+          const int j = n - 2 * KS;
+          return kt_.along_rows(dofs + (j % MA) * 32 + l32, st * 32, j / MA, h);
+        };
+        frag ring[RA];
+#pragma unroll
+        for (int n = 0; n < RA; ++n) ring[n] = opnd(n);
+#pragma unroll
+        for (int n = 0; n < 2 * KS; ++n) {
+          const frag a = ring[n % RA];
+          if (n + RA < NOP) ring[n % RA] = opnd(n + RA);
+          if (n < KS) s = M::mma(a, qf[n], s);
+          else dp = M::mma(a, of[n - KS], dp);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float p = fast_exp2(__builtin_fmaf(s[r], scale_log2, Lq));
+          if (MASKED && ka + acc_row(r, h) > klim) p = 0.f;
+          dp[r] = p * (dp[r] + Dq);
+        }
+        frag bds[RS];
+#pragma unroll
+        for (int ss = 0; ss < RS; ++ss) bds[ss] = M::pack(dp, ss);
+#pragma unroll
+        for (int j = 0; j < RS * MA; ++j) {
+          const int n = 2 * KS + j;
+          const frag a = ring[n % RA];
+          if (n + RA < NOP) ring[n % RA] = opnd(n + RA);
+          acc[j % MA] = M::mma(a, bds[j / MA], acc[j % MA]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        continue;
+      }
       frag ak[KS], av[KS];
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) ak[kk] = kt_.along_cols(st * 32 + l32, kk, h);
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) av[kk] = vt_.along_cols(st * 32 + l32, kk, h);
-      f32x16 s = zero16(), dp = zero16();
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) s = M::mma(ak[kk], qf[kk], s);
 #pragma unroll
