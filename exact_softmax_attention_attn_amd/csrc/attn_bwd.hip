@@ -174,6 +174,67 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     for (int st = 0; st < BQ / 32; ++st) {
       const int qa = q0 + st * 32;                 // first query row of the sub-tile
       if (MASKED && qa + 31 < kv0) continue;       // every pair above the diagonal
+      if constexpr (sizeof(T) == 2 && D > 128) {
+        // bf16 head dim 256: the sub-tile's operands (Q, dO along the head
+        // dim for S and dP; dO, Q across positions for dV and dK) are read
+        // in one sequence, RA fragments ahead of their products through a
+        // ring, with the order held by scheduling fences, so that no product
+        // waits on a read issued right before it
+        constexpr int RA = 3, NG = RS * MA, NOP = 2 * KS + 2 * NG;
+        auto opnd = [&](int n) ATTN_INLINE -> frag {
+          if (n < KS) return qt_.along_cols(st * 32 + l32, n, h);
+          if (n < 2 * KS) return ot_.along_cols(st * 32 + l32, n - KS, h);
+          const int j = (n - 2 * KS) % NG;
+          const QT& src = n < 2 * KS + NG ? ot_ : qt_;
+          return src.along_rows(dofs + (j % MA) * 32 + l32, st * 32, j / MA, h);
+        };
+        frag ring[RA];
+#pragma unroll
+        for (int n = 0; n < RA; ++n) ring[n] = opnd(n);
+        auto take = [&](int n) ATTN_INLINE -> frag {
+          const frag a = ring[n % RA];
+          if (n + RA < NOP) ring[n % RA] = opnd(n + RA);
+          return a;
+        };
+        f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+        for (int n = 0; n < 2 * KS; ++n) {
+          const frag a = take(n);
+          if (n < KS) s = M::mma(a, kf[n], s);
+          else dp = M::mma(a, vf[n - KS], dp);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 lg = *reinterpret_cast<const f32x4*>(&B.l[st * 32 + 8 * g + 4 * h]);
+          const f32x4 dg = *reinterpret_cast<const f32x4*>(&B.dd[st * 32 + 8 * g + 4 * h]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 4 * g + i;
+            float p = fast_exp2(__builtin_fmaf(s[r], scale_log2, lg[i]));
+            if (MASKED && kv > qa + acc_row(r, h)) p = 0.f;
+            s[r] = p;
+            dp[r] = p * (dp[r] + dg[i]);
+          }
+        }
+        frag bp[RS], bds[RS];
+#pragma unroll
+        for (int ss = 0; ss < RS; ++ss) {
+          bp[ss] = M::pack(s, ss);
+          bds[ss] = M::pack(dp, ss);
+        }
+#pragma unroll
+        for (int j = 0; j < NG; ++j) {
+          dv_acc[j % MA] = M::mma(take(2 * KS + j), bp[j / MA], dv_acc[j % MA]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int j = 0; j < NG; ++j) {
+          dk_acc[j % MA] = M::mma(take(2 * KS + NG + j), bds[j / MA], dk_acc[j % MA]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        continue;
+      }
       // S and dP: register r = query row qa + acc_row(r, h), column = key row kv
       frag aq[KS], ao[KS];
 #pragma unroll
