@@ -109,9 +109,40 @@ __global__ __launch_bounds__(256, 1) void fwd_lse_kernel(const T* __restrict__ Q
     for (int st = 0; st < BKV / 32; ++st) {
       const int ka = k0 + st * 32;
       if (MASKED && CAUSAL && ka > qw + 31) continue;
+      // (bf16 head dim 256: the sub-tile's K and V operands are read in one
+      // sequence, RA fragments ahead of their products through a ring, with
+      // the order held by scheduling fences, so that no product waits on a
+      // read issued right before it)
+      constexpr bool RING = sizeof(T) == 2 && D > 128;
+      constexpr int RA = 3, NOP = KS + RS * MA;
+      auto opnd = [&](int n) ATTN_INLINE -> frag {
+        if (n < KS) return kt_.along_cols(st * 32 + l32, n, h);
+        const int j = n - KS;
+        return vt_.along_rows(dofs + (j % MA) * 32 + l32, st * 32, j / MA, h);
+      };
+      frag ring[RING ? RA : 1];
+      if constexpr (RING) {
+#pragma unroll
+        for (int n = 0; n < RA; ++n) ring[n] = opnd(n);
+      }
+      auto take = [&](int n) ATTN_INLINE -> frag {
+        if constexpr (RING) {
+          const frag a = ring[n % RA];
+          if (n + RA < NOP) ring[n % RA] = opnd(n + RA);
+          return a;
+        } else {
+          return opnd(n);
+        }
+      };
+      auto fence_if_ring = [&]() ATTN_INLINE {
+        if constexpr (RING) __builtin_amdgcn_sched_barrier(0);
+      };
       f32x16 s = zero16();
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk) s = M::mma(kt_.along_cols(st * 32 + l32, kk, h), qf[kk], s);
+      for (int kk = 0; kk < KS; ++kk) {
+        s = M::mma(take(kk), qf[kk], s);
+        fence_if_ring();
+      }
       // register r = key row ka + acc_row(r, h), column = query row q.  The
       // row max is taken on the raw scores (scale > 0 keeps the order).
       float mx = -__builtin_inff();
@@ -150,8 +181,10 @@ __global__ __launch_bounds__(256, 1) void fwd_lse_kernel(const T* __restrict__ Q
       for (int ss = 0; ss < RS; ++ss) {
         const frag bp = M::pack(s, ss);
 #pragma unroll
-        for (int mt = 0; mt < MA; ++mt)
-          acc[mt] = M::mma(vt_.along_rows(dofs + mt * 32 + l32, st * 32, ss, h), bp, acc[mt]);
+        for (int mt = 0; mt < MA; ++mt) {
+          acc[mt] = M::mma(take(KS + ss * MA + mt), bp, acc[mt]);
+          fence_if_ring();
+        }
       }
     }
   };
