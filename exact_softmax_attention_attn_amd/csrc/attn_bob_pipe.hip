@@ -186,16 +186,17 @@ __global__ __launch_bounds__(256, 1) void bob_q2_pipe_kernel(
     X.g = zero16();
     X.dp = splat16(d0);
     X.a = splat16(e0);
-    // K and gK of the next K step are read one step ahead, V and gV at the
-    // start of their own step (their products come third to fifth)
+    // K, gK, V and gV of the next K step are read one step ahead
     frag kc = plan.cols(T.k, 0, 0), gkc = plan.cols(T.gk, 0, 0);
+    frag vc = plan.cols(T.v, 0, 0), gvc = plan.cols(T.gv, 0, 0);
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
-      const frag c0 = kc, c1 = gkc;
-      const frag c2 = plan.cols(T.v, 0, kk), c3 = plan.cols(T.gv, 0, kk);
+      const frag c0 = kc, c1 = gkc, c2 = vc, c3 = gvc;
       if (kk + 1 < KS) {
         kc = plan.cols(T.k, 0, kk + 1);
         gkc = plan.cols(T.gk, 0, kk + 1);
+        vc = plan.cols(T.v, 0, kk + 1);
+        gvc = plan.cols(T.gv, 0, kk + 1);
       }
       X.s = M::mma(c0, qf[kk], X.s);
       X.g = M::mma(c0, gqf[kk], X.g);
@@ -210,17 +211,18 @@ __global__ __launch_bounds__(256, 1) void bob_q2_pipe_kernel(
   // T (packed operands), with `beside(i)` after product group i
   auto prods = [&](const Buf& T, const frag (&bp)[RS], const frag (&bds)[RS],
                    const frag (&bds2)[RS], const frag (&bw)[RS], auto&& beside) ATTN_INLINE {
-    // K^T and gK^T of the next group are read one group ahead, gV^T and V^T
-    // at the start of their own group (their products come third and fourth)
+    // K^T, gK^T, gV^T and V^T of the next group are read one group ahead
     frag nk = plan.rows(T.k, 0, 0, 0), ngk = plan.rows(T.gk, 0, 0, 0);
+    frag ngv = plan.rows(T.gv, 0, 0, 0), nv = plan.rows(T.v, 0, 0, 0);
 #pragma unroll
     for (int i = 0; i < RS * MT; ++i) {
       const int ss = i / MT, mt = i % MT;
-      const frag ok = nk, ogk = ngk;
-      const frag ogv = plan.rows(T.gv, 0, ss, mt), ov = plan.rows(T.v, 0, ss, mt);
+      const frag ok = nk, ogk = ngk, ogv = ngv, ov = nv;
       if (i + 1 < RS * MT) {
         nk = plan.rows(T.k, 0, (i + 1) / MT, (i + 1) % MT);
         ngk = plan.rows(T.gk, 0, (i + 1) / MT, (i + 1) % MT);
+        ngv = plan.rows(T.gv, 0, (i + 1) / MT, (i + 1) % MT);
+        nv = plan.rows(T.v, 0, (i + 1) / MT, (i + 1) % MT);
       }
       need_both(ok, ogk);
       mma_acc_agpr(acc[0][mt], ok, bds2[ss]);
